@@ -1,0 +1,364 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, fp64 CPU oracle for exact attention and for the ring of
+ * blockwise partial attentions that reaches it.  Only the test suite, the
+ * smoke check and the benchmark's CPU-baseline leg may load or call this
+ * code; the product path (the HIP library) never does, and the two share no
+ * source, header, table or helper.
+ *
+ * Sources (cited by page title and section):
+ *  [ZZ]  highthink.cn repost of the article on context parallelism and Ring
+ *        Attention (by Khang Pham), section "Zig Zag Ring Attention
+ *        通信和计算重叠": the ring loop (each rank keeps its Q chunk, K/V
+ *        chunks travel to the next rank), the causal rule (a token sees only
+ *        earlier tokens) and the interleaved assignment (rank 0 holds tokens
+ *        0, 4, 8, ...; rank 1 holds 1, 5, 9, ... for four ranks).
+ *  [DE]  aiunderstanding.org guide "Sequenzparallelität und
+ *        Ringaufmerksamkeit", sections "Tiefer Einblick" and "Häufig gestellte
+ *        Fragen": contiguous split, online softmax with running max and sum,
+ *        and the statement that the blockwise result equals full attention
+ *        after one full loop.
+ *  [TH]  the Thai version of the same guide, section on the technical
+ *        insight: running maximum, running normaliser, rescaling of earlier
+ *        partial sums when a larger value appears.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  - causal includes the diagonal (key j is allowed for query i iff j <= i);
+ *  - a row with no allowed key in a block is the partial (O=0, m=-inf, l=0);
+ *  - query head h reads key/value head h / (Hq/Hkv) (grouped-query reading);
+ *  - LSE = m + ln(l), natural log, scale included.
+ *
+ * Every input arrives as float32 (bf16 and fp16 values are exact in float32)
+ * and is widened to double on use; all arithmetic is double.  OpenMP only
+ * splits independent rows across threads; it changes no arithmetic order
+ * inside a row.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORA_LAYOUT_CONTIGUOUS 0
+#define ORA_LAYOUT_STRIPED 1
+
+int ora_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void ora_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+/*
+ * Token of slot p = r*n + j (rank r, local position j), with n = S/R.
+ *  contiguous ([DE] "Tiefer Einblick": each rank owns a contiguous run):
+ *      token = r*n + j
+ *  striped/interleaved ([ZZ] worked example: rank r holds r, r+R, r+2R...):
+ *      token = j*R + r
+ * Returns 0 on success, -1 if the arguments do not describe an even split.
+ */
+int ora_layout_maps(int layout, int64_t S, int32_t R, int32_t *fwd,
+                    int32_t *inv) {
+  if (R <= 0 || S < 0 || S % R != 0) return -1;
+  if (layout != ORA_LAYOUT_CONTIGUOUS && layout != ORA_LAYOUT_STRIPED)
+    return -1;
+  int64_t n = S / R;
+  for (int64_t r = 0; r < R; ++r) {
+    for (int64_t j = 0; j < n; ++j) {
+      int64_t p = r * n + j;
+      int64_t t = (layout == ORA_LAYOUT_CONTIGUOUS) ? p : j * R + r;
+      fwd[p] = (int32_t)t;
+      if (inv) inv[t] = (int32_t)p;
+    }
+  }
+  return 0;
+}
+
+/*
+ * Full-softmax attention for a list of query rows, in the original token
+ * order, against the whole key/value sequence with an explicit mask.
+ *
+ *   q_rows [nrows][d]   the query vectors of the listed rows
+ *   row_b, row_h, row_t the batch, query head and global token of each row
+ *   k, v   [B][Hkv][S][d]
+ *   For row (b, h, t) with g = h / (Hq/Hkv) and allowed set
+ *   A = { j : j <= t } (causal) or { 0..S-1 }:
+ *     s_j = scale * <q, k[b][g][j]>
+ *     m   = max_{j in A} s_j
+ *     l   = sum_{j in A} exp(s_j - m)
+ *     O   = sum_{j in A} exp(s_j - m) v[b][g][j] / l
+ *     LSE = m + ln l
+ *   Two passes over the keys per row: the max, then the sums.
+ *   Outputs o_rows [nrows][d] and lse_rows [nrows], double.
+ */
+void ora_attention_rows(const float *q_rows, const int64_t *row_b,
+                        const int64_t *row_h, const int64_t *row_t,
+                        int64_t nrows, const float *k, const float *v,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t S,
+                        int64_t d, double scale, int causal, double *o_rows,
+                        double *lse_rows) {
+  (void)B;
+  int64_t group = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const float *q = q_rows + r * d;
+    int64_t b = row_b[r], h = row_h[r], t = row_t[r];
+    int64_t g = h / group;
+    const float *kb = k + (b * Hkv + g) * S * d;
+    const float *vb = v + (b * Hkv + g) * S * d;
+    int64_t last = causal ? t : S - 1; /* allowed keys are 0..last */
+    double m = -INFINITY;
+    for (int64_t j = 0; j <= last; ++j) {
+      double s = 0.0;
+      for (int64_t c = 0; c < d; ++c) s += (double)q[c] * (double)kb[j * d + c];
+      s *= scale;
+      if (s > m) m = s;
+    }
+    double l = 0.0;
+    double *o = o_rows + r * d;
+    for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+    for (int64_t j = 0; j <= last; ++j) {
+      double s = 0.0;
+      for (int64_t c = 0; c < d; ++c) s += (double)q[c] * (double)kb[j * d + c];
+      s *= scale;
+      double p = exp(s - m);
+      l += p;
+      for (int64_t c = 0; c < d; ++c) o[c] += p * (double)vb[j * d + c];
+    }
+    for (int64_t c = 0; c < d; ++c) o[c] /= l;
+    lse_rows[r] = m + log(l);
+  }
+}
+
+/*
+ * Partial attention of a query shard against ONE key/value block, the unit
+ * of work of one ring hop ([ZZ]; [DE] "Tiefer Einblick": as each block
+ * arrives the rank computes a partial attention).
+ *
+ *   q [B][Hq][nq][d], k, v [B][Hkv][nk][d] (contiguous)
+ *   global id of local query i: qg0 + i*qstep; of local key j: kg0 + j*kstep
+ *   causal: key j allowed for query i iff gid(j) <= gid(i)
+ *   out: o [B][Hq][nq][d] normalised (sum p v / l), m [B][Hq][nq] (natural
+ *   units, scale included), l = sum exp(s - m).  A row with no allowed key
+ *   gets (O = 0, m = -inf, l = 0).
+ */
+void ora_block_partial(const float *q, const float *k, const float *v,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t nq,
+                       int64_t nk, int64_t d, double scale, int causal,
+                       int64_t qg0, int64_t qstep, int64_t kg0, int64_t kstep,
+                       double *o, double *m_out, double *l_out) {
+  int64_t group = Hq / Hkv;
+  int64_t rows = B * Hq * nq;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t row = 0; row < rows; ++row) {
+    int64_t i = row % nq;
+    int64_t bh = row / nq;
+    int64_t h = bh % Hq, b = bh / Hq;
+    int64_t g = h / group;
+    const float *qi = q + row * d;
+    const float *kb = k + (b * Hkv + g) * nk * d;
+    const float *vb = v + (b * Hkv + g) * nk * d;
+    int64_t gq = qg0 + i * qstep;
+    double m = -INFINITY;
+    int any = 0;
+    for (int64_t j = 0; j < nk; ++j) {
+      if (causal && kg0 + j * kstep > gq) continue;
+      double s = 0.0;
+      for (int64_t c = 0; c < d; ++c) s += (double)qi[c] * (double)kb[j * d + c];
+      s *= scale;
+      if (!any || s > m) m = s;
+      any = 1;
+    }
+    double *oi = o + row * d;
+    for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
+    if (!any) {
+      m_out[row] = -INFINITY;
+      l_out[row] = 0.0;
+      continue;
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < nk; ++j) {
+      if (causal && kg0 + j * kstep > gq) continue;
+      double s = 0.0;
+      for (int64_t c = 0; c < d; ++c) s += (double)qi[c] * (double)kb[j * d + c];
+      s *= scale;
+      double p = exp(s - m);
+      l += p;
+      for (int64_t c = 0; c < d; ++c) oi[c] += p * (double)vb[j * d + c];
+    }
+    for (int64_t c = 0; c < d; ++c) oi[c] /= l;
+    m_out[row] = m;
+    l_out[row] = l;
+  }
+}
+
+/*
+ * Online-softmax combine of two partials of the same rows ([TH] technical
+ * insight: keep a running maximum and running normaliser and rescale the
+ * earlier partial sums when a larger maximum appears; [DE] FAQ: this makes
+ * the blockwise result equal to full attention).
+ *
+ *   m = max(m_a, m_b); w_a = l_a e^{m_a - m}; w_b = l_b e^{m_b - m}
+ *   l = w_a + w_b;     O = (w_a O_a + w_b O_b) / l
+ *   (0, -inf, 0) is the identity; two empty rows stay empty.
+ * Result is written over (o_a, m_a, l_a).
+ */
+void ora_merge(double *o_a, double *m_a, double *l_a, const double *o_b,
+               const double *m_b, const double *l_b, int64_t rows,
+               int64_t d) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    double ma = m_a[r], mb = m_b[r];
+    double m = ma > mb ? ma : mb;
+    if (m == -INFINITY) { /* both empty */
+      for (int64_t c = 0; c < d; ++c) o_a[r * d + c] = 0.0;
+      m_a[r] = -INFINITY;
+      l_a[r] = 0.0;
+      continue;
+    }
+    double wa = (ma == -INFINITY) ? 0.0 : l_a[r] * exp(ma - m);
+    double wb = (mb == -INFINITY) ? 0.0 : l_b[r] * exp(mb - m);
+    double l = wa + wb;
+    for (int64_t c = 0; c < d; ++c)
+      o_a[r * d + c] = (wa * o_a[r * d + c] + wb * o_b[r * d + c]) / l;
+    m_a[r] = m;
+    l_a[r] = l;
+  }
+}
+
+/*
+ * The ring, emulated on the CPU in fp64, in the pages' order ([ZZ]: each
+ * rank holds its Q, K, V chunk, attends its Q to the K/V it holds, passes
+ * the K/V on to the next rank and receives from the previous, until every
+ * query has met every key; [DE]/[TH]: partials are folded by online softmax).
+ *
+ * q, k, v are in the ORIGINAL token order, [B][H][S][d].  For each rank r,
+ * hop h = 0..R-1 brings the block of source rank s = (r - h) mod R (the
+ * block that has travelled h steps forward).  Each hop's partial is folded
+ * into the running (O, m, l) with ora_merge.  The result, O and LSE, is
+ * written back in the original token order: o [B][Hq][S][d], lse [B][Hq][S].
+ * Returns 0, or -1 on a bad split / allocation failure.
+ */
+int ora_ring_emulate(const float *q, const float *k, const float *v,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t S, int64_t d,
+                     int32_t R, int layout, double scale, int causal,
+                     double *o, double *lse) {
+  if (R <= 0 || S % R != 0) return -1;
+  int64_t n = S / R;
+  int32_t *fwd = (int32_t *)malloc(sizeof(int32_t) * (size_t)S);
+  float *qs = (float *)malloc(sizeof(float) * (size_t)(B * Hq * n * d));
+  float *ks = (float *)malloc(sizeof(float) * (size_t)(R * B * Hkv * n * d));
+  float *vs = (float *)malloc(sizeof(float) * (size_t)(R * B * Hkv * n * d));
+  int64_t rows = B * Hq * n;
+  double *oacc = (double *)malloc(sizeof(double) * (size_t)(rows * d));
+  double *macc = (double *)malloc(sizeof(double) * (size_t)rows);
+  double *lacc = (double *)malloc(sizeof(double) * (size_t)rows);
+  double *oblk = (double *)malloc(sizeof(double) * (size_t)(rows * d));
+  double *mblk = (double *)malloc(sizeof(double) * (size_t)rows);
+  double *lblk = (double *)malloc(sizeof(double) * (size_t)rows);
+  int rc = 0;
+  if (!fwd || !qs || !ks || !vs || !oacc || !macc || !lacc || !oblk || !mblk ||
+      !lblk || ora_layout_maps(layout, S, R, fwd, NULL) != 0) {
+    rc = -1;
+    goto done;
+  }
+  /* every rank's K and V shard, [R][B][Hkv][n][d] */
+  for (int64_t r = 0; r < R; ++r)
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t g = 0; g < Hkv; ++g)
+        for (int64_t j = 0; j < n; ++j) {
+          int64_t t = fwd[r * n + j];
+          const float *src_k = k + ((b * Hkv + g) * S + t) * d;
+          const float *src_v = v + ((b * Hkv + g) * S + t) * d;
+          float *dk = ks + (((r * B + b) * Hkv + g) * n + j) * d;
+          float *dv = vs + (((r * B + b) * Hkv + g) * n + j) * d;
+          memcpy(dk, src_k, sizeof(float) * (size_t)d);
+          memcpy(dv, src_v, sizeof(float) * (size_t)d);
+        }
+  for (int64_t r = 0; r < R; ++r) {
+    /* this rank's query shard */
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t h = 0; h < Hq; ++h)
+        for (int64_t j = 0; j < n; ++j) {
+          int64_t t = fwd[r * n + j];
+          memcpy(qs + ((b * Hq + h) * n + j) * d, q + ((b * Hq + h) * S + t) * d,
+                 sizeof(float) * (size_t)d);
+        }
+    for (int64_t i = 0; i < rows; ++i) {
+      macc[i] = -INFINITY;
+      lacc[i] = 0.0;
+    }
+    for (int64_t i = 0; i < rows * d; ++i) oacc[i] = 0.0;
+    /* global ids are affine in the local index for both layouts */
+    int64_t step = (layout == ORA_LAYOUT_CONTIGUOUS) ? 1 : R;
+    int64_t qg0 = (layout == ORA_LAYOUT_CONTIGUOUS) ? r * n : r;
+    for (int64_t hop = 0; hop < R; ++hop) {
+      int64_t s = ((r - hop) % R + R) % R;
+      int64_t kg0 = (layout == ORA_LAYOUT_CONTIGUOUS) ? s * n : s;
+      const float *kb = ks + s * B * Hkv * n * d;
+      const float *vb = vs + s * B * Hkv * n * d;
+      ora_block_partial(qs, kb, vb, B, Hq, Hkv, n, n, d, scale, causal, qg0,
+                        step, kg0, step, oblk, mblk, lblk);
+      ora_merge(oacc, macc, lacc, oblk, mblk, lblk, rows, d);
+    }
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t h = 0; h < Hq; ++h)
+        for (int64_t j = 0; j < n; ++j) {
+          int64_t t = fwd[r * n + j];
+          int64_t row = (b * Hq + h) * n + j;
+          int64_t dst = (b * Hq + h) * S + t;
+          memcpy(o + dst * d, oacc + row * d, sizeof(double) * (size_t)d);
+          lse[dst] = macc[row] + log(lacc[row]);
+        }
+  }
+done:
+  free(fwd);
+  free(qs);
+  free(ks);
+  free(vs);
+  free(oacc);
+  free(macc);
+  free(lacc);
+  free(oblk);
+  free(mblk);
+  free(lblk);
+  return rc;
+}
+
+/*
+ * Causal work per rank by brute force: W[r] = number of (query of rank r,
+ * key) pairs with key token <= query token, over the whole sequence.
+ * O(S^2): for the small sequences of the tests ([ZZ]: the interleaved
+ * assignment is there to even out exactly this count).
+ */
+int ora_pair_counts(int layout, int64_t S, int32_t R, int64_t *W) {
+  if (R <= 0 || S % R != 0) return -1;
+  int32_t *fwd = (int32_t *)malloc(sizeof(int32_t) * (size_t)S);
+  int32_t *owner = (int32_t *)malloc(sizeof(int32_t) * (size_t)S);
+  if (!fwd || !owner || ora_layout_maps(layout, S, R, fwd, NULL) != 0) {
+    free(fwd);
+    free(owner);
+    return -1;
+  }
+  int64_t n = S / R;
+  for (int64_t p = 0; p < S; ++p) owner[fwd[p]] = (int32_t)(p / n);
+  for (int32_t r = 0; r < R; ++r) W[r] = 0;
+  for (int64_t tq = 0; tq < S; ++tq)
+    for (int64_t tk = 0; tk < S; ++tk)
+      if (tk <= tq) W[owner[tq]] += 1;
+  free(fwd);
+  free(owner);
+  return 0;
+}

@@ -1,0 +1,402 @@
+"""Pins of the fp64 oracle against facts fixed by the pages and by mathematics.
+
+Each ``check_*`` takes an oracle binding and raises AssertionError when the
+oracle disagrees with the pinned fact.  ``test_oracle_pins.py`` runs them on
+the committed oracle; ``test_oracle_mutants.py`` plants plausible mistakes in
+copies of the oracle source and shows that each one trips at least one pin.
+
+Page citations (page title and section):
+* [ZZ] highthink.cn repost of the context-parallelism / Ring Attention article,
+  section "Zig Zag Ring Attention 通信和计算重叠";
+* [DE] aiunderstanding.org "Sequenzparallelität und Ringaufmerksamkeit",
+  sections "Tiefer Einblick" and FAQ;
+* [TH] Thai version of that guide, technical-insight section.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+CONTIGUOUS, STRIPED = 0, 1
+
+
+# --------------------------------------------------------------------------- helpers
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def brute_head(q, k, v, scale, causal):
+    """Pure-Python exact-as-possible attention for one head (math.fsum, math.exp).
+
+    q, k, v are lists of lists of floats [S][d].  Returns (O rows, LSE list).
+    """
+    S = len(q)
+    d = len(q[0])
+    outs, lses = [], []
+    for i in range(S):
+        allowed = list(range(i + 1)) if causal else list(range(S))
+        s = [scale * math.fsum(q[i][c] * k[j][c] for c in range(d)) for j in allowed]
+        m = max(s)
+        p = [math.exp(x - m) for x in s]
+        lsum = math.fsum(p)
+        outs.append([math.fsum(p[t] * v[j][c] for t, j in enumerate(allowed)) / lsum
+                     for c in range(d)])
+        lses.append(m + math.log(lsum))
+    return outs, lses
+
+
+def _close(a, b, rtol, atol, what):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    ok = np.isclose(a, b, rtol=rtol, atol=atol) | ((a == b) & np.isinf(a))
+    if not ok.all():
+        diff = np.abs(np.nan_to_num(a - b, nan=np.inf))
+        raise AssertionError("%s: max |diff| %.3e" % (what, diff.max()))
+
+
+def read_interleave_golden():
+    """Parse tests/golden/interleave_r4.txt -> (R, {rank: [tokens]})."""
+    R = None
+    ranks = {}
+    with open(os.path.join(GOLDEN, "interleave_r4.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("R "):
+                R = int(line.split()[1])
+            elif line.startswith("rank"):
+                head, toks = line.split(":")
+                ranks[int(head.split()[1])] = [int(t) for t in toks.split()]
+    return R, ranks
+
+
+def closed_form_counts(layout, S, R):
+    """Per-rank causal pairs: contiguous r*n^2 + n(n+1)/2; striped R n^2/2 + n(2r+2-R)/2."""
+    n = S // R
+    if layout == CONTIGUOUS:
+        return np.array([r * n * n + n * (n + 1) // 2 for r in range(R)], np.int64)
+    return np.array([(R * n * n + n * (2 * r + 2 - R)) // 2 for r in range(R)], np.int64)
+
+
+# --------------------------------------------------------------------------- PIN-1
+def check_layout_golden(orc):
+    """[ZZ] worked example: with four ranks, rank 0 holds 0,4,8...; rank 1 holds 1,5,9..."""
+    R, ranks = read_interleave_golden()
+    for S in (12, 16, 64):
+        fwd, _ = orc.layout_maps(STRIPED, S, R)
+        n = S // R
+        for r, toks in ranks.items():
+            got = list(fwd[r * n: r * n + len(toks)])
+            assert got == toks, (S, r, got, toks)
+
+
+def check_layout_bijection(orc):
+    """Both maps are bijections with inv(fwd(p)) = p; contiguous is the identity;
+    every striped slot holds a token congruent to its rank mod R."""
+    for S, R in ((12, 4), (1024, 4), (48, 3), (64, 64), (7, 1), (32768, 8)):
+        n = S // R
+        for layout in (CONTIGUOUS, STRIPED):
+            fwd, inv = orc.layout_maps(layout, S, R)
+            assert sorted(fwd.tolist()) == list(range(S))
+            assert (inv[fwd] == np.arange(S)).all()
+            assert (fwd[inv] == np.arange(S)).all()
+            if layout == CONTIGUOUS:
+                assert (fwd == np.arange(S)).all()
+            else:
+                p = np.arange(S)
+                assert (fwd % R == p // n).all()          # owner rank
+                assert (fwd // R == p % n).all()          # local position
+                # within a rank tokens increase, so masks stay monotone
+                assert (np.diff(fwd.reshape(R, n), axis=1) > 0).all()
+
+
+# --------------------------------------------------------------------------- PIN-2
+def check_brute_force(orc):
+    """Oracle = pure-Python fsum brute force on tiny inputs (MHA and GQA, both masks)."""
+    rng = _rng(11)
+    B, Hq, Hkv, S, d = 2, 4, 2, 9, 5
+    q = rng.standard_normal((B, Hq, S, d)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, S, d)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, S, d)).astype(np.float32)
+    scale = 1 / math.sqrt(d)
+    for causal in (True, False):
+        o, lse = orc.attention_full(q, k, v, scale, causal)
+        for b in range(B):
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                bo, bl = brute_head(q[b, h].astype(np.float64).tolist(),
+                                    k[b, g].astype(np.float64).tolist(),
+                                    v[b, g].astype(np.float64).tolist(), scale, causal)
+                _close(o[b, h], bo, 1e-13, 1e-14, "brute O")
+                _close(lse[b, h], bl, 1e-13, 1e-14, "brute LSE")
+
+
+def check_block_partial_brute(orc):
+    """One block with affine global ids against brute force over the allowed subset;
+    rows that see no key give (0, -inf, 0)."""
+    rng = _rng(12)
+    B, Hq, Hkv, nq, nk, d = 1, 2, 1, 6, 7, 4
+    q = rng.standard_normal((B, Hq, nq, d)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, nk, d)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, nk, d)).astype(np.float32)
+    scale = 0.7
+    # striped-like ids: query rank 1, key source 2, R = 4 -> key j allowed iff 4j+2 <= 4i+1
+    qg0, qs, kg0, ks = 1, 4, 2, 4
+    o, m, l = orc.block_partial(q, k, v, scale, True, qg0, qs, kg0, ks)
+    for h in range(Hq):
+        for i in range(nq):
+            allowed = [j for j in range(nk) if kg0 + j * ks <= qg0 + i * qs]
+            if not allowed:
+                assert (o[0, h, i] == 0).all() and m[0, h, i] == -math.inf and l[0, h, i] == 0
+                continue
+            s = [scale * math.fsum(float(q[0, h, i, c]) * float(k[0, 0, j, c]) for c in range(d))
+                 for j in allowed]
+            mm = max(s)
+            p = [math.exp(x - mm) for x in s]
+            ll = math.fsum(p)
+            oo = [math.fsum(p[t] * float(v[0, 0, j, c]) for t, j in enumerate(allowed)) / ll
+                  for c in range(d)]
+            _close(o[0, h, i], oo, 1e-13, 1e-14, "block O")
+            _close(m[0, h, i], mm, 1e-14, 1e-15, "block m")
+            _close(l[0, h, i], ll, 1e-13, 1e-15, "block l")
+    # row 0 of this block has no allowed key (4*0+2 > 4*0+1)
+    assert m[0, 0, 0] == -math.inf
+
+
+# --------------------------------------------------------------------------- PIN-3..6
+def check_identical_keys(orc):
+    """All keys equal: O_i = mean of the allowed values (prefix mean when causal),
+    LSE_i = scale <q_i, k> + ln(#allowed)."""
+    rng = _rng(13)
+    B, H, S, d = 1, 2, 33, 8
+    q = rng.standard_normal((B, H, S, d)).astype(np.float32)
+    kv = rng.standard_normal(d).astype(np.float32)
+    k = np.broadcast_to(kv, (B, H, S, d)).copy()
+    v = rng.standard_normal((B, H, S, d)).astype(np.float32)
+    scale = 0.3
+    for causal in (True, False):
+        o, lse = orc.attention_full(q, k, v, scale, causal)
+        v64 = v.astype(np.float64)
+        cnt = np.arange(1, S + 1) if causal else np.full(S, S)
+        if causal:
+            mean = np.cumsum(v64, axis=2) / cnt[None, None, :, None]
+        else:
+            mean = np.broadcast_to(v64.mean(axis=2, keepdims=True), v64.shape)
+        _close(o, mean, 1e-12, 1e-13, "identical-keys O")
+        expect = scale * (q.astype(np.float64) @ kv.astype(np.float64)) + np.log(cnt)[None, None]
+        _close(lse, expect, 1e-12, 1e-13, "identical-keys LSE")
+
+
+def check_dominant_logit(orc):
+    """One allowed logit beats all others by >= 40: O = that value row within
+    #A e^-40 max|v|, LSE = that logit within the same bound."""
+    rng = _rng(14)
+    S, d = 40, 16
+    scale = 0.25
+    q = rng.standard_normal((1, 1, S, d)).astype(np.float32)
+    k = (0.01 * rng.standard_normal((1, 1, S, d))).astype(np.float32)
+    v = rng.standard_normal((1, 1, S, d)).astype(np.float32)
+    t = S - 1
+    jstar = 17
+    qq = q[0, 0, t].astype(np.float64)
+    k[0, 0, jstar] = (qq * (50.0 / (scale * qq @ qq))).astype(np.float32)
+    o, lse = orc.attention_rows(q[0, 0, t:t + 1], [0], [0], [t], k, v, 1, scale, True)
+    sstar = scale * float(q[0, 0, t].astype(np.float64) @ k[0, 0, jstar].astype(np.float64))
+    others = scale * (k[0, 0, :t + 1].astype(np.float64) @ qq)
+    others = np.delete(others, jstar)
+    gap = sstar - others.max()
+    assert gap >= 40, gap
+    bound = (t + 1) * math.exp(-gap) * np.abs(v).max()
+    assert np.abs(o[0] - v[0, 0, jstar]).max() <= bound + 1e-15
+    assert abs(lse[0] - sstar) <= (t + 1) * math.exp(-gap) + 1e-13
+
+
+def check_constant_values(orc):
+    """All value rows equal c: O_i = c for every row (normalisation)."""
+    rng = _rng(15)
+    B, Hq, Hkv, S, d = 1, 4, 2, 50, 8
+    q = (3 * rng.standard_normal((B, Hq, S, d))).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, S, d)).astype(np.float32)
+    c = rng.standard_normal(d).astype(np.float32)
+    v = np.broadcast_to(c, (B, Hkv, S, d)).copy()
+    for causal in (True, False):
+        o, _ = orc.attention_full(q, k, v, 0.35, causal)
+        _close(o, np.broadcast_to(c.astype(np.float64), o.shape), 1e-13, 1e-14, "const-V O")
+
+
+def check_key_shift(orc):
+    """k_j -> k_j + u for all j leaves O unchanged and shifts LSE_i by scale <q_i, u>.
+    Small-integer inputs keep k + u exact in float32."""
+    rng = _rng(16)
+    B, H, S, d = 1, 2, 24, 8
+    q = rng.integers(-3, 4, (B, H, S, d)).astype(np.float32)
+    k = rng.integers(-3, 4, (B, H, S, d)).astype(np.float32)
+    v = rng.standard_normal((B, H, S, d)).astype(np.float32)
+    u = rng.integers(-2, 3, d).astype(np.float32)
+    scale = 0.25
+    for causal in (True, False):
+        o1, l1 = orc.attention_full(q, k, v, scale, causal)
+        o2, l2 = orc.attention_full(q, k + u, v, scale, causal)
+        _close(o2, o1, 1e-12, 1e-13, "shift O")
+        shift = scale * (q.astype(np.float64) @ u.astype(np.float64))
+        _close(l2, l1 + shift, 1e-12, 1e-12, "shift LSE")
+
+
+# --------------------------------------------------------------------------- PIN-7
+def check_library_sdpa(orc):
+    """R = 1 is plain attention: O against torch's scaled_dot_product_attention in
+    float64 on the CPU (grouped heads by repeating K/V), LSE against scipy's
+    logsumexp over the masked logits."""
+    import torch
+    from scipy.special import logsumexp
+    rng = _rng(17)
+    B, Hq, Hkv, S, d = 2, 4, 2, 37, 16
+    q = rng.standard_normal((B, Hq, S, d)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, S, d)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, S, d)).astype(np.float32)
+    scale = 1 / math.sqrt(d)
+    rep = Hq // Hkv
+    tq = torch.from_numpy(q).double()
+    tk = torch.from_numpy(k).double().repeat_interleave(rep, dim=1)
+    tv = torch.from_numpy(v).double().repeat_interleave(rep, dim=1)
+    for causal in (True, False):
+        o, lse = orc.attention_full(q, k, v, scale, causal)
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+                                                               scale=scale).numpy()
+        _close(o, ref, 1e-11, 1e-12, "sdpa O")
+        logits = scale * np.matmul(tq.numpy(), np.swapaxes(tk.numpy(), -1, -2))
+        if causal:
+            logits = np.where(np.tril(np.ones((S, S), bool)), logits, -np.inf)
+        _close(lse, logsumexp(logits, axis=-1), 1e-12, 1e-12, "scipy LSE")
+
+
+# --------------------------------------------------------------------------- PIN-8/9
+def check_ring_equals_full(orc):
+    """[DE] FAQ / [TH]: the blockwise online-softmax ring equals full attention,
+    for every ring size and both layouts (fp64, up to rounding)."""
+    rng = _rng(18)
+    B, Hq, Hkv, S, d = 1, 2, 1, 48, 8
+    q = rng.standard_normal((B, Hq, S, d)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, S, d)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, S, d)).astype(np.float32)
+    scale = 1 / math.sqrt(d)
+    for causal in (True, False):
+        o, lse = orc.attention_full(q, k, v, scale, causal)
+        for R in (1, 2, 3, 4, 8, 16, 48):
+            for layout in (CONTIGUOUS, STRIPED):
+                ro, rl = orc.ring_emulate(q, k, v, R, layout, scale, causal)
+                _close(ro, o, 1e-12, 1e-13, "ring O R=%d L=%d" % (R, layout))
+                _close(rl, lse, 1e-12, 1e-13, "ring LSE R=%d L=%d" % (R, layout))
+
+
+def check_layout_independence(orc):
+    """Striped and contiguous rings give the same result in the original order."""
+    rng = _rng(19)
+    B, H, S, d = 2, 2, 64, 4
+    q = rng.standard_normal((B, H, S, d)).astype(np.float32)
+    k = rng.standard_normal((B, H, S, d)).astype(np.float32)
+    v = rng.standard_normal((B, H, S, d)).astype(np.float32)
+    for R in (4, 8):
+        a = orc.ring_emulate(q, k, v, R, CONTIGUOUS, 0.5, True)
+        b = orc.ring_emulate(q, k, v, R, STRIPED, 0.5, True)
+        _close(a[0], b[0], 1e-12, 1e-13, "layouts O")
+        _close(a[1], b[1], 1e-12, 1e-13, "layouts LSE")
+
+
+# --------------------------------------------------------------------------- PIN-10
+def check_merge_algebra(orc):
+    """(+) is commutative, associative to rounding, has identity (0, -inf, 0), and
+    folding the partials of any partition of a row's keys gives the full row."""
+    rng = _rng(20)
+    rows, d = 16, 8
+
+    def part(seed):
+        r = _rng(seed)
+        return (r.standard_normal((rows, d)), r.standard_normal(rows) * 3,
+                np.exp(r.standard_normal(rows)))
+
+    a, b, c = part(1), part(2), part(3)
+    ab = orc.merge(*a, *b)
+    ba = orc.merge(*b, *a)
+    for x, y in zip(ab, ba):
+        assert np.array_equal(x, y)
+    ab_c = orc.merge(*ab, *c)
+    a_bc = orc.merge(*a, *orc.merge(*b, *c))
+    for x, y in zip(ab_c, a_bc):
+        _close(x, y, 1e-13, 1e-14, "assoc")
+    ident = (np.zeros((rows, d)), np.full(rows, -np.inf), np.zeros(rows))
+    for x, y in zip(orc.merge(*a, *ident), a):
+        _close(x, y, 1e-15, 1e-15, "identity right")
+    for x, y in zip(orc.merge(*ident, *a), a):
+        _close(x, y, 1e-15, 1e-15, "identity left")
+    e = orc.merge(*ident, *ident)
+    assert (e[0] == 0).all() and (e[1] == -np.inf).all() and (e[2] == 0).all()
+    # partition folding: keys split into uneven contiguous pieces
+    B, H, S, dd = 1, 1, 30, 8
+    q = rng.standard_normal((B, H, S, dd)).astype(np.float32)
+    k = rng.standard_normal((B, H, S, dd)).astype(np.float32)
+    v = rng.standard_normal((B, H, S, dd)).astype(np.float32)
+    o_full, lse_full = orc.attention_full(q, k, v, 0.4, True)
+    cuts = [0, 7, 8, 19, 30]
+    acc = (np.zeros((S, dd)), np.full(S, -np.inf), np.zeros(S))
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        po, pm, pl = orc.block_partial(q, k[:, :, lo:hi], v[:, :, lo:hi], 0.4, True, 0, 1, lo, 1)
+        acc = orc.merge(*acc, po[0, 0], pm[0, 0], pl[0, 0])
+    _close(acc[0], o_full[0, 0], 1e-12, 1e-13, "partition O")
+    _close(acc[1] + np.log(acc[2]), lse_full[0, 0], 1e-12, 1e-13, "partition LSE")
+
+
+# --------------------------------------------------------------------------- PIN-11
+def check_pair_counts(orc):
+    """Per-rank causal pair counts: brute force equals the closed forms, sums to
+    S(S+1)/2; the striped layout is balanced to within one row per block ([ZZ])."""
+    for S, R in ((8, 2), (16, 4), (24, 4), (32, 8), (64, 8), (60, 6), (48, 3), (128, 16)):
+        for layout in (CONTIGUOUS, STRIPED):
+            W = orc.pair_counts(layout, S, R)
+            assert (W == closed_form_counts(layout, S, R)).all(), (S, R, layout, W)
+            assert W.sum() == S * (S + 1) // 2
+        Ws = orc.pair_counts(STRIPED, S, R)
+        assert Ws.max() - Ws.min() == (R - 1) * (S // R)
+
+
+def check_coverage(orc):
+    """[ZZ]/[DE]: after one full loop every query has met every allowed key exactly
+    once.  With all-zero Q and K every logit is 0, so e^LSE counts the keys seen."""
+    B, H, S, d = 1, 1, 40, 4
+    z = np.zeros((B, H, S, d), np.float32)
+    v = np.ones((B, H, S, d), np.float32)
+    for R in (1, 2, 4, 5, 8):
+        for layout in (CONTIGUOUS, STRIPED):
+            for causal in (True, False):
+                _, lse = orc.ring_emulate(z, z, v, R, layout, 1.0, causal)
+                seen = np.exp(lse[0, 0])
+                expect = np.arange(1, S + 1) if causal else np.full(S, S)
+                _close(seen, expect, 1e-12, 1e-12, "coverage")
+
+
+# --------------------------------------------------------------------------- PIN-12
+def check_gqa_equals_repeated_mha(orc):
+    """Grouped heads equal MHA with each K/V head repeated Hq/Hkv times (bitwise)."""
+    rng = _rng(21)
+    B, Hq, Hkv, S, d = 1, 8, 2, 20, 8
+    q = rng.standard_normal((B, Hq, S, d)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, S, d)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, S, d)).astype(np.float32)
+    o1, l1 = orc.attention_full(q, k, v, 0.3, True)
+    kr = np.repeat(k, Hq // Hkv, axis=1)
+    vr = np.repeat(v, Hq // Hkv, axis=1)
+    o2, l2 = orc.attention_full(q, kr, vr, 0.3, True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+ALL_CHECKS = [
+    check_layout_golden, check_layout_bijection, check_brute_force, check_block_partial_brute,
+    check_identical_keys, check_dominant_logit, check_constant_values, check_key_shift,
+    check_library_sdpa, check_ring_equals_full, check_layout_independence, check_merge_algebra,
+    check_pair_counts, check_coverage, check_gqa_equals_repeated_mha,
+]
