@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the ring-attention path on one MI355X.
+
+A step is one full pass of the path over one batch of synthetic input:
+index maps -> shard gather of Q, K, V -> R hops of block attention folded by
+online softmax, with the K/V hand-off copied on a side stream -> scatter of O
+and LSE back to the original token order.  The default workload is one rank's
+share of a 1M-token causal context: rank 3 of an 8-rank striped ring,
+131072 queries x 8 K/V blocks of 131072 keys, Hq = Hkv = 8, d = 128, bf16.
+
+Prints ONE JSON line (rank 0).  value = causal attention TFLOP/s with the
+metric's FLOP count (4*B*H*Sq*Sk*d, halved for causal) over the measured step
+time; roofline = the block-attention kernel's algorithmic FLOPs per launch over
+its average launch time (HIP events recorded around every launch by the
+library's timing hook, on the compute stream); cpu_baseline = the fp64 oracle
+on a bounded sample of the same workload's query rows, on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def hop_pairs(w, layout_code):
+    """Allowed (query, key) pairs per head at each hop, summed over computed ranks."""
+    n, R = w.n, w.R
+    out = []
+    for h in range(R):
+        tot = 0
+        for r in range(w.rank0, w.rank0 + w.ranks):
+            s = (r - h) % R
+            if not w.causal:
+                tot += n * n
+            elif layout_code == 0:  # contiguous: past block full, own block triangle, future none
+                tot += n * n if s < r else (n * (n + 1) // 2 if s == r else 0)
+            else:  # striped: key j allowed iff j*R+s <= i*R+r
+                tot += n * (n + 1) // 2 if s <= r else n * (n - 1) // 2
+        out.append(tot)
+    return out
+
+
+def cpu_baseline(w, data, layout_code, seconds_target, seed=4242):
+    """Time the fp64 oracle on a bounded, seeded sample of the workload's query rows."""
+    import oracle
+    oracle.build(force=False)
+    orc = oracle.default()
+    fwd, _ = orc.layout_maps(layout_code, w.S, w.R)
+    n = w.n
+    owned = fwd[w.rank0 * n:(w.rank0 + w.ranks) * n].astype(np.int64)
+    rng = np.random.default_rng(seed)
+    q32, k32, v32 = data["q32"], data["k32"], data["v32"]
+    # calibrate with a few rows, then size the sample for ~seconds_target
+    def run(nrows):
+        t = rng.choice(owned, size=nrows, replace=False)
+        b = rng.integers(0, w.B, nrows)
+        hh = rng.integers(0, w.Hq, nrows)
+        qrows = q32[b, hh, t]
+        keys = (t + 1) if w.causal else np.full(nrows, w.S)
+        t0 = time.perf_counter()
+        orc.attention_rows(qrows, b, hh, t, k32, v32, w.Hq, w.scale, w.causal)
+        dt = time.perf_counter() - t0
+        return dt, float(keys.sum())
+    dt0, k0 = run(max(orc.num_threads(), 8))
+    per_key = dt0 / max(k0, 1.0)
+    avg_keys = (w.S / 2) if w.causal else w.S
+    rows = int(max(orc.num_threads(), min(4096, seconds_target / (per_key * avg_keys))))
+    dt, keys = run(rows)
+    flops = 4.0 * w.d * keys
+    total_pairs = w.metric_flops() / (4.0 * w.d)
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
+        "kind": "oracle",
+        "sample": "%d seeded query rows of the same workload (all heads, tokens of the computed "
+                  "rank), each against its full allowed key set: %.3g pairs in %.2f s; whole "
+                  "workload extrapolates to %.0f s" % (rows, keys, dt, total_pairs / (keys / dt)),
+    }
+
+
+def merge_bench(torch, rb, rows=4 * 16 * 512 * 64, d=64, iters=20):
+    """ra_merge on the short-block shapes (B=4, H=16, 512-token shards, R=64, d=64)."""
+    dev = "cuda"
+    o_a = torch.randn(rows, d, device=dev)
+    o_b = torch.randn(rows, d, device=dev)
+    m_a = torch.randn(rows, device=dev)
+    m_b = torch.randn(rows, device=dev)
+    l_a = torch.rand(rows, device=dev) + 0.5
+    l_b = torch.rand(rows, device=dev) + 0.5
+    for _ in range(3):
+        rb.ra_merge(o_a, m_a, l_a, o_b, m_b, l_b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(iters):
+        rb.ra_merge(o_a, m_a, l_a, o_b, m_b, l_b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    nbytes = (12 * d + 24) * rows
+    return {"rows": rows, "d": d, "us_per_launch": ms * 1e3, "bytes_per_launch": nbytes,
+            "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 /
+            PEAK_HBM_GBS}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=None, help="workload name (default: 1M-token share)")
+    ap.add_argument("--layout", default=None)
+    ap.add_argument("--handoff", default="copy", choices=["copy", "swap"])
+    ap.add_argument("--merge", default="fused", choices=["fused", "separate"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-merge-bench", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build emulates the ring of ranks on a single "
+              "MI355X and has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from long_context_exact_block_amd import binding as rb
+    from long_context_exact_block_amd import configs, inputs
+    from long_context_exact_block_amd.pipeline import RingAttention
+
+    w = configs.BY_NAME[args.workload] if args.workload else configs.SHARE_1M
+    layout = args.layout or w.layouts[0]
+    lcode = rb.LAYOUTS[layout]
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    rb.lib()  # fail loudly if the HIP library is missing
+
+    log("workload %s layout %s: generating inputs" % (w.name, layout))
+    t0 = time.perf_counter()
+    data = inputs.qkv(w.B, w.Hq, w.Hkv, w.S, w.d, w.seed, w.dtype, w.q_scale)
+    log("inputs ready in %.1f s" % (time.perf_counter() - t0))
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
+
+    def dev(a):
+        t = torch.from_numpy(a)
+        return (t.view(torch.bfloat16) if w.dtype == "bf16" else t).cuda()
+
+    q, k, v = dev(data["q"]), dev(data["k"]), dev(data["v"])
+    o = torch.zeros((w.B, w.Hq, w.S, w.d), dtype=tdt, device="cuda")
+    lse = torch.zeros((w.B, w.Hq, w.S), dtype=torch.float32, device="cuda")
+    ra = RingAttention(w.B, w.Hq, w.Hkv, w.S, w.d, w.R, layout, tdt, w.causal, w.scale,
+                       rank0=w.rank0, n_ranks=w.ranks,
+                       handoff=rb.HANDOFF_COPY if args.handoff == "copy" else rb.HANDOFF_SWAP,
+                       merge_mode=rb.MERGE_FUSED if args.merge == "fused" else rb.MERGE_SEPARATE)
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        ra.run(q, k, v, o, lse)
+    torch.cuda.synchronize()
+
+    # per-launch timing of the block kernel through the library's hook
+    R, K = w.R, args.steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * R * K)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    handles = [(ctypes.c_void_p * (2 * R))(*[evs[s * 2 * R + i].cuda_event for i in range(2 * R)])
+               for s in range(K)]
+    log("timing %d steps" % K)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(K):
+        ra.args.hop_events = ctypes.cast(handles[s], ctypes.POINTER(ctypes.c_void_p))
+        ra.run(q, k, v, o, lse)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ra.args.hop_events = None
+    ms_per_step = wall / K * 1e3
+    hop_ms = np.array([[evs[s * 2 * R + 2 * h].elapsed_time(evs[s * 2 * R + 2 * h + 1])
+                        for h in range(R)] for s in range(K)])
+    pairs = hop_pairs(w, lcode)
+    flops_per_launch = [4.0 * w.d * w.B * w.Hq * p for p in pairs]
+    achieved = sum(flops_per_launch) * K / (hop_ms.sum() * 1e-3) / 1e12
+    value = w.metric_flops() / (ms_per_step * 1e-3) / 1e12
+    exact_flops = 4.0 * w.d * w.B * w.Hq * sum(pairs)
+    log("step %.2f ms, %.1f TFLOP/s; block kernel %.1f TFLOP/s" % (ms_per_step, value, achieved))
+
+    merge = None if args.no_merge_bench else merge_bench(torch, rb)
+    imbalance = {}
+    for name, code in (("contiguous", 0), ("striped", 1)):
+        W = rb.ra_causal_work(code, w.S, w.R)
+        imbalance[name] = float(W.max() / W.mean())
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (~%.0f s)" % args.cpu_seconds)
+        cpu = cpu_baseline(w, data, lcode, args.cpu_seconds)
+
+    line = {
+        "metric": "causal ring-attention fwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1))",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "S": w.S,
+                   "R": w.R, "layout": layout, "causal": w.causal, "query_ranks":
+                   list(range(w.rank0, w.rank0 + w.ranks)), "handoff": args.handoff,
+                   "merge": args.merge},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "exact_pair_tflops": round(exact_flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "attn_block16_kernel<128,bf16>",
+                     "launches": R * K, "avg_launch_ms": round(float(hop_ms.mean()), 4),
+                     "algorithmic_flops_per_launch": sum(flops_per_launch) / R},
+        "hop_ms": [round(float(x), 3) for x in hop_ms.mean(axis=0)],
+        "merge": merge,
+        "causal_imbalance_max_over_mean": imbalance,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,253 @@
+/*
+ * ra.h -- C ABI of the MI355X (gfx950) ring-attention library (libra.so).
+ *
+ * The library computes exact causal / non-causal attention the way a ring of
+ * R ranks does it: every rank keeps its query shard, key/value blocks travel
+ * hop by hop, and each arriving block's partial attention is folded into a
+ * running (O, m, l) with online softmax.  On one GPU the ring is emulated:
+ * all computed ranks run in one launch per hop and the hop-to-hop K/V
+ * hand-off is an on-device copy on a second HIP stream, overlapped with the
+ * compute of the current hop.
+ *
+ * Page citations (page title and section):
+ *  [ZZ] highthink.cn repost of the context-parallelism / Ring Attention
+ *       article, section "Zig Zag Ring Attention 通信和计算重叠": ring of
+ *       ranks, K/V passed to the next rank while the current block is
+ *       computed, causal rule, interleaved token assignment.
+ *  [DE] aiunderstanding.org "Sequenzparallelität und Ringaufmerksamkeit",
+ *       "Tiefer Einblick" and FAQ: contiguous split, online softmax with
+ *       running max and sum, blockwise result equals full attention, only
+ *       K/V move while queries stay.
+ *  [TH] Thai version of that guide, technical-insight section: running
+ *       maximum, running normaliser, rescaling of earlier partial sums.
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are HIP device pointers; "host" are host
+ *    pointers.  The caller allocates and frees every buffer.
+ *  - `stream` arguments are hipStream_t values passed as void* (NULL is the
+ *    null stream).  Calls are asynchronous: they return once the work is
+ *    enqueued.  Argument validation happens on the host before anything is
+ *    enqueued; on a non-OK status nothing was enqueued.
+ *  - A HIP launch/copy failure returns RA_ERR_HIP; ra_last_error() then
+ *    holds the HIP error text.  Faults inside kernels surface at the
+ *    caller's next synchronisation.  No C++ exception crosses the ABI.
+ *  - Outputs never alias inputs (ra_merge updates its accumulator in place).
+ *  - No floating-point atomics are used: results are bitwise reproducible
+ *    for identical arguments on the same device.
+ *  - Element dtypes: bf16 and fp16 (16-bit MFMA path), fp32 (fp32 MFMA path).
+ *    Head dimension d must be 64 or 128.  Rows (the last, d-long dimension)
+ *    must be contiguous and 16-byte aligned.
+ */
+#ifndef RA_H_
+#define RA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *ra_stream; /* a hipStream_t */
+
+typedef enum {
+  RA_OK = 0,
+  RA_ERR_INVALID_ARG = 1, /* null pointer, bad enum value, bad scalar          */
+  RA_ERR_SHAPE = 2,       /* sizes inconsistent (S % R, Hq % Hkv, d, ranks...)  */
+  RA_ERR_DTYPE = 3,       /* unknown dtype                                      */
+  RA_ERR_ALIGNMENT = 4,   /* pointer or row stride not 16-byte aligned          */
+  RA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required         */
+  RA_ERR_UNSUPPORTED = 6, /* valid request this build does not implement        */
+  RA_ERR_HIP = 7          /* a HIP runtime call failed                          */
+} ra_status;
+
+typedef enum { RA_LAYOUT_CONTIGUOUS = 0, RA_LAYOUT_STRIPED = 1 } ra_layout;
+typedef enum { RA_DT_BF16 = 0, RA_DT_FP16 = 1, RA_DT_FP32 = 2 } ra_dtype;
+/* How the next K/V block reaches a rank. COPY: an on-device copy on the copy
+ * stream into the rank's receive buffer (the emulated link); SWAP: the rank
+ * reads the resident block in place (no transfer; an upper bound). */
+typedef enum { RA_HANDOFF_COPY = 0, RA_HANDOFF_SWAP = 1 } ra_handoff;
+/* How each hop's partial is folded. FUSED: the block kernel continues the
+ * running online softmax from the accumulator; SEPARATE: ra_block_fwd writes
+ * the hop's partial and ra_merge folds it in. */
+typedef enum { RA_MERGE_FUSED = 0, RA_MERGE_SEPARATE = 1 } ra_merge_mode;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int ra_version(void);
+/* Static text for a status code. */
+const char *ra_status_string(ra_status s);
+/* Detail of the last non-OK status returned on this host thread ("" if none). */
+const char *ra_last_error(void);
+
+/*
+ * ra_layout_permute -- token <-> slot index maps of a sequence split over R
+ * ranks.  Slot p = r*n + j is local position j of rank r (n = S/R).
+ *   RA_LAYOUT_CONTIGUOUS ([DE] "Tiefer Einblick": each rank owns a contiguous
+ *     run of tokens):           fwd[p] = p
+ *   RA_LAYOUT_STRIPED ([ZZ] interleaved assignment, rank r holds r, r+R,
+ *     r+2R, ...):               fwd[r*n + j] = j*R + r
+ *   inv[fwd[p]] = p.
+ * fwd, inv: device int32[S] (inv may be NULL).  Requires S % R == 0,
+ * 1 <= R, S < 2^31.  Errors: RA_ERR_INVALID_ARG, RA_ERR_SHAPE, RA_ERR_HIP.
+ */
+ra_status ra_layout_permute(int32_t layout, int64_t S, int32_t R, int32_t *fwd,
+                            int32_t *inv, ra_stream stream);
+
+/*
+ * ra_layout_gather -- move rows from the original token order into rank
+ * shards using a map from ra_layout_permute ([ZZ], [DE]: each rank holds the
+ * Q, K and V rows of its own tokens).
+ *   x    device [B][H][S][d] elements of elem_bytes each (original order)
+ *   fwd  device int32[S] (slot -> token)
+ *   x_sh device [n_ranks][B][H][n][d], shard k holding rank rank0+k:
+ *        x_sh[k][b][h][j] = x[b][h][fwd[(rank0+k)*n + j]]
+ * elem_bytes in {1, 2, 4, 8}; (d*elem_bytes) % 16 == 0 and 16-byte aligned
+ * pointers give the vector path, anything else a scalar path.
+ * Errors: RA_ERR_INVALID_ARG, RA_ERR_SHAPE, RA_ERR_HIP.
+ */
+ra_status ra_layout_gather(const void *x, void *x_sh, const int32_t *fwd, int32_t elem_bytes,
+                           int64_t B, int64_t H, int64_t S, int64_t d, int32_t R, int32_t rank0,
+                           int32_t n_ranks, ra_stream stream);
+
+/*
+ * ra_layout_scatter -- inverse of ra_layout_gather for the ranks given:
+ *   x[b][h][fwd[(rank0+k)*n + j]] = x_sh[k][b][h][j]
+ * Rows of x owned by other ranks are left untouched.  Same arguments and
+ * errors as ra_layout_gather (x is the output here).
+ */
+ra_status ra_layout_scatter(const void *x_sh, void *x, const int32_t *fwd, int32_t elem_bytes,
+                            int64_t B, int64_t H, int64_t S, int64_t d, int32_t R,
+                            int32_t rank0, int32_t n_ranks, ra_stream stream);
+
+/*
+ * ra_block_fwd -- partial attention of one query shard against one K/V block:
+ * the work a rank does when a block arrives ([DE] "Tiefer Einblick": partial
+ * attention per arriving block; [TH]: running max and normaliser).
+ *
+ * For batch b, query head h (K/V head g = h / (Hq/Hkv)) and local query i,
+ * the allowed keys are A = { j : !causal || kgid(j) <= qgid(i) } with
+ * qgid(i) = q_gid0 + i*q_gid_step and kgid(j) = k_gid0 + j*k_gid_step
+ * ([ZZ]: a token attends only to tokens not after it; the diagonal is
+ * included).  With s_j = scale * <q_i, k_j> (fp32 accumulation of products of
+ * the input dtype):
+ *   m = max_{j in A} s_j (natural units, scale included)
+ *   l = sum_{j in A} exp(s_j - m)          (fp32, from unrounded p)
+ *   O = sum_{j in A} exp(s_j - m) v_j / l  (p rounded to the input dtype for
+ *                                           the PV product; fp32 accumulate)
+ * A row with no allowed key gets O = 0, m = -inf, l = 0.
+ *
+ * Layout: q element (b,h,i,c) at q + b*q_stride[0] + h*q_stride[1]
+ * + i*q_stride[2] + c (element strides); likewise k, v with Hkv heads and
+ * n_k rows, and o (fp32) with o_stride.  m, l are dense fp32 [B][Hq][n_q].
+ * All device pointers.  Requires Hq % Hkv == 0, d in {64,128}, n_q, n_k >= 0,
+ * the global-id steps >= 1, 16-byte aligned rows.
+ * Errors: RA_ERR_INVALID_ARG, RA_ERR_SHAPE, RA_ERR_DTYPE, RA_ERR_ALIGNMENT,
+ * RA_ERR_HIP.
+ */
+typedef struct {
+  const void *q, *k, *v;
+  int32_t dtype; /* ra_dtype */
+  int32_t B, Hq, Hkv, n_q, n_k, d;
+  int64_t q_stride[3], k_stride[3], v_stride[3];
+  float scale;
+  int32_t causal;
+  int64_t q_gid0, q_gid_step, k_gid0, k_gid_step;
+  float *o;
+  int64_t o_stride[3];
+  float *m, *l;
+} ra_block_args;
+
+ra_status ra_block_fwd(const ra_block_args *a, ra_stream stream);
+
+/*
+ * ra_merge -- online-softmax combine of two partials of the same rows, in
+ * place on the accumulator ([TH]: rescale the earlier partial sums when a
+ * larger maximum appears; [DE] FAQ: blockwise equals full attention):
+ *   m = max(m_a, m_b); w_a = l_a e^{m_a-m}; w_b = l_b e^{m_b-m};
+ *   l = w_a + w_b;     O = (w_a O_a + w_b O_b) / l
+ * (0, -inf, 0) is the identity; two empty rows stay (0, -inf, 0).
+ * o_*: device fp32 [rows][d] contiguous; m_*, l_*: device fp32 [rows].
+ * d % 4 == 0, 16-byte aligned o pointers.
+ * Errors: RA_ERR_INVALID_ARG, RA_ERR_SHAPE, RA_ERR_ALIGNMENT, RA_ERR_HIP.
+ */
+ra_status ra_merge(float *o_acc, float *m_acc, float *l_acc, const float *o_blk,
+                   const float *m_blk, const float *l_blk, int64_t rows, int32_t d,
+                   ra_stream stream);
+
+/*
+ * ra_finalize -- running state to outputs: out = O rounded to nearest even
+ * in `dtype`, lse = m + ln(l) (fp32, natural log; -inf for an empty row).
+ * o_acc device fp32 [rows][d]; out device [rows][d] of dtype; m, l, lse
+ * device fp32 [rows].  Errors as ra_merge, plus RA_ERR_DTYPE.
+ */
+ra_status ra_finalize(const float *o_acc, const float *m, const float *l, void *out,
+                      float *lse, int32_t dtype, int64_t rows, int32_t d, ra_stream stream);
+
+/*
+ * ra_ring_fwd -- the whole ring on one GPU ([ZZ]: every rank keeps its Q
+ * chunk, passes its K/V chunk to the next rank and receives the previous
+ * rank's, until every query has met every key; the transfer overlaps the
+ * compute of the current block).
+ *
+ * Computed query ranks r = rank0 .. rank0+n_ranks-1 (all R, or a single
+ * rank's share; rank0 + n_ranks <= R).  At hop h = 0..R-1 rank r holds the block of source rank
+ * s = (r - h) mod R.  Global token ids follow `layout` (contiguous: rank r,
+ * local j -> r*n + j; striped: j*R + r).
+ *   q_sh  device [n_ranks][B][Hq][n][d]   query shards of the computed ranks
+ *   k_sh, v_sh device [R][B][Hkv][n][d]   every source rank's K/V shard (on
+ *         one GPU they stand in for the other ranks' memory)
+ *   o     device [n_ranks][B][Hq][n][d] in dtype
+ *   lse   device fp32 [n_ranks][B][Hq][n] (natural log)
+ * handoff COPY: before hop h+1 each rank's receive buffer is filled, on the
+ * `copy` stream, with the block its ring predecessor holds at hop h, while
+ * the `compute` stream runs hop h; events order the two streams (no
+ * write-after-read on the double buffer).  SWAP reads blocks in place.
+ * The copy stream first waits for work already on the compute stream; the
+ * compute stream waits for the copy stream before the call's last kernel,
+ * so everything is complete when `compute` is.  Passing the same stream
+ * twice is allowed (serialised, same results).
+ * The workspace (device, ra_ring_fwd_workspace_size bytes, 256-byte
+ * aligned) holds the two receive buffers and the fp32 running state.
+ * COPY and SWAP give bitwise-identical outputs; FUSED and SEPARATE agree to
+ * rounding.
+ * Errors: RA_ERR_INVALID_ARG, RA_ERR_SHAPE, RA_ERR_DTYPE, RA_ERR_ALIGNMENT,
+ * RA_ERR_WORKSPACE, RA_ERR_HIP.
+ */
+typedef struct {
+  const void *q_sh, *k_sh, *v_sh;
+  int32_t dtype;  /* ra_dtype */
+  int32_t R, rank0, n_ranks;
+  int32_t B, Hq, Hkv, n, d;
+  float scale;
+  int32_t causal;
+  int32_t layout;     /* ra_layout */
+  int32_t handoff;    /* ra_handoff */
+  int32_t merge_mode; /* ra_merge_mode */
+  void *o;
+  float *lse;
+  /* Optional timing hook (host array of 2*R hipEvent_t created by the caller,
+   * or NULL): event 2h is recorded on `compute` right before hop h's block
+   * kernel and event 2h+1 right after it. */
+  void **hop_events;
+} ra_ring_args;
+
+/* Bytes of workspace ra_ring_fwd needs for these arguments (0 on invalid
+ * arguments; ra_last_error() says why). */
+size_t ra_ring_fwd_workspace_size(const ra_ring_args *a);
+
+ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_bytes,
+                      ra_stream compute, ra_stream copy);
+
+/*
+ * ra_causal_work -- per-rank count of allowed causal (query, key) pairs over
+ * the whole ring, W[r] for r < R (host int64 array of R entries), from the
+ * same block classification the kernels use ([ZZ]: the interleaved layout
+ * exists to even out this count across ranks).  Host-only, synchronous.
+ * Errors: RA_ERR_INVALID_ARG, RA_ERR_SHAPE.
+ */
+ra_status ra_causal_work(int32_t layout, int64_t S, int32_t R, int64_t *W);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RA_H_ */

@@ -1,0 +1,541 @@
+// api.cpp -- the C ABI of libra.so: host-side validation, status reporting,
+// and the ring driver that runs R hops on one GPU with the K/V hand-off on a
+// second stream.
+//
+// Ring structure: highthink.cn Ring Attention article, section "Zig Zag Ring
+// Attention 通信和计算重叠" (each rank keeps its Q chunk, computes attention
+// with the K/V it holds, sends that K/V to the next rank and receives the
+// previous rank's, until every query has met every key; the next block is
+// received while the current one is computed).  Folding of the per-hop
+// partials: aiunderstanding.org "Sequenzparallelität und Ringaufmerksamkeit",
+// "Tiefer Einblick", and its Thai version, technical-insight section.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <vector>
+
+#include "ra_internal.h"
+
+namespace ra {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+void clear_error() { g_err[0] = 0; }
+
+namespace {
+
+int elt_bytes(int dtype) {
+  switch (dtype) {
+    case RA_DT_BF16:
+    case RA_DT_FP16:
+      return 2;
+    case RA_DT_FP32:
+      return 4;
+    default:
+      return 0;
+  }
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+ra_status fail(ra_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+ra_status hip_fail(hipError_t e, const char *what) {
+  return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define RA_HIP(call, what)                     \
+  do {                                         \
+    hipError_t e_ = (call);                    \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+constexpr int64_t kMaxI32 = 2147483647;
+
+// Events used by the ring driver, created once per (thread, device) and
+// reused by later calls on the same thread.
+std::vector<hipEvent_t> *event_pool(int device, size_t need, hipError_t *err) {
+  static thread_local std::map<int, std::vector<hipEvent_t>> pools;
+  auto &v = pools[device];
+  while (v.size() < need) {
+    hipEvent_t e;
+    hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (r != hipSuccess) {
+      *err = r;
+      return nullptr;
+    }
+    v.push_back(e);
+  }
+  *err = hipSuccess;
+  return &v;
+}
+
+struct WsLayout {
+  size_t kbuf[2], vbuf[2], o_acc, m_acc, l_acc, o_blk, m_blk, l_blk, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const ra_ring_args *a) {
+  WsLayout w{};
+  const size_t elt = (size_t)elt_bytes(a->dtype);
+  const size_t blk = (size_t)a->B * a->Hkv * a->n * a->d;
+  const size_t kv_bytes = (size_t)a->n_ranks * blk * elt;
+  const size_t rows = (size_t)a->n_ranks * a->B * a->Hq * a->n;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  if (a->handoff == RA_HANDOFF_COPY && a->R > 1) {
+    w.kbuf[0] = take(kv_bytes);
+    w.kbuf[1] = take(kv_bytes);
+    w.vbuf[0] = take(kv_bytes);
+    w.vbuf[1] = take(kv_bytes);
+  }
+  w.o_acc = take(rows * a->d * sizeof(float));
+  w.m_acc = take(rows * sizeof(float));
+  w.l_acc = take(rows * sizeof(float));
+  if (a->merge_mode == RA_MERGE_SEPARATE) {
+    w.o_blk = take(rows * a->d * sizeof(float));
+    w.m_blk = take(rows * sizeof(float));
+    w.l_blk = take(rows * sizeof(float));
+  }
+  w.total = off;
+  return w;
+}
+
+ra_status check_ring(const ra_ring_args *a) {
+  if (!a) return fail(RA_ERR_INVALID_ARG, "args is NULL");
+  if (!elt_bytes(a->dtype)) return fail(RA_ERR_DTYPE, "unknown dtype %d", a->dtype);
+  if (a->layout != RA_LAYOUT_CONTIGUOUS && a->layout != RA_LAYOUT_STRIPED)
+    return fail(RA_ERR_INVALID_ARG, "unknown layout %d", a->layout);
+  if (a->handoff != RA_HANDOFF_COPY && a->handoff != RA_HANDOFF_SWAP)
+    return fail(RA_ERR_INVALID_ARG, "unknown handoff %d", a->handoff);
+  if (a->merge_mode != RA_MERGE_FUSED && a->merge_mode != RA_MERGE_SEPARATE)
+    return fail(RA_ERR_INVALID_ARG, "unknown merge_mode %d", a->merge_mode);
+  if (a->R < 1) return fail(RA_ERR_SHAPE, "R must be >= 1 (got %d)", a->R);
+  if (a->n_ranks < 1 || a->n_ranks > a->R)
+    return fail(RA_ERR_SHAPE, "n_ranks must be in [1, R] (got %d, R=%d)", a->n_ranks, a->R);
+  if (a->rank0 < 0 || a->rank0 + a->n_ranks > a->R)
+    return fail(RA_ERR_SHAPE, "ranks [rank0, rank0+n_ranks) must lie in [0, R) (rank0=%d)",
+                a->rank0);
+  if (a->B < 1 || a->Hq < 1 || a->Hkv < 1)
+    return fail(RA_ERR_SHAPE, "B, Hq, Hkv must be >= 1");
+  if (a->Hq % a->Hkv) return fail(RA_ERR_SHAPE, "Hq %% Hkv != 0 (%d, %d)", a->Hq, a->Hkv);
+  if (a->d != 64 && a->d != 128) return fail(RA_ERR_SHAPE, "d must be 64 or 128 (got %d)", a->d);
+  if (a->n < 0) return fail(RA_ERR_SHAPE, "n must be >= 0");
+  if ((int64_t)a->n * a->R > kMaxI32) return fail(RA_ERR_SHAPE, "S = n*R must be < 2^31");
+  if (!(a->scale > 0.f) || !std::isfinite(a->scale))
+    return fail(RA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (a->n > 0) {
+    if (!a->q_sh || !a->k_sh || !a->v_sh || !a->o || !a->lse)
+      return fail(RA_ERR_INVALID_ARG, "null tensor pointer");
+    if (!aligned16(a->q_sh) || !aligned16(a->k_sh) || !aligned16(a->v_sh) || !aligned16(a->o))
+      return fail(RA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  }
+  return RA_OK;
+}
+
+ra_status check_block(const ra_block_args *a) {
+  if (!a) return fail(RA_ERR_INVALID_ARG, "args is NULL");
+  const int elt = elt_bytes(a->dtype);
+  if (!elt) return fail(RA_ERR_DTYPE, "unknown dtype %d", a->dtype);
+  if (a->B < 1 || a->Hq < 1 || a->Hkv < 1)
+    return fail(RA_ERR_SHAPE, "B, Hq, Hkv must be >= 1");
+  if (a->Hq % a->Hkv) return fail(RA_ERR_SHAPE, "Hq %% Hkv != 0 (%d, %d)", a->Hq, a->Hkv);
+  if (a->d != 64 && a->d != 128) return fail(RA_ERR_SHAPE, "d must be 64 or 128 (got %d)", a->d);
+  if (a->n_q < 0 || a->n_k < 0) return fail(RA_ERR_SHAPE, "n_q, n_k must be >= 0");
+  if (a->q_gid_step < 1 || a->k_gid_step < 1)
+    return fail(RA_ERR_INVALID_ARG, "global-id steps must be >= 1");
+  if (!(a->scale > 0.f) || !std::isfinite(a->scale))
+    return fail(RA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (a->n_q == 0) return RA_OK;
+  if (!a->q || !a->o || !a->m || !a->l) return fail(RA_ERR_INVALID_ARG, "null tensor pointer");
+  if (a->n_k > 0 && (!a->k || !a->v)) return fail(RA_ERR_INVALID_ARG, "null k/v pointer");
+  if (!aligned16(a->q) || !aligned16(a->o) || (a->n_k > 0 && (!aligned16(a->k) || !aligned16(a->v))))
+    return fail(RA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  for (int i = 0; i < 3; ++i) {
+    if ((a->q_stride[i] * elt) % 16 || (a->k_stride[i] * elt) % 16 || (a->v_stride[i] * elt) % 16 ||
+        (a->o_stride[i] * 4) % 16)
+      return fail(RA_ERR_ALIGNMENT, "strides must keep rows 16-byte aligned");
+    if (a->q_stride[i] < 0 || a->k_stride[i] < 0 || a->v_stride[i] < 0 || a->o_stride[i] < 0)
+      return fail(RA_ERR_SHAPE, "negative stride");
+  }
+  if (a->q_stride[2] < a->d || a->o_stride[2] < a->d || (a->n_k > 0 && (a->k_stride[2] < a->d ||
+                                                                      a->v_stride[2] < a->d)))
+    return fail(RA_ERR_SHAPE, "token stride smaller than d");
+  return RA_OK;
+}
+
+}  // namespace
+}  // namespace ra
+
+using namespace ra;
+
+extern "C" {
+
+int ra_version(void) { return 100; }
+
+const char *ra_status_string(ra_status s) {
+  switch (s) {
+    case RA_OK:
+      return "RA_OK";
+    case RA_ERR_INVALID_ARG:
+      return "RA_ERR_INVALID_ARG";
+    case RA_ERR_SHAPE:
+      return "RA_ERR_SHAPE";
+    case RA_ERR_DTYPE:
+      return "RA_ERR_DTYPE";
+    case RA_ERR_ALIGNMENT:
+      return "RA_ERR_ALIGNMENT";
+    case RA_ERR_WORKSPACE:
+      return "RA_ERR_WORKSPACE";
+    case RA_ERR_UNSUPPORTED:
+      return "RA_ERR_UNSUPPORTED";
+    case RA_ERR_HIP:
+      return "RA_ERR_HIP";
+  }
+  return "RA_ERR_UNKNOWN";
+}
+
+const char *ra_last_error(void) { return g_err; }
+
+ra_status ra_layout_permute(int32_t layout, int64_t S, int32_t R, int32_t *fwd, int32_t *inv,
+                            ra_stream stream) {
+  clear_error();
+  if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED)
+    return fail(RA_ERR_INVALID_ARG, "unknown layout %d", layout);
+  if (R < 1 || S < 0 || S % R) return fail(RA_ERR_SHAPE, "need R >= 1, S >= 0, S %% R == 0");
+  if (S > kMaxI32) return fail(RA_ERR_SHAPE, "S must be < 2^31");
+  if (S > 0 && !fwd) return fail(RA_ERR_INVALID_ARG, "fwd is NULL");
+  RA_HIP(launch_layout_permute(layout, S, R, fwd, inv, (hipStream_t)stream), "layout kernel");
+  return RA_OK;
+}
+
+static ra_status layout_move(bool gather, const void *src, void *dst, const int32_t *fwd,
+                             int32_t elem_bytes, int64_t B, int64_t H, int64_t S, int64_t d,
+                             int32_t R, int32_t rank0, int32_t n_ranks, ra_stream stream) {
+  clear_error();
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+    return fail(RA_ERR_INVALID_ARG, "elem_bytes must be 1, 2, 4 or 8");
+  if (R < 1 || S < 0 || S % R) return fail(RA_ERR_SHAPE, "need R >= 1, S >= 0, S %% R == 0");
+  if (S > kMaxI32) return fail(RA_ERR_SHAPE, "S must be < 2^31");
+  if (B < 0 || H < 0 || d < 0) return fail(RA_ERR_SHAPE, "negative size");
+  if (rank0 < 0 || n_ranks < 0 || rank0 + n_ranks > R)
+    return fail(RA_ERR_SHAPE, "ranks [rank0, rank0+n_ranks) must lie in [0, R)");
+  if (B * H * S * d * n_ranks == 0) return RA_OK;
+  if (!src || !dst || !fwd) return fail(RA_ERR_INVALID_ARG, "null pointer");
+  RA_HIP(launch_layout_move(gather, src, dst, fwd, elem_bytes, B, H, S, d, R, rank0, n_ranks,
+                            (hipStream_t)stream),
+         "layout move kernel");
+  return RA_OK;
+}
+
+ra_status ra_layout_gather(const void *x, void *x_sh, const int32_t *fwd, int32_t elem_bytes,
+                           int64_t B, int64_t H, int64_t S, int64_t d, int32_t R, int32_t rank0,
+                           int32_t n_ranks, ra_stream stream) {
+  return layout_move(true, x, x_sh, fwd, elem_bytes, B, H, S, d, R, rank0, n_ranks, stream);
+}
+
+ra_status ra_layout_scatter(const void *x_sh, void *x, const int32_t *fwd, int32_t elem_bytes,
+                            int64_t B, int64_t H, int64_t S, int64_t d, int32_t R, int32_t rank0,
+                            int32_t n_ranks, ra_stream stream) {
+  return layout_move(false, x_sh, x, fwd, elem_bytes, B, H, S, d, R, rank0, n_ranks, stream);
+}
+
+ra_status ra_block_fwd(const ra_block_args *a, ra_stream stream) {
+  clear_error();
+  ra_status st = check_block(a);
+  if (st != RA_OK) return st;
+  if (a->n_q == 0) return RA_OK;
+  BatchParams p{};
+  p.q = a->q;
+  p.k = a->n_k > 0 ? a->k : a->q;  // never read when n_k == 0
+  p.v = a->n_k > 0 ? a->v : a->q;
+  p.q_zstride = 0;
+  p.kv_zstride = 0;
+  p.kv_idx0 = 0;
+  p.kv_idx_mod = 1;
+  p.qs_b = a->q_stride[0];
+  p.qs_h = a->q_stride[1];
+  p.qs_t = a->q_stride[2];
+  p.ks_b = a->k_stride[0];
+  p.ks_h = a->k_stride[1];
+  p.ks_t = a->k_stride[2];
+  p.vs_b = a->v_stride[0];
+  p.vs_h = a->v_stride[1];
+  p.vs_t = a->v_stride[2];
+  p.B = a->B;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.nq = a->n_q;
+  p.nk = a->n_k;
+  p.d = a->d;
+  p.nz = 1;
+  p.scale = a->scale;
+  p.causal = a->causal ? 1 : 0;
+  p.qg_add = a->q_gid0;
+  p.qg_z = 0;
+  p.q_step = a->q_gid_step;
+  p.kg_add = a->k_gid0;
+  p.kg_mult = 0;
+  p.k_step = a->k_gid_step;
+  p.kg_s0 = 0;
+  p.kg_smod = 1;
+  p.o = a->o;
+  p.o_zstride = 0;
+  p.os_b = a->o_stride[0];
+  p.os_h = a->o_stride[1];
+  p.os_t = a->o_stride[2];
+  p.m = a->m;
+  p.l = a->l;
+  p.ml_zstride = 0;
+  p.accumulate = 0;
+  RA_HIP(launch_block_fwd(p, a->dtype, (hipStream_t)stream), "block kernel");
+  return RA_OK;
+}
+
+ra_status ra_merge(float *o_acc, float *m_acc, float *l_acc, const float *o_blk,
+                   const float *m_blk, const float *l_blk, int64_t rows, int32_t d,
+                   ra_stream stream) {
+  clear_error();
+  if (rows < 0 || d < 0 || d % 4) return fail(RA_ERR_SHAPE, "rows >= 0 and d %% 4 == 0 required");
+  if (rows == 0 || d == 0) return RA_OK;
+  if (!o_acc || !m_acc || !l_acc || !o_blk || !m_blk || !l_blk)
+    return fail(RA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(o_acc) || !aligned16(o_blk))
+    return fail(RA_ERR_ALIGNMENT, "o pointers must be 16-byte aligned");
+  RA_HIP(launch_merge(o_acc, m_acc, l_acc, o_blk, m_blk, l_blk, rows, d, (hipStream_t)stream),
+         "merge kernel");
+  return RA_OK;
+}
+
+ra_status ra_finalize(const float *o_acc, const float *m, const float *l, void *out, float *lse,
+                      int32_t dtype, int64_t rows, int32_t d, ra_stream stream) {
+  clear_error();
+  if (!elt_bytes(dtype)) return fail(RA_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (rows < 0 || d < 0 || d % 4) return fail(RA_ERR_SHAPE, "rows >= 0 and d %% 4 == 0 required");
+  if (rows == 0 || d == 0) return RA_OK;
+  if (!o_acc || !m || !l || !out || !lse) return fail(RA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(o_acc)) return fail(RA_ERR_ALIGNMENT, "o_acc must be 16-byte aligned");
+  RA_HIP(launch_finalize(o_acc, m, l, out, lse, dtype, rows, d, (hipStream_t)stream),
+         "finalize kernel");
+  return RA_OK;
+}
+
+size_t ra_ring_fwd_workspace_size(const ra_ring_args *a) {
+  clear_error();
+  if (check_ring(a) != RA_OK) return 0;
+  return ws_layout(a).total;
+}
+
+ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_bytes,
+                      ra_stream compute_s, ra_stream copy_s) {
+  clear_error();
+  ra_status st = check_ring(a);
+  if (st != RA_OK) return st;
+  if (a->n == 0) return RA_OK;
+  const WsLayout L = ws_layout(a);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(RA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", L.total, workspace_bytes);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(RA_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+
+  hipStream_t cs = (hipStream_t)compute_s, xs = (hipStream_t)copy_s;
+  char *ws = (char *)workspace;
+  const int R = a->R, n = a->n, nr = a->n_ranks, r0 = a->rank0;
+  const bool contig = a->layout == RA_LAYOUT_CONTIGUOUS;
+  const bool copy = a->handoff == RA_HANDOFF_COPY && R > 1;
+  const int elt = elt_bytes(a->dtype);
+  const int64_t blk = (int64_t)a->B * a->Hkv * n * a->d;  // elements of one K (or V) block
+  const size_t blk_bytes = (size_t)blk * elt;
+  const int64_t qz = (int64_t)a->B * a->Hq * n * a->d;
+  const int64_t rows = (int64_t)nr * a->B * a->Hq * n;
+  float *o_acc = (float *)(ws + L.o_acc), *m_acc = (float *)(ws + L.m_acc),
+        *l_acc = (float *)(ws + L.l_acc);
+  float *o_blk = (float *)(ws + L.o_blk), *m_blk = (float *)(ws + L.m_blk),
+        *l_blk = (float *)(ws + L.l_blk);
+  const char *ksh = (const char *)a->k_sh, *vsh = (const char *)a->v_sh;
+  char *kb[2] = {ws + L.kbuf[0], ws + L.kbuf[1]};
+  char *vb[2] = {ws + L.vbuf[0], ws + L.vbuf[1]};
+
+  int dev = 0;
+  RA_HIP(hipGetDevice(&dev), "hipGetDevice");
+  hipError_t herr;
+  std::vector<hipEvent_t> *ev = event_pool(dev, (size_t)2 * R + 2, &herr);
+  if (!ev) return hip_fail(herr, "hipEventCreate");
+  hipEvent_t ev_entry = (*ev)[0], ev_join = (*ev)[1];
+  auto ev_comp = [&](int h) { return (*ev)[2 + 2 * h]; };
+  auto ev_copy = [&](int h) { return (*ev)[3 + 2 * h]; };
+
+  if (copy) {
+    RA_HIP(hipEventRecord(ev_entry, cs), "hipEventRecord");
+    RA_HIP(hipStreamWaitEvent(xs, ev_entry, 0), "hipStreamWaitEvent");
+  }
+
+  // block pointer that computed rank index k holds at hop h (copy mode)
+  auto front = [&](const char *sh, char *const *buf, int h, int k) -> const char * {
+    if (h == 0) return sh + (size_t)((r0 + k) % R) * blk_bytes;
+    return buf[(h - 1) & 1] + (size_t)k * blk_bytes;
+  };
+
+  BatchParams p{};
+  p.q = a->q_sh;
+  p.q_zstride = qz;
+  p.kv_zstride = blk;
+  p.qs_b = (int64_t)a->Hq * n * a->d;
+  p.qs_h = (int64_t)n * a->d;
+  p.qs_t = a->d;
+  p.ks_b = p.vs_b = (int64_t)a->Hkv * n * a->d;
+  p.ks_h = p.vs_h = (int64_t)n * a->d;
+  p.ks_t = p.vs_t = a->d;
+  p.B = a->B;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.nq = n;
+  p.nk = n;
+  p.d = a->d;
+  p.nz = nr;
+  p.scale = a->scale;
+  p.causal = a->causal ? 1 : 0;
+  p.qg_add = contig ? (int64_t)r0 * n : r0;
+  p.qg_z = contig ? n : 1;
+  p.q_step = contig ? 1 : R;
+  p.kg_add = 0;
+  p.kg_mult = contig ? n : 1;
+  p.k_step = contig ? 1 : R;
+  p.kg_smod = R;
+  p.o_zstride = qz;
+  p.os_b = p.qs_b;
+  p.os_h = p.qs_h;
+  p.os_t = a->d;
+  p.ml_zstride = (int64_t)a->B * a->Hq * n;
+
+  for (int h = 0; h < R; ++h) {
+    // ---- compute hop h: every computed rank r attends to the block of source (r - h) mod R
+    if (copy && h > 0) RA_HIP(hipStreamWaitEvent(cs, ev_copy(h - 1), 0), "hipStreamWaitEvent");
+    p.kg_s0 = ((r0 - h) % R + R) % R;
+    if (copy && h > 0) {
+      p.k = kb[(h - 1) & 1];
+      p.v = vb[(h - 1) & 1];
+      p.kv_idx0 = 0;
+      p.kv_idx_mod = nr;
+    } else if (copy) {
+      p.k = ksh;
+      p.v = vsh;
+      p.kv_idx0 = r0;
+      p.kv_idx_mod = R;
+    } else {
+      p.k = ksh;
+      p.v = vsh;
+      p.kv_idx0 = p.kg_s0;
+      p.kv_idx_mod = R;
+    }
+    const bool into_acc = a->merge_mode == RA_MERGE_FUSED || h == 0;
+    p.o = into_acc ? o_acc : o_blk;
+    p.m = into_acc ? m_acc : m_blk;
+    p.l = into_acc ? l_acc : l_blk;
+    p.accumulate = (a->merge_mode == RA_MERGE_FUSED && h > 0) ? 1 : 0;
+    if (a->hop_events)
+      RA_HIP(hipEventRecord((hipEvent_t)a->hop_events[2 * h], cs), "hipEventRecord");
+    RA_HIP(launch_block_fwd(p, a->dtype, cs), "block kernel");
+    if (a->hop_events)
+      RA_HIP(hipEventRecord((hipEvent_t)a->hop_events[2 * h + 1], cs), "hipEventRecord");
+    if (!into_acc)
+      RA_HIP(launch_merge(o_acc, m_acc, l_acc, o_blk, m_blk, l_blk, rows, a->d, cs),
+             "merge kernel");
+    if (!copy || h + 1 >= R) continue;
+    RA_HIP(hipEventRecord(ev_comp(h), cs), "hipEventRecord");
+    // ---- hand-off for hop h+1 on the copy stream: rank r receives what its
+    // ring predecessor r-1 holds now.  The destination buffer was last read by
+    // hop h-1's compute.
+    if (h >= 1) RA_HIP(hipStreamWaitEvent(xs, ev_comp(h - 1), 0), "hipStreamWaitEvent");
+    for (int t = 0; t < 2; ++t) {
+      const char *sh = t ? vsh : ksh;
+      char *const *buf = t ? vb : kb;
+      char *dst_base = buf[h & 1];
+      const char *run_src = nullptr;
+      char *run_dst = nullptr;
+      size_t run_len = 0;
+      for (int k = 0; k < nr; ++k) {
+        const int r = r0 + k;
+        const int rp = (r - 1 + R) % R;
+        const int kp = ((rp - r0) % R + R) % R;
+        const char *src = kp < nr ? front(sh, buf, h, kp)
+                                  : sh + (size_t)(((r - 1 - h) % R + R) % R) * blk_bytes;
+        char *dst = dst_base + (size_t)k * blk_bytes;
+        if (run_len && src == run_src + run_len && dst == run_dst + run_len) {
+          run_len += blk_bytes;
+          continue;
+        }
+        if (run_len)
+          RA_HIP(hipMemcpyAsync(run_dst, run_src, run_len, hipMemcpyDeviceToDevice, xs),
+                 "hand-off copy");
+        run_src = src;
+        run_dst = dst;
+        run_len = blk_bytes;
+      }
+      if (run_len)
+        RA_HIP(hipMemcpyAsync(run_dst, run_src, run_len, hipMemcpyDeviceToDevice, xs),
+               "hand-off copy");
+    }
+    RA_HIP(hipEventRecord(ev_copy(h), xs), "hipEventRecord");
+  }
+  if (copy) {
+    RA_HIP(hipEventRecord(ev_join, xs), "hipEventRecord");
+    RA_HIP(hipStreamWaitEvent(cs, ev_join, 0), "hipStreamWaitEvent");
+  }
+  RA_HIP(launch_finalize(o_acc, m_acc, l_acc, a->o, a->lse, a->dtype, rows, a->d, cs),
+         "finalize kernel");
+  return RA_OK;
+}
+
+ra_status ra_causal_work(int32_t layout, int64_t S, int32_t R, int64_t *W) {
+  clear_error();
+  if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED)
+    return fail(RA_ERR_INVALID_ARG, "unknown layout %d", layout);
+  if (R < 1 || S < 0 || S % R) return fail(RA_ERR_SHAPE, "need R >= 1, S >= 0, S %% R == 0");
+  if (!W) return fail(RA_ERR_INVALID_ARG, "W is NULL");
+  const int64_t n = S / R;
+  const bool contig = layout == RA_LAYOUT_CONTIGUOUS;
+  const int64_t step = contig ? 1 : R;
+  for (int32_t r = 0; r < R; ++r) {
+    int64_t total = 0;
+    const int64_t qg0 = contig ? (int64_t)r * n : r;
+    for (int32_t h = 0; h < R; ++h) {
+      const int32_t s = ((r - h) % R + R) % R;
+      const int64_t kg0 = contig ? (int64_t)s * n : s;
+      // allowed keys of query i form the prefix [0, (gq - kg0)/step + 1) of the block
+      for (int64_t i = 0; i < n; ++i) {
+        const int64_t gq = qg0 + i * step;
+        if (gq < kg0) continue;
+        const int64_t c = (gq - kg0) / step + 1;
+        total += c < n ? c : n;
+      }
+    }
+    W[r] = total;
+  }
+  return RA_OK;
+}
+
+}  // extern "C"

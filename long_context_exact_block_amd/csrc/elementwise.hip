@@ -1,0 +1,204 @@
+// elementwise.hip -- the bandwidth-bound kernels of the ring path: the
+// online-softmax combine of two partials, the final cast + log-sum-exp, the
+// token <-> slot index maps and the row gather/scatter between the original
+// token order and rank shards.
+//
+// Page citations (page title and section):
+//  * combine: Thai Ring Attention guide, technical-insight section (running
+//    maximum and normaliser; earlier partial sums rescaled when a larger
+//    maximum appears) and the German guide "Sequenzparallelität und
+//    Ringaufmerksamkeit", FAQ (this makes the blockwise result equal full
+//    attention);
+//  * index maps: highthink.cn Ring Attention article, section "Zig Zag Ring
+//    Attention 通信和计算重叠" (interleaved assignment: rank r holds tokens
+//    r, r+R, r+2R, ...) and the German guide, "Tiefer Einblick" (contiguous
+//    runs).
+#include <cmath>
+
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+// One thread per 4 consecutive floats of a row; d/4 threads share a row.
+// Reads O_a, O_b (8d bytes), writes O (4d), plus the row's (m, l) pairs.
+__global__ void __launch_bounds__(256) merge_kernel(float *__restrict__ o_acc,
+                                                    float *__restrict__ m_acc,
+                                                    float *__restrict__ l_acc,
+                                                    const float *__restrict__ o_blk,
+                                                    const float *__restrict__ m_blk,
+                                                    const float *__restrict__ l_blk, int64_t rows,
+                                                    int d4, int64_t total) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= total) return;
+  const int64_t row = tid / d4;
+  const int q = (int)(tid - row * d4);
+  const float ma = m_acc[row], mb = m_blk[row];
+  const float la = l_acc[row], lb = l_blk[row];
+  const float m = fmaxf(ma, mb);
+  float4 r;
+  float l;
+  if (m == -INFINITY) {  // both partials empty: stay the identity (0, -inf, 0)
+    r = make_float4(0.f, 0.f, 0.f, 0.f);
+    l = 0.f;
+  } else {
+    const float wa = (ma == -INFINITY) ? 0.f : la * __expf(ma - m);
+    const float wb = (mb == -INFINITY) ? 0.f : lb * __expf(mb - m);
+    l = wa + wb;
+    const float inv = 1.f / l;
+    const float ca = wa * inv, cb = wb * inv;
+    const float4 a = ((const float4 *)o_acc)[tid];
+    const float4 b = ((const float4 *)o_blk)[tid];
+    r.x = ca * a.x + cb * b.x;
+    r.y = ca * a.y + cb * b.y;
+    r.z = ca * a.z + cb * b.z;
+    r.w = ca * a.w + cb * b.w;
+  }
+  ((float4 *)o_acc)[tid] = r;
+  if (q == 0) {
+    m_acc[row] = m;
+    l_acc[row] = l;
+  }
+  (void)rows;
+}
+
+template <typename T>
+__device__ __forceinline__ T cast_out(float x);
+template <>
+__device__ __forceinline__ __bf16 cast_out<__bf16>(float x) {
+  return (__bf16)x;  // v_cvt_pk_bf16_f32: round to nearest even
+}
+template <>
+__device__ __forceinline__ _Float16 cast_out<_Float16>(float x) {
+  return (_Float16)x;  // round to nearest even
+}
+template <>
+__device__ __forceinline__ float cast_out<float>(float x) {
+  return x;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) finalize_kernel(const float *__restrict__ o_acc,
+                                                       const float *__restrict__ m,
+                                                       const float *__restrict__ l,
+                                                       T *__restrict__ out, float *__restrict__ lse,
+                                                       int d4, int64_t total) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= total) return;
+  const int64_t row = tid / d4;
+  const int q = (int)(tid - row * d4);
+  const float4 a = ((const float4 *)o_acc)[tid];
+  T *o = out + tid * 4;
+  o[0] = cast_out<T>(a.x);
+  o[1] = cast_out<T>(a.y);
+  o[2] = cast_out<T>(a.z);
+  o[3] = cast_out<T>(a.w);
+  if (q == 0) {
+    const float lv = l[row];
+    lse[row] = lv > 0.f ? m[row] + __logf(lv) : -INFINITY;
+  }
+}
+
+__global__ void layout_kernel(int layout, int64_t S, int32_t R, int64_t n, int32_t *fwd,
+                              int32_t *inv) {
+  const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= S) return;
+  const int64_t r = p / n, j = p - r * n;
+  const int64_t t = (layout == RA_LAYOUT_CONTIGUOUS) ? p : j * R + r;
+  fwd[p] = (int32_t)t;
+  if (inv) inv[t] = (int32_t)p;
+}
+
+// One thread per 16-byte chunk (vector path) or element (scalar path) of a
+// shard row.  Shard row (k, b, h, j) <-> token row fwd[(rank0+k)*n + j].
+template <typename U>
+__global__ void move_kernel(bool gather, const U *__restrict__ src, U *__restrict__ dst,
+                            const int32_t *__restrict__ fwd, int64_t BH, int64_t S, int64_t n,
+                            int64_t row_units, int32_t rank0, int64_t total) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= total) return;
+  const int64_t u = tid % row_units;
+  const int64_t shard_row = tid / row_units;  // ((k*BH) + bh)*n + j
+  const int64_t j = shard_row % n;
+  const int64_t kbh = shard_row / n;
+  const int64_t bh = kbh % BH;
+  const int64_t k = kbh / BH;
+  const int64_t tok = fwd[(rank0 + k) * n + j];
+  const int64_t orig = (bh * S + tok) * row_units + u;
+  if (gather)
+    dst[tid] = src[orig];
+  else
+    dst[orig] = src[tid];
+}
+
+inline unsigned blocks_for(int64_t total) { return (unsigned)((total + 255) / 256); }
+
+}  // namespace
+
+hipError_t launch_merge(float *o_acc, float *m_acc, float *l_acc, const float *o_blk,
+                        const float *m_blk, const float *l_blk, int64_t rows, int32_t d,
+                        hipStream_t s) {
+  const int64_t total = rows * (d / 4);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(merge_kernel, dim3(blocks_for(total)), dim3(256), 0, s, o_acc, m_acc, l_acc,
+                     o_blk, m_blk, l_blk, rows, d / 4, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const float *o_acc, const float *m, const float *l, void *out,
+                           float *lse, int dtype, int64_t rows, int32_t d, hipStream_t s) {
+  const int64_t total = rows * (d / 4);
+  if (total == 0) return hipSuccess;
+  if (dtype == RA_DT_BF16)
+    hipLaunchKernelGGL(finalize_kernel<__bf16>, dim3(blocks_for(total)), dim3(256), 0, s, o_acc, m,
+                       l, (__bf16 *)out, lse, d / 4, total);
+  else if (dtype == RA_DT_FP16)
+    hipLaunchKernelGGL(finalize_kernel<_Float16>, dim3(blocks_for(total)), dim3(256), 0, s, o_acc,
+                       m, l, (_Float16 *)out, lse, d / 4, total);
+  else
+    hipLaunchKernelGGL(finalize_kernel<float>, dim3(blocks_for(total)), dim3(256), 0, s, o_acc, m,
+                       l, (float *)out, lse, d / 4, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_layout_permute(int layout, int64_t S, int32_t R, int32_t *fwd, int32_t *inv,
+                                 hipStream_t s) {
+  if (S == 0) return hipSuccess;
+  hipLaunchKernelGGL(layout_kernel, dim3(blocks_for(S)), dim3(256), 0, s, layout, S, R, S / R,
+                     fwd, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_layout_move(bool gather, const void *src, void *dst, const int32_t *fwd,
+                              int32_t elem_bytes, int64_t B, int64_t H, int64_t S, int64_t d,
+                              int32_t R, int32_t rank0, int32_t n_ranks, hipStream_t s) {
+  const int64_t n = S / R;
+  const int64_t row_bytes = d * elem_bytes;
+  const int64_t rows = (int64_t)n_ranks * B * H * n;
+  if (rows == 0 || row_bytes == 0) return hipSuccess;
+  const bool vec = (row_bytes % 16 == 0) && ((uintptr_t)src % 16 == 0) && ((uintptr_t)dst % 16 == 0);
+  if (vec) {
+    const int64_t ru = row_bytes / 16, total = rows * ru;
+    hipLaunchKernelGGL(move_kernel<uint4>, dim3(blocks_for(total)), dim3(256), 0, s, gather,
+                       (const uint4 *)src, (uint4 *)dst, fwd, B * H, S, n, ru, rank0, total);
+  } else if (elem_bytes == 8) {
+    const int64_t total = rows * d;
+    hipLaunchKernelGGL(move_kernel<uint64_t>, dim3(blocks_for(total)), dim3(256), 0, s, gather,
+                       (const uint64_t *)src, (uint64_t *)dst, fwd, B * H, S, n, d, rank0, total);
+  } else if (elem_bytes == 4) {
+    const int64_t total = rows * d;
+    hipLaunchKernelGGL(move_kernel<uint32_t>, dim3(blocks_for(total)), dim3(256), 0, s, gather,
+                       (const uint32_t *)src, (uint32_t *)dst, fwd, B * H, S, n, d, rank0, total);
+  } else if (elem_bytes == 2) {
+    const int64_t total = rows * d;
+    hipLaunchKernelGGL(move_kernel<uint16_t>, dim3(blocks_for(total)), dim3(256), 0, s, gather,
+                       (const uint16_t *)src, (uint16_t *)dst, fwd, B * H, S, n, d, rank0, total);
+  } else {
+    const int64_t total = rows * d;
+    hipLaunchKernelGGL(move_kernel<uint8_t>, dim3(blocks_for(total)), dim3(256), 0, s, gather,
+                       (const uint8_t *)src, (uint8_t *)dst, fwd, B * H, S, n, d, rank0, total);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ra

@@ -1,0 +1,60 @@
+// ra_internal.h -- declarations shared by the host side of libra.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "ra.h"
+
+namespace ra {
+
+// A batch of nz (query shard, K/V block) problems with one shape, launched
+// together.  Problem z uses
+//   q          = q + z*q_zstride
+//   k, v       = k/v + ((kv_idx0 + z) % kv_idx_mod) * kv_zstride
+//   qgid(i)    = qg_add + z*qg_z + i*q_step
+//   kgid(j)    = kg_add + ((kg_s0 + z) % kg_smod)*kg_mult + j*k_step
+//   o, m, l    = + z*o_zstride / z*ml_zstride
+// which covers one public block call (nz = 1) and one ring hop over all
+// computed ranks (z = rank index, block index and key ids follow the ring).
+struct BatchParams {
+  const void *q, *k, *v;
+  int64_t q_zstride, kv_zstride;
+  int32_t kv_idx0, kv_idx_mod;
+  int64_t qs_b, qs_h, qs_t;
+  int64_t ks_b, ks_h, ks_t;
+  int64_t vs_b, vs_h, vs_t;
+  int32_t B, Hq, Hkv, nq, nk, d, nz;
+  float scale;
+  int32_t causal;
+  int64_t qg_add, qg_z, q_step;
+  int64_t kg_add, kg_mult, k_step;
+  int32_t kg_s0, kg_smod;
+  float *o;
+  int64_t o_zstride, os_b, os_h, os_t;
+  float *m, *l;
+  int64_t ml_zstride;
+  // 0: write this block's partial (O normalised, m, l).
+  // 1: continue the running state stored in o/m/l (same format) and write it
+  //    back -- online softmax carried across hops.
+  int32_t accumulate;
+};
+
+hipError_t launch_block_fwd(const BatchParams &p, int dtype, hipStream_t s);
+hipError_t launch_merge(float *o_acc, float *m_acc, float *l_acc, const float *o_blk,
+                        const float *m_blk, const float *l_blk, int64_t rows, int32_t d,
+                        hipStream_t s);
+hipError_t launch_finalize(const float *o_acc, const float *m, const float *l, void *out,
+                           float *lse, int dtype, int64_t rows, int32_t d, hipStream_t s);
+hipError_t launch_layout_permute(int layout, int64_t S, int32_t R, int32_t *fwd, int32_t *inv,
+                                 hipStream_t s);
+hipError_t launch_layout_move(bool gather, const void *src, void *dst, const int32_t *fwd,
+                              int32_t elem_bytes, int64_t B, int64_t H, int64_t S, int64_t d,
+                              int32_t R, int32_t rank0, int32_t n_ranks, hipStream_t s);
+
+// Per-thread detail text for ra_last_error().
+void set_error(const char *fmt, ...);
+void clear_error();
+
+}  // namespace ra

@@ -1,0 +1,148 @@
+"""The C ABI library: builds, loads, exports what include/ra.h declares, and
+rejects bad arguments on the host before touching the GPU (CPU only)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from long_context_exact_block_amd import binding as rb
+from long_context_exact_block_amd import build as rbuild
+from tests import oracle_pins as pins
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "ra.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    rbuild.build(force=False)
+    return rb.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("ra_layout_permute", "ra_block_fwd", "ra_merge", "ra_ring_fwd",
+              "ra_ring_fwd_workspace_size", "ra_status_string", "ra_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(rb.EXPORTED) == set(declared_functions())
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ra_version() >= 100
+    for code, name in rb.STATUS_NAMES.items():
+        assert lib.ra_status_string(code).decode() == name
+
+
+def _block(**kw):
+    a = rb.BlockArgs()
+    a.q = a.k = a.v = a.o = a.m = a.l = 4096
+    a.dtype, a.B, a.Hq, a.Hkv, a.n_q, a.n_k, a.d = rb.DT_BF16, 1, 4, 2, 8, 8, 128
+    for i, s in enumerate((4 * 8 * 128, 8 * 128, 128)):
+        a.q_stride[i] = a.o_stride[i] = s
+    for i, s in enumerate((2 * 8 * 128, 8 * 128, 128)):
+        a.k_stride[i] = a.v_stride[i] = s
+    a.scale, a.causal = 0.088, 1
+    a.q_gid0, a.q_gid_step, a.k_gid0, a.k_gid_step = 0, 1, 0, 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dtype", 9, 3), ("d", 96, 2), ("Hkv", 3, 2), ("Hq", 0, 2), ("n_q", -1, 2),
+    ("q_gid_step", 0, 1), ("scale", -1.0, 1), ("scale", float("nan"), 1), ("q", 0, 1),
+    ("k", 4097, 4), ("o", 4100, 4),
+])
+def test_block_fwd_rejects(lib, field, value, status):
+    a = _block(**{field: value})
+    st = lib.ra_block_fwd(ctypes.byref(a), None)
+    assert st == status, (st, rb.last_error())
+    assert rb.last_error()
+
+
+def test_block_fwd_rejects_bad_stride(lib):
+    a = _block()
+    a.q_stride[2] = 100  # rows no longer 16-byte aligned
+    assert lib.ra_block_fwd(ctypes.byref(a), None) == 4
+
+
+def _ring(**kw):
+    a = rb.RingArgs()
+    a.q_sh = a.k_sh = a.v_sh = a.o = a.lse = 4096
+    a.dtype, a.R, a.rank0, a.n_ranks = rb.DT_BF16, 8, 0, 8
+    a.B, a.Hq, a.Hkv, a.n, a.d = 1, 4, 2, 256, 128
+    a.scale, a.causal, a.layout, a.handoff, a.merge_mode = 0.088, 1, 1, 0, 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("R", 0, 2), ("n_ranks", 9, 2), ("rank0", 8, 2), ("rank0", -1, 2), ("rank0", 1, 2), ("layout", 5, 1),
+    ("handoff", 2, 1), ("merge_mode", 7, 1), ("dtype", -1, 3), ("d", 32, 2), ("Hkv", 3, 2),
+    ("q_sh", 0, 1), ("o", 4104, 4),
+])
+def test_ring_rejects(lib, field, value, status):
+    a = _ring(**{field: value})
+    st = lib.ra_ring_fwd(ctypes.byref(a), ctypes.c_void_p(4096), 1 << 40, None, None)
+    assert st == status, (st, rb.last_error())
+    assert lib.ra_ring_fwd_workspace_size(ctypes.byref(a)) == 0
+
+
+def test_ring_workspace_checks(lib):
+    a = _ring()
+    need = lib.ra_ring_fwd_workspace_size(ctypes.byref(a))
+    elt, blk = 2, 1 * 2 * 256 * 128
+    rows = 8 * 1 * 4 * 256
+    assert need >= 4 * 8 * blk * elt + rows * 128 * 4 + 2 * rows * 4
+    assert lib.ra_ring_fwd(ctypes.byref(a), None, need, None, None) == 5
+    assert lib.ra_ring_fwd(ctypes.byref(a), ctypes.c_void_p(4096), need - 1, None, None) == 5
+    assert lib.ra_ring_fwd(ctypes.byref(a), ctypes.c_void_p(4096 + 16), need, None, None) == 4
+    swap = _ring(handoff=1)
+    assert lib.ra_ring_fwd_workspace_size(ctypes.byref(swap)) < need
+    sep = _ring(merge_mode=1)
+    assert lib.ra_ring_fwd_workspace_size(ctypes.byref(sep)) > need
+
+
+def test_layout_rejects(lib):
+    assert lib.ra_layout_permute(0, 10, 4, ctypes.c_void_p(4096), None, None) == 2
+    assert lib.ra_layout_permute(3, 8, 4, ctypes.c_void_p(4096), None, None) == 1
+    assert lib.ra_layout_permute(1, 8, 4, None, None, None) == 1
+    assert lib.ra_layout_gather(4096, 8192, 4096, 3, 1, 1, 8, 4, 4, 0, 4, None) == 1
+    assert lib.ra_layout_gather(4096, 8192, 4096, 2, 1, 1, 8, 4, 4, 2, 3, None) == 2
+
+
+def test_merge_finalize_reject(lib):
+    assert lib.ra_merge(4096, 4096, 4096, 4096, 4096, 4096, 10, 6, None) == 2
+    assert lib.ra_merge(4100, 4096, 4096, 4096, 4096, 4096, 10, 8, None) == 4
+    assert lib.ra_merge(None, 4096, 4096, 4096, 4096, 4096, 10, 8, None) == 1
+    assert lib.ra_finalize(4096, 4096, 4096, 4096, 4096, 5, 10, 8, None) == 3
+
+
+@pytest.mark.parametrize("S,R", [(8, 2), (16, 4), (24, 4), (32, 8), (64, 8), (60, 6), (48, 3),
+                                 (128, 16), (1024, 4), (512, 64)])
+def test_causal_work_matches_oracle_brute_force(lib, ora, S, R):
+    """The library's per-rank causal work equals brute-force counting (bit-exact)."""
+    for layout in (rb.LAYOUT_CONTIGUOUS, rb.LAYOUT_STRIPED):
+        assert np.array_equal(rb.ra_causal_work(layout, S, R), ora.pair_counts(layout, S, R))
+
+
+@pytest.mark.parametrize("S,R", [(32768, 8), (131072, 8), (1048576, 8), (32768, 64)])
+def test_causal_work_closed_forms_at_full_size(lib, S, R):
+    for layout in (rb.LAYOUT_CONTIGUOUS, rb.LAYOUT_STRIPED):
+        W = rb.ra_causal_work(layout, S, R)
+        assert np.array_equal(W, pins.closed_form_counts(layout, S, R))
+        assert W.sum() == S * (S + 1) // 2
