@@ -138,7 +138,9 @@ ra_status ra_layout_scatter(const void *x_sh, void *x, const int32_t *fwd, int32
  *
  * Layout: q element (b,h,i,c) at q + b*q_stride[0] + h*q_stride[1]
  * + i*q_stride[2] + c (element strides); likewise k, v with Hkv heads and
- * n_k rows, and o (fp32) with o_stride.  m, l are dense fp32 [B][Hq][n_q].
+ * n_k rows, and o (fp32) with o_stride.  With v_packed = 1, v is the output
+ * of ra_pack_v for (B, Hkv, n_k, d) and v_stride is ignored; that path reads
+ * V with plain 16-byte loads and is the fast one.  m, l are dense fp32 [B][Hq][n_q].
  * All device pointers.  Requires Hq % Hkv == 0, d in {64,128}, n_q, n_k >= 0,
  * the global-id steps >= 1, 16-byte aligned rows.
  * Errors: RA_ERR_INVALID_ARG, RA_ERR_SHAPE, RA_ERR_DTYPE, RA_ERR_ALIGNMENT,
@@ -147,6 +149,7 @@ ra_status ra_layout_scatter(const void *x_sh, void *x, const int32_t *fwd, int32
 typedef struct {
   const void *q, *k, *v;
   int32_t dtype; /* ra_dtype */
+  int32_t v_packed; /* 0: v rows with v_stride; 1: v from ra_pack_v (bf16/fp16 only) */
   int32_t B, Hq, Hkv, n_q, n_k, d;
   int64_t q_stride[3], k_stride[3], v_stride[3];
   float scale;
@@ -158,6 +161,22 @@ typedef struct {
 } ra_block_args;
 
 ra_status ra_block_fwd(const ra_block_args *a, ra_stream stream);
+
+/*
+ * ra_pack_v -- repack V rows for the fast PV path of ra_block_fwd (the ring
+ * does this itself).  v: device [B][H][n][d] with element strides v_stride
+ * (d contiguous, 16-byte aligned rows); vp: device, ra_packed_v_bytes bytes.
+ * Packed layout: per (b, h) a [d][n_pad] array, n_pad = n rounded up to 64;
+ * row c, position q holds V[b][h][key][c] with key = q except that within
+ * every 16 positions the 2nd and 3rd groups of four keys are swapped (the
+ * order in which the probability matrix feeds the PV product); zero where
+ * key >= n.  bf16 / fp16 only.
+ * Errors: RA_ERR_INVALID_ARG, RA_ERR_SHAPE, RA_ERR_DTYPE, RA_ERR_ALIGNMENT,
+ * RA_ERR_HIP.
+ */
+size_t ra_packed_v_bytes(int32_t dtype, int32_t B, int32_t H, int32_t n, int32_t d);
+ra_status ra_pack_v(const void *v, void *vp, int32_t dtype, int32_t B, int32_t H, int32_t n,
+                    int32_t d, const int64_t v_stride[3], ra_stream stream);
 
 /*
  * ra_merge -- online-softmax combine of two partials of the same rows, in
@@ -207,7 +226,8 @@ ra_status ra_finalize(const float *o_acc, const float *m, const float *l, void *
  * so everything is complete when `compute` is.  Passing the same stream
  * twice is allowed (serialised, same results).
  * The workspace (device, ra_ring_fwd_workspace_size bytes, 256-byte
- * aligned) holds the two receive buffers and the fp32 running state.
+ * aligned) holds the packed V blocks (16-bit dtypes; see ra_pack_v), the
+ * two receive buffers and the fp32 running state.
  * COPY and SWAP give bitwise-identical outputs; FUSED and SEPARATE agree to
  * rounding.
  * Errors: RA_ERR_INVALID_ARG, RA_ERR_SHAPE, RA_ERR_DTYPE, RA_ERR_ALIGNMENT,

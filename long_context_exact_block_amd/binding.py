@@ -24,8 +24,9 @@ MERGE_FUSED, MERGE_SEPARATE = 0, 1
 LAYOUTS = {"contiguous": LAYOUT_CONTIGUOUS, "striped": LAYOUT_STRIPED}
 
 EXPORTED = ("ra_version", "ra_status_string", "ra_last_error", "ra_layout_permute",
-            "ra_layout_gather", "ra_layout_scatter", "ra_block_fwd", "ra_merge", "ra_finalize",
-            "ra_ring_fwd_workspace_size", "ra_ring_fwd", "ra_causal_work")
+            "ra_layout_gather", "ra_layout_scatter", "ra_block_fwd", "ra_packed_v_bytes",
+            "ra_pack_v", "ra_merge", "ra_finalize", "ra_ring_fwd_workspace_size", "ra_ring_fwd",
+            "ra_causal_work")
 
 
 class RAError(RuntimeError):
@@ -41,7 +42,8 @@ P = ctypes.c_void_p
 
 
 class BlockArgs(ctypes.Structure):
-    _fields_ = [("q", P), ("k", P), ("v", P), ("dtype", I32), ("B", I32), ("Hq", I32),
+    _fields_ = [("q", P), ("k", P), ("v", P), ("dtype", I32), ("v_packed", I32), ("B", I32),
+                ("Hq", I32),
                 ("Hkv", I32), ("n_q", I32), ("n_k", I32), ("d", I32), ("q_stride", I64 * 3),
                 ("k_stride", I64 * 3), ("v_stride", I64 * 3), ("scale", ctypes.c_float),
                 ("causal", I32), ("q_gid0", I64), ("q_gid_step", I64), ("k_gid0", I64),
@@ -76,6 +78,9 @@ def lib():
     L.ra_layout_gather.argtypes = [P, P, P, I32, I64, I64, I64, I64, I32, I32, I32, P]
     L.ra_layout_scatter.argtypes = [P, P, P, I32, I64, I64, I64, I64, I32, I32, I32, P]
     L.ra_block_fwd.argtypes = [ctypes.POINTER(BlockArgs), P]
+    L.ra_packed_v_bytes.argtypes = [I32, I32, I32, I32, I32]
+    L.ra_packed_v_bytes.restype = ctypes.c_size_t
+    L.ra_pack_v.argtypes = [P, P, I32, I32, I32, I32, I32, ctypes.POINTER(I64), P]
     L.ra_merge.argtypes = [P, P, P, P, P, P, I64, I32, P]
     L.ra_finalize.argtypes = [P, P, P, P, P, I32, I64, I32, P]
     L.ra_ring_fwd_workspace_size.argtypes = [ctypes.POINTER(RingArgs)]
@@ -83,7 +88,7 @@ def lib():
     L.ra_ring_fwd.argtypes = [ctypes.POINTER(RingArgs), P, ctypes.c_size_t, P, P]
     L.ra_causal_work.argtypes = [I32, I64, I32, P]
     for name in ("ra_layout_permute", "ra_layout_gather", "ra_layout_scatter", "ra_block_fwd",
-                 "ra_merge", "ra_finalize", "ra_ring_fwd", "ra_causal_work"):
+                 "ra_pack_v", "ra_merge", "ra_finalize", "ra_ring_fwd", "ra_causal_work"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -143,17 +148,18 @@ def ra_layout_scatter(x_sh, x, fwd, R: int, rank0: int = 0, n_ranks: int = -1, s
 
 
 def block_args(q, k, v, o, m, l, scale, causal, q_gid0=0, q_gid_step=1, k_gid0=0,
-               k_gid_step=1) -> BlockArgs:
+               k_gid_step=1, v_packed=False) -> BlockArgs:
     B, Hq, nq, d = q.shape
     _, Hkv, nk, _ = k.shape
     a = BlockArgs()
     a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
     a.dtype = dtype_code(q)
+    a.v_packed = int(bool(v_packed))
     a.B, a.Hq, a.Hkv, a.n_q, a.n_k, a.d = B, Hq, Hkv, nq, nk, d
     for i in range(3):
         a.q_stride[i] = q.stride(i)
         a.k_stride[i] = k.stride(i)
-        a.v_stride[i] = v.stride(i)
+        a.v_stride[i] = 0 if v_packed else v.stride(i)
         a.o_stride[i] = o.stride(i)
     a.scale = float(scale)
     a.causal = int(bool(causal))
@@ -163,10 +169,28 @@ def block_args(q, k, v, o, m, l, scale, causal, q_gid0=0, q_gid_step=1, k_gid0=0
 
 
 def ra_block_fwd(q, k, v, o, m, l, scale, causal, q_gid0=0, q_gid_step=1, k_gid0=0,
-                 k_gid_step=1, stream=None):
-    """q [B][Hq][nq][d], k, v [B][Hkv][nk][d] -> o fp32 [B][Hq][nq][d], m, l fp32 [B][Hq][nq]."""
-    a = block_args(q, k, v, o, m, l, scale, causal, q_gid0, q_gid_step, k_gid0, k_gid_step)
+                 k_gid_step=1, stream=None, v_packed=False):
+    """q [B][Hq][nq][d], k, v [B][Hkv][nk][d] -> o fp32 [B][Hq][nq][d], m, l fp32 [B][Hq][nq].
+
+    With v_packed=True, v is the buffer ra_pack_v filled for this K/V block."""
+    a = block_args(q, k, v, o, m, l, scale, causal, q_gid0, q_gid_step, k_gid0, k_gid_step,
+                   v_packed)
     _check(lib().ra_block_fwd(ctypes.byref(a), _stream(stream)))
+
+
+def ra_packed_v_bytes(dtype: int, B: int, H: int, n: int, d: int) -> int:
+    nb = lib().ra_packed_v_bytes(int(dtype), int(B), int(H), int(n), int(d))
+    if nb == 0 and last_error():
+        raise RAError(3, last_error())
+    return int(nb)
+
+
+def ra_pack_v(v, vp, stream=None):
+    """v [B][H][n][d] (bf16/fp16, strided rows) -> vp (uint8/16-bit buffer of
+    ra_packed_v_bytes bytes) in the packed layout."""
+    B, H, n, d = v.shape
+    st = (I64 * 3)(v.stride(0), v.stride(1), v.stride(2))
+    _check(lib().ra_pack_v(_ptr(v), _ptr(vp), dtype_code(v), B, H, n, d, st, _stream(stream)))
 
 
 def ra_merge(o_acc, m_acc, l_acc, o_blk, m_blk, l_blk, stream=None):

@@ -89,8 +89,11 @@ std::vector<hipEvent_t> *event_pool(int device, size_t need, hipError_t *err) {
 }
 
 struct WsLayout {
-  size_t kbuf[2], vbuf[2], o_acc, m_acc, l_acc, o_blk, m_blk, l_blk, total;
+  size_t vpack, kbuf[2], vbuf[2], o_acc, m_acc, l_acc, o_blk, m_blk, l_blk, total;
 };
+
+// The ring feeds 16-bit V to the block kernel in the packed layout.
+bool ring_packs_v(const ra_ring_args *a) { return a->dtype != RA_DT_FP32; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -98,7 +101,9 @@ WsLayout ws_layout(const ra_ring_args *a) {
   WsLayout w{};
   const size_t elt = (size_t)elt_bytes(a->dtype);
   const size_t blk = (size_t)a->B * a->Hkv * a->n * a->d;
-  const size_t kv_bytes = (size_t)a->n_ranks * blk * elt;
+  const size_t blkv = ring_packs_v(a) ? (size_t)a->B * a->Hkv * a->d * packed_n(a->n) : blk;
+  const size_t k_bytes = (size_t)a->n_ranks * blk * elt;
+  const size_t v_bytes = (size_t)a->n_ranks * blkv * elt;
   const size_t rows = (size_t)a->n_ranks * a->B * a->Hq * a->n;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -106,11 +111,12 @@ WsLayout ws_layout(const ra_ring_args *a) {
     off = align256(off + bytes);
     return at;
   };
+  if (ring_packs_v(a)) w.vpack = take((size_t)a->R * blkv * elt);
   if (a->handoff == RA_HANDOFF_COPY && a->R > 1) {
-    w.kbuf[0] = take(kv_bytes);
-    w.kbuf[1] = take(kv_bytes);
-    w.vbuf[0] = take(kv_bytes);
-    w.vbuf[1] = take(kv_bytes);
+    w.kbuf[0] = take(k_bytes);
+    w.kbuf[1] = take(k_bytes);
+    w.vbuf[0] = take(v_bytes);
+    w.vbuf[1] = take(v_bytes);
   }
   w.o_acc = take(rows * a->d * sizeof(float));
   w.m_acc = take(rows * sizeof(float));
@@ -165,6 +171,9 @@ ra_status check_block(const ra_block_args *a) {
   if (a->Hq % a->Hkv) return fail(RA_ERR_SHAPE, "Hq %% Hkv != 0 (%d, %d)", a->Hq, a->Hkv);
   if (a->d != 64 && a->d != 128) return fail(RA_ERR_SHAPE, "d must be 64 or 128 (got %d)", a->d);
   if (a->n_q < 0 || a->n_k < 0) return fail(RA_ERR_SHAPE, "n_q, n_k must be >= 0");
+  if (a->v_packed != 0 && a->v_packed != 1) return fail(RA_ERR_INVALID_ARG, "v_packed must be 0 or 1");
+  if (a->v_packed && a->dtype == RA_DT_FP32)
+    return fail(RA_ERR_UNSUPPORTED, "packed V is for bf16/fp16 inputs");
   if (a->q_gid_step < 1 || a->k_gid_step < 1)
     return fail(RA_ERR_INVALID_ARG, "global-id steps must be >= 1");
   if (!(a->scale > 0.f) || !std::isfinite(a->scale))
@@ -174,15 +183,17 @@ ra_status check_block(const ra_block_args *a) {
   if (a->n_k > 0 && (!a->k || !a->v)) return fail(RA_ERR_INVALID_ARG, "null k/v pointer");
   if (!aligned16(a->q) || !aligned16(a->o) || (a->n_k > 0 && (!aligned16(a->k) || !aligned16(a->v))))
     return fail(RA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  const int64_t vs_chk = a->v_packed ? 0 : 1;
   for (int i = 0; i < 3; ++i) {
-    if ((a->q_stride[i] * elt) % 16 || (a->k_stride[i] * elt) % 16 || (a->v_stride[i] * elt) % 16 ||
-        (a->o_stride[i] * 4) % 16)
+    if ((a->q_stride[i] * elt) % 16 || (a->k_stride[i] * elt) % 16 ||
+        (vs_chk * a->v_stride[i] * elt) % 16 || (a->o_stride[i] * 4) % 16)
       return fail(RA_ERR_ALIGNMENT, "strides must keep rows 16-byte aligned");
-    if (a->q_stride[i] < 0 || a->k_stride[i] < 0 || a->v_stride[i] < 0 || a->o_stride[i] < 0)
+    if (a->q_stride[i] < 0 || a->k_stride[i] < 0 || vs_chk * a->v_stride[i] < 0 ||
+        a->o_stride[i] < 0)
       return fail(RA_ERR_SHAPE, "negative stride");
   }
-  if (a->q_stride[2] < a->d || a->o_stride[2] < a->d || (a->n_k > 0 && (a->k_stride[2] < a->d ||
-                                                                      a->v_stride[2] < a->d)))
+  if (a->q_stride[2] < a->d || a->o_stride[2] < a->d ||
+      (a->n_k > 0 && (a->k_stride[2] < a->d || (!a->v_packed && a->v_stride[2] < a->d))))
     return fail(RA_ERR_SHAPE, "token stride smaller than d");
   return RA_OK;
 }
@@ -274,6 +285,7 @@ ra_status ra_block_fwd(const ra_block_args *a, ra_stream stream) {
   p.v = a->n_k > 0 ? a->v : a->q;
   p.q_zstride = 0;
   p.kv_zstride = 0;
+  p.kv_vzstride = 0;
   p.kv_idx0 = 0;
   p.kv_idx_mod = 1;
   p.qs_b = a->q_stride[0];
@@ -282,9 +294,17 @@ ra_status ra_block_fwd(const ra_block_args *a, ra_stream stream) {
   p.ks_b = a->k_stride[0];
   p.ks_h = a->k_stride[1];
   p.ks_t = a->k_stride[2];
-  p.vs_b = a->v_stride[0];
-  p.vs_h = a->v_stride[1];
-  p.vs_t = a->v_stride[2];
+  p.v_packed = a->v_packed;
+  if (a->v_packed) {
+    const int64_t np = packed_n(a->n_k);
+    p.vs_b = (int64_t)a->Hkv * a->d * np;
+    p.vs_h = (int64_t)a->d * np;
+    p.vs_t = np;
+  } else {
+    p.vs_b = a->v_stride[0];
+    p.vs_h = a->v_stride[1];
+    p.vs_t = a->v_stride[2];
+  }
   p.B = a->B;
   p.Hq = a->Hq;
   p.Hkv = a->Hkv;
@@ -312,6 +332,40 @@ ra_status ra_block_fwd(const ra_block_args *a, ra_stream stream) {
   p.ml_zstride = 0;
   p.accumulate = 0;
   RA_HIP(launch_block_fwd(p, a->dtype, (hipStream_t)stream), "block kernel");
+  return RA_OK;
+}
+
+size_t ra_packed_v_bytes(int32_t dtype, int32_t B, int32_t H, int32_t n, int32_t d) {
+  clear_error();
+  if (dtype != RA_DT_BF16 && dtype != RA_DT_FP16) {
+    fail(RA_ERR_DTYPE, "packed V is for bf16/fp16");
+    return 0;
+  }
+  if (B < 0 || H < 0 || n < 0 || d < 0) {
+    fail(RA_ERR_SHAPE, "negative size");
+    return 0;
+  }
+  return (size_t)B * H * d * packed_n(n) * 2;
+}
+
+ra_status ra_pack_v(const void *v, void *vp, int32_t dtype, int32_t B, int32_t H, int32_t n,
+                    int32_t d, const int64_t v_stride[3], ra_stream stream) {
+  clear_error();
+  if (dtype != RA_DT_BF16 && dtype != RA_DT_FP16)
+    return fail(RA_ERR_DTYPE, "packed V is for bf16/fp16");
+  if (B < 0 || H < 0 || n < 0) return fail(RA_ERR_SHAPE, "negative size");
+  if (d != 64 && d != 128) return fail(RA_ERR_SHAPE, "d must be 64 or 128 (got %d)", d);
+  if ((int64_t)B * H * n == 0) return RA_OK;
+  if (!v || !vp || !v_stride) return fail(RA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(v) || !aligned16(vp)) return fail(RA_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+  for (int i = 0; i < 3; ++i) {
+    if (v_stride[i] < 0) return fail(RA_ERR_SHAPE, "negative stride");
+    if ((v_stride[i] * 2) % 16) return fail(RA_ERR_ALIGNMENT, "strides must keep rows 16-byte aligned");
+  }
+  if (v_stride[2] < d) return fail(RA_ERR_SHAPE, "token stride smaller than d");
+  RA_HIP(launch_pack_v(v, vp, 2, (int64_t)B * H, H, n, d, v_stride[0], v_stride[1], v_stride[2],
+                       (hipStream_t)stream),
+         "pack kernel");
   return RA_OK;
 }
 
@@ -367,15 +421,20 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
   const bool contig = a->layout == RA_LAYOUT_CONTIGUOUS;
   const bool copy = a->handoff == RA_HANDOFF_COPY && R > 1;
   const int elt = elt_bytes(a->dtype);
-  const int64_t blk = (int64_t)a->B * a->Hkv * n * a->d;  // elements of one K (or V) block
+  const int64_t blk = (int64_t)a->B * a->Hkv * n * a->d;  // elements of one K block
   const size_t blk_bytes = (size_t)blk * elt;
+  const bool packed = ring_packs_v(a);
+  const int64_t n_pad = packed ? packed_n(n) : n;
+  const int64_t blkv = (int64_t)a->B * a->Hkv * a->d * n_pad;  // elements of one V block
+  const size_t blkv_bytes = (size_t)blkv * elt;
   const int64_t qz = (int64_t)a->B * a->Hq * n * a->d;
   const int64_t rows = (int64_t)nr * a->B * a->Hq * n;
   float *o_acc = (float *)(ws + L.o_acc), *m_acc = (float *)(ws + L.m_acc),
         *l_acc = (float *)(ws + L.l_acc);
   float *o_blk = (float *)(ws + L.o_blk), *m_blk = (float *)(ws + L.m_blk),
         *l_blk = (float *)(ws + L.l_blk);
-  const char *ksh = (const char *)a->k_sh, *vsh = (const char *)a->v_sh;
+  const char *ksh = (const char *)a->k_sh;
+  const char *vsh = packed ? (const char *)(ws + L.vpack) : (const char *)a->v_sh;
   char *kb[2] = {ws + L.kbuf[0], ws + L.kbuf[1]};
   char *vb[2] = {ws + L.vbuf[0], ws + L.vbuf[1]};
 
@@ -388,27 +447,42 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
   auto ev_comp = [&](int h) { return (*ev)[2 + 2 * h]; };
   auto ev_copy = [&](int h) { return (*ev)[3 + 2 * h]; };
 
+  // V of every source block in the packed layout the block kernel reads
+  if (packed)
+    RA_HIP(launch_pack_v(a->v_sh, ws + L.vpack, elt, (int64_t)R * a->B * a->Hkv, a->Hkv, n, a->d,
+                         (int64_t)a->Hkv * n * a->d, (int64_t)n * a->d, a->d, cs),
+           "pack kernel");
   if (copy) {
     RA_HIP(hipEventRecord(ev_entry, cs), "hipEventRecord");
     RA_HIP(hipStreamWaitEvent(xs, ev_entry, 0), "hipStreamWaitEvent");
   }
 
   // block pointer that computed rank index k holds at hop h (copy mode)
-  auto front = [&](const char *sh, char *const *buf, int h, int k) -> const char * {
-    if (h == 0) return sh + (size_t)((r0 + k) % R) * blk_bytes;
-    return buf[(h - 1) & 1] + (size_t)k * blk_bytes;
+  auto front = [&](const char *sh, char *const *buf, size_t bbytes, int h, int k) -> const char * {
+    if (h == 0) return sh + (size_t)((r0 + k) % R) * bbytes;
+    return buf[(h - 1) & 1] + (size_t)k * bbytes;
   };
 
   BatchParams p{};
   p.q = a->q_sh;
   p.q_zstride = qz;
   p.kv_zstride = blk;
+  p.kv_vzstride = blkv;
+  p.v_packed = packed ? 1 : 0;
   p.qs_b = (int64_t)a->Hq * n * a->d;
   p.qs_h = (int64_t)n * a->d;
   p.qs_t = a->d;
-  p.ks_b = p.vs_b = (int64_t)a->Hkv * n * a->d;
-  p.ks_h = p.vs_h = (int64_t)n * a->d;
-  p.ks_t = p.vs_t = a->d;
+  p.ks_b = (int64_t)a->Hkv * n * a->d;
+  p.ks_h = (int64_t)n * a->d;
+  p.ks_t = a->d;
+  p.vs_b = (int64_t)a->Hkv * a->d * n_pad;
+  p.vs_h = (int64_t)a->d * n_pad;
+  p.vs_t = n_pad;
+  if (!packed) {
+    p.vs_b = p.ks_b;
+    p.vs_h = p.ks_h;
+    p.vs_t = p.ks_t;
+  }
   p.B = a->B;
   p.Hq = a->Hq;
   p.Hkv = a->Hkv;
@@ -473,6 +547,7 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
     for (int t = 0; t < 2; ++t) {
       const char *sh = t ? vsh : ksh;
       char *const *buf = t ? vb : kb;
+      const size_t bb = t ? blkv_bytes : blk_bytes;
       char *dst_base = buf[h & 1];
       const char *run_src = nullptr;
       char *run_dst = nullptr;
@@ -481,11 +556,11 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
         const int r = r0 + k;
         const int rp = (r - 1 + R) % R;
         const int kp = ((rp - r0) % R + R) % R;
-        const char *src = kp < nr ? front(sh, buf, h, kp)
-                                  : sh + (size_t)(((r - 1 - h) % R + R) % R) * blk_bytes;
-        char *dst = dst_base + (size_t)k * blk_bytes;
+        const char *src = kp < nr ? front(sh, buf, bb, h, kp)
+                                  : sh + (size_t)(((r - 1 - h) % R + R) % R) * bb;
+        char *dst = dst_base + (size_t)k * bb;
         if (run_len && src == run_src + run_len && dst == run_dst + run_len) {
-          run_len += blk_bytes;
+          run_len += bb;
           continue;
         }
         if (run_len)
@@ -493,7 +568,7 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
                  "hand-off copy");
         run_src = src;
         run_dst = dst;
-        run_len = blk_bytes;
+        run_len = bb;
       }
       if (run_len)
         RA_HIP(hipMemcpyAsync(run_dst, run_src, run_len, hipMemcpyDeviceToDevice, xs),

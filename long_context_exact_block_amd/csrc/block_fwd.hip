@@ -46,228 +46,12 @@
 #include <cfloat>
 #include <cmath>
 
-#include "ra_internal.h"
+#include "attn_common.h"
 
 namespace ra {
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kTau = 8.0f;  // lazy rescale threshold (log2 units)
-
-template <bool BF16>
-struct Mfma16;
-
-template <>
-struct Mfma16<true> {
-  static __device__ __forceinline__ f32x16 mma(s16x8 a, s16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ s16x8 pack(const f32x16 &p, int base) {
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = (__bf16)p[base + e];
-    return __builtin_bit_cast(s16x8, r);
-  }
-};
-
-template <>
-struct Mfma16<false> {
-  static __device__ __forceinline__ f32x16 mma(s16x8 a, s16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ s16x8 pack(const f32x16 &p, int base) {
-    f16x8 r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = (_Float16)p[base + e];
-    return __builtin_bit_cast(s16x8, r);
-  }
-};
-
-// Lane l and lane l^32 hold two halves of the same query's keys.  After
-// v_permlane32_swap(x, x) the two results hold {x[l], x[l^32]} in some order
-// on every lane, so symmetric reductions need no lane select.
-__device__ __forceinline__ float half_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ bool wave_any(bool pred) {
-  return __builtin_amdgcn_ballot_w64(pred) != 0;
-}
-
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
-
-// Number of keys of the block allowed for a query with global id gq: the
-// allowed keys are always a prefix because key ids increase with j.
-__device__ __forceinline__ int key_prefix(const BatchParams &p, int64_t kg0, int64_t gq) {
-  if (!p.causal) return p.nk;
-  if (gq < kg0) return 0;
-  int64_t c = (gq - kg0) / p.k_step + 1;
-  return c < p.nk ? (int)c : p.nk;
-}
-
-struct Work {
-  int z, b, h, kvh, qtile;
-};
-
-// Workgroup index -> (problem, batch, head, query tile).  Heaviest causal
-// tiles first; when the number of K/V groups is a multiple of 8, all query
-// tiles of one K/V group land on the same XCD.
-__device__ __forceinline__ Work decode(const BatchParams &p, int ntq) {
-  const int hpg = p.Hq / p.Hkv;
-  const int NG = p.nz * p.B * p.Hkv;
-  const int L = blockIdx.x;
-  int trank, g, hh;
-  if ((NG & 7) == 0) {
-    const int xcd = L & 7, idx = L >> 3;
-    const int per_xcd = (NG >> 3) * hpg;
-    trank = idx / per_xcd;
-    const int rem = idx - trank * per_xcd;
-    const int gl = rem / hpg;
-    hh = rem - gl * hpg;
-    g = gl * 8 + xcd;
-  } else {
-    const int per_t = NG * hpg;
-    trank = L / per_t;
-    const int rem = L - trank * per_t;
-    g = rem / hpg;
-    hh = rem - g * hpg;
-  }
-  Work w;
-  w.qtile = p.causal ? (ntq - 1 - trank) : trank;
-  w.kvh = g % p.Hkv;
-  const int zb = g / p.Hkv;
-  w.b = zb % p.B;
-  w.z = zb / p.B;
-  w.h = w.kvh * hpg + hh;
-  return w;
-}
-
-// Row-state load/store shared by both kernels.  The lane owns query row i and,
-// in each 32x32 O^T tile dt, the 16 values d = 32dt + 8(r/4) + 4*half + r%4.
-template <int D>
-__device__ __forceinline__ void load_state(const BatchParams &p, const Work &w, int i, bool valid,
-                                           float c, f32x16 (&O)[D / 32], float &m_run,
-                                           float &m_top, float &lsum) {
-  const int hl = (threadIdx.x >> 5) & 1;
-  float m_acc = -INFINITY, l_acc = 0.f;
-  if (valid) {
-    const int64_t mi = w.z * p.ml_zstride + ((int64_t)w.b * p.Hq + w.h) * p.nq + i;
-    m_acc = p.m[mi];
-    l_acc = p.l[mi];
-  }
-  if (l_acc > 0.f) {
-    m_run = m_acc * kLog2e;
-    m_top = m_run;
-    lsum = hl ? 0.f : l_acc;
-    const float *orow = p.o + w.z * p.o_zstride + w.b * p.os_b + w.h * p.os_h + (int64_t)i * p.os_t;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const float4 v = *(const float4 *)(orow + 32 * dt + 8 * rg + 4 * hl);
-        O[dt][4 * rg + 0] = v.x * l_acc;
-        O[dt][4 * rg + 1] = v.y * l_acc;
-        O[dt][4 * rg + 2] = v.z * l_acc;
-        O[dt][4 * rg + 3] = v.w * l_acc;
-      }
-  } else {
-    m_run = -FLT_MAX;
-    m_top = -FLT_MAX;
-    lsum = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
-  }
-  (void)c;
-}
-
-template <int D>
-__device__ __forceinline__ void store_state(const BatchParams &p, const Work &w, int i, bool valid,
-                                            const f32x16 (&O)[D / 32], float m_run, float m_top,
-                                            float lsum) {
-  const int hl = (threadIdx.x >> 5) & 1;
-  const float lt = half_sum(lsum);
-  if (!valid) return;
-  float *orow = p.o + w.z * p.o_zstride + w.b * p.os_b + w.h * p.os_h + (int64_t)i * p.os_t;
-  float mo, lo, inv;
-  if (lt > 0.f) {
-    inv = 1.f / lt;
-    mo = m_top * kLn2;
-    lo = lt * __builtin_amdgcn_exp2f(m_run - m_top);
-  } else {
-    inv = 0.f;
-    mo = -INFINITY;
-    lo = 0.f;
-  }
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      float4 v;
-      v.x = O[dt][4 * rg + 0] * inv;
-      v.y = O[dt][4 * rg + 1] * inv;
-      v.z = O[dt][4 * rg + 2] * inv;
-      v.w = O[dt][4 * rg + 3] * inv;
-      *(float4 *)(orow + 32 * dt + 8 * rg + 4 * hl) = v;
-    }
-  if (hl == 0) {
-    const int64_t mi = w.z * p.ml_zstride + ((int64_t)w.b * p.Hq + w.h) * p.nq + i;
-    p.m[mi] = mo;
-    p.l[mi] = lo;
-  }
-}
-
-// Online-softmax update of one query block for one tile of 32*NKH keys held
-// in S[kh] (masked entries already -inf).  Returns probabilities in S.
-template <int D, int NKH>
-__device__ __forceinline__ void softmax_tile(f32x16 (&S)[NKH], f32x16 (&O)[D / 32], float c,
-                                             float &m_run, float &m_top, float &lsum) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kh = 0; kh < NKH; ++kh)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kh][r]);
-  mx = half_max(mx);
-  const float mt = mx * c;
-  m_top = fmaxf(m_top, mt);
-  if (wave_any(mt > m_run + kTau)) {
-    const float mn = fmaxf(m_run, mt);
-    const float al = __builtin_amdgcn_exp2f(m_run - mn);
-    lsum *= al;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) O[dt][r] *= al;
-    m_run = mn;
-  }
-  const float nm = -m_run;
-  float ls = 0.f;
-#pragma unroll
-  for (int kh = 0; kh < NKH; ++kh)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float pv = __builtin_amdgcn_exp2f(fmaf(S[kh][r], c, nm));
-      ls += pv;
-      S[kh][r] = pv;
-    }
-  lsum += ls;
-}
+using namespace attn;
 
 // ---------------------------------------------------------------------------
 // 16-bit kernel
@@ -294,7 +78,7 @@ __global__ void __launch_bounds__(256) attn_block16_kernel(BatchParams p, int nt
   const short *qp = (const short *)p.q + w.z * p.q_zstride + w.b * p.qs_b + w.h * p.qs_h;
   const int kvi = (p.kv_idx0 + w.z) % p.kv_idx_mod;
   const short *kp = (const short *)p.k + kvi * p.kv_zstride + w.b * p.ks_b + w.kvh * p.ks_h;
-  const short *vp = (const short *)p.v + kvi * p.kv_zstride + w.b * p.vs_b + w.kvh * p.vs_h;
+  const short *vp = (const short *)p.v + kvi * p.kv_vzstride + w.b * p.vs_b + w.kvh * p.vs_h;
   const int64_t qg0 = p.qg_add + w.z * p.qg_z;
   const int64_t kg0 = p.kg_add + (int64_t)((p.kg_s0 + w.z) % p.kg_smod) * p.kg_mult;
   const float c = p.scale * kLog2e;
@@ -474,7 +258,7 @@ __global__ void __launch_bounds__(256) attn_block32_kernel(BatchParams p, int nt
   const float *qp = (const float *)p.q + w.z * p.q_zstride + w.b * p.qs_b + w.h * p.qs_h;
   const int kvi = (p.kv_idx0 + w.z) % p.kv_idx_mod;
   const float *kp = (const float *)p.k + kvi * p.kv_zstride + w.b * p.ks_b + w.kvh * p.ks_h;
-  const float *vp = (const float *)p.v + kvi * p.kv_zstride + w.b * p.vs_b + w.kvh * p.vs_h;
+  const float *vp = (const float *)p.v + kvi * p.kv_vzstride + w.b * p.vs_b + w.kvh * p.vs_h;
   const int64_t qg0 = p.qg_add + w.z * p.qg_z;
   const int64_t kg0 = p.kg_add + (int64_t)((p.kg_s0 + w.z) % p.kg_smod) * p.kg_mult;
   const float c = p.scale * kLog2e;
@@ -566,6 +350,7 @@ hipError_t launch32(const BatchParams &p, hipStream_t s) {
 
 hipError_t launch_block_fwd(const BatchParams &p, int dtype, hipStream_t s) {
   if ((int64_t)p.nq * p.nz * p.B * p.Hq == 0) return hipSuccess;
+  if (p.v_packed) return launch_block_fwd_packed(p, dtype, s);
   if (dtype == RA_DT_BF16) return p.d == 64 ? launch16<64, true>(p, s) : launch16<128, true>(p, s);
   if (dtype == RA_DT_FP16)
     return p.d == 64 ? launch16<64, false>(p, s) : launch16<128, false>(p, s);

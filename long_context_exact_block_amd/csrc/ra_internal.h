@@ -12,7 +12,8 @@ namespace ra {
 // A batch of nz (query shard, K/V block) problems with one shape, launched
 // together.  Problem z uses
 //   q          = q + z*q_zstride
-//   k, v       = k/v + ((kv_idx0 + z) % kv_idx_mod) * kv_zstride
+//   k          = k + ((kv_idx0 + z) % kv_idx_mod) * kv_zstride
+//   v          = v + ((kv_idx0 + z) % kv_idx_mod) * kv_vzstride
 //   qgid(i)    = qg_add + z*qg_z + i*q_step
 //   kgid(j)    = kg_add + ((kg_s0 + z) % kg_smod)*kg_mult + j*k_step
 //   o, m, l    = + z*o_zstride / z*ml_zstride
@@ -20,7 +21,7 @@ namespace ra {
 // computed ranks (z = rank index, block index and key ids follow the ring).
 struct BatchParams {
   const void *q, *k, *v;
-  int64_t q_zstride, kv_zstride;
+  int64_t q_zstride, kv_zstride, kv_vzstride;
   int32_t kv_idx0, kv_idx_mod;
   int64_t qs_b, qs_h, qs_t;
   int64_t ks_b, ks_h, ks_t;
@@ -39,7 +40,20 @@ struct BatchParams {
   // 1: continue the running state stored in o/m/l (same format) and write it
   //    back -- online softmax carried across hops.
   int32_t accumulate;
+  // V layout: 0 = rows [token][d] (strides vs_*); 1 = packed transposed
+  // blocks from pack_v (vs_b, vs_h as given, vs_t = the packed row length).
+  int32_t v_packed;
 };
+
+// Packed V: for each (b, h) a [d][n_pad] array, n_pad = n rounded up to 64,
+// position q of a row holding key perm16(q) (the 2nd and 3rd groups of four
+// keys of every 16 swapped) and zero past n.  This is the key order in which
+// the PV product consumes probabilities, so every operand read is 16 bytes.
+constexpr int kPackAlign = 64;
+inline int64_t packed_n(int64_t n) { return (n + kPackAlign - 1) / kPackAlign * kPackAlign; }
+hipError_t launch_pack_v(const void *v, void *vp, int elt, int64_t BH, int64_t H, int64_t n,
+                         int64_t d, int64_t vs_b, int64_t vs_h, int64_t vs_t, hipStream_t s);
+hipError_t launch_block_fwd_packed(const BatchParams &p, int dtype, hipStream_t s);
 
 hipError_t launch_block_fwd(const BatchParams &p, int dtype, hipStream_t s);
 hipError_t launch_merge(float *o_acc, float *m_acc, float *l_acc, const float *o_blk,

@@ -64,13 +64,33 @@ def _block(**kw):
 @pytest.mark.parametrize("field,value,status", [
     ("dtype", 9, 3), ("d", 96, 2), ("Hkv", 3, 2), ("Hq", 0, 2), ("n_q", -1, 2),
     ("q_gid_step", 0, 1), ("scale", -1.0, 1), ("scale", float("nan"), 1), ("q", 0, 1),
-    ("k", 4097, 4), ("o", 4100, 4),
+    ("k", 4097, 4), ("o", 4100, 4), ("v_packed", 2, 1),
 ])
 def test_block_fwd_rejects(lib, field, value, status):
     a = _block(**{field: value})
     st = lib.ra_block_fwd(ctypes.byref(a), None)
     assert st == status, (st, rb.last_error())
     assert rb.last_error()
+
+
+def test_block_fwd_packed_v_rules(lib):
+    a = _block(v_packed=1, dtype=rb.DT_FP32)
+    assert lib.ra_block_fwd(ctypes.byref(a), None) == 6  # unsupported for fp32
+    a = _block(v_packed=1)
+    a.v_stride[2] = 3  # ignored for packed V
+    a.q = 0
+    assert lib.ra_block_fwd(ctypes.byref(a), None) == 1  # fails on q, not on v_stride
+
+
+def test_pack_v_sizes_and_rejects(lib):
+    assert lib.ra_packed_v_bytes(rb.DT_BF16, 2, 3, 100, 128) == 2 * 3 * 128 * 128 * 2
+    assert lib.ra_packed_v_bytes(rb.DT_FP16, 1, 1, 64, 64) == 64 * 64 * 2
+    assert lib.ra_packed_v_bytes(rb.DT_FP32, 1, 1, 64, 64) == 0
+    st = (rb.I64 * 3)(8 * 128, 128, 128)
+    assert lib.ra_pack_v(4096, 8192, rb.DT_FP32, 1, 1, 8, 128, st, None) == 3
+    assert lib.ra_pack_v(4096, 8192, rb.DT_BF16, 1, 1, 8, 96, st, None) == 2
+    assert lib.ra_pack_v(4098, 8192, rb.DT_BF16, 1, 1, 8, 128, st, None) == 4
+    assert lib.ra_pack_v(None, 8192, rb.DT_BF16, 1, 1, 8, 128, st, None) == 1
 
 
 def test_block_fwd_rejects_bad_stride(lib):

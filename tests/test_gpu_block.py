@@ -26,7 +26,7 @@ CASES = [
 ]
 
 
-def run_case(case, dtype, d, strided=False, seed=0):
+def run_case(case, dtype, d, strided=False, seed=0, packed=False):
     import torch
     name, B, Hq, Hkv, nq, nk, causal, qg0, qs, kg0, ks = case
     rng_seed = 100 + seed
@@ -49,7 +49,13 @@ def run_case(case, dtype, d, strided=False, seed=0):
     o = torch.full((B, Hq, nq, d), float("nan"), dtype=torch.float32, device="cuda")
     m = torch.full((B, Hq, nq), float("nan"), dtype=torch.float32, device="cuda")
     l = torch.full((B, Hq, nq), float("nan"), dtype=torch.float32, device="cuda")
-    rb.ra_block_fwd(q, k, v, o, m, l, scale, causal, qg0, qs, kg0, ks)
+    if packed:
+        nbytes = rb.ra_packed_v_bytes(rb.dtype_code(v), B, Hkv, nk, d)
+        vp = torch.empty(max(nbytes // 2, 8), dtype=v.dtype, device="cuda")
+        rb.ra_pack_v(v, vp)
+        rb.ra_block_fwd(q, k, vp, o, m, l, scale, causal, qg0, qs, kg0, ks, v_packed=True)
+    else:
+        rb.ra_block_fwd(q, k, v, o, m, l, scale, causal, qg0, qs, kg0, ks)
     torch.cuda.synchronize()
     import oracle
     ro, rm, rl = oracle.block_partial(qf, kf, vf, scale, causal, qg0, qs, kg0, ks)
@@ -72,9 +78,47 @@ def test_block_partial_matches_oracle(case, dtype, d):
     run_case(case, dtype, d)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_block_partial_packed_v_matches_oracle(case, dtype, d):
+    run_case(case, dtype, d, packed=True)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_block_strided_views(dtype):
     run_case(CASES[0], dtype, 128, strided=True)
+    if dtype == "bf16":
+        run_case(CASES[0], dtype, 128, strided=True, packed=True)
+
+
+def perm16(q):
+    """Packed position q -> key (the 2nd and 3rd groups of four of every 16 swapped)."""
+    quad = (q >> 2) & 3
+    sq = {0: 0, 1: 2, 2: 1, 3: 3}[quad]
+    return (q & ~15) | (sq << 2) | (q & 3)
+
+
+@pytest.mark.parametrize("n,d", [(64, 128), (200, 64), (1, 128), (130, 128)])
+def test_pack_v_layout_bit_exact(n, d):
+    import torch
+    B, H = 2, 3
+    rng = np.random.default_rng(n + d)
+    v = torch.from_numpy(rng.integers(-30000, 30000, (B, H, n, d)).astype(np.int16))
+    v = v.view(torch.bfloat16).cuda()
+    nbytes = rb.ra_packed_v_bytes(rb.DT_BF16, B, H, n, d)
+    n_pad = (n + 63) // 64 * 64
+    assert nbytes == B * H * d * n_pad * 2
+    vp = torch.full((nbytes // 2,), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    rb.ra_pack_v(v, vp)
+    got = vp.view(torch.int16).cpu().numpy().reshape(B, H, d, n_pad)
+    src = v.view(torch.int16).cpu().numpy()
+    expect = np.zeros((B, H, d, n_pad), np.int16)
+    for q in range(n_pad):
+        key = perm16(q)
+        if key < n:
+            expect[:, :, :, q] = src[:, :, key, :]
+    assert np.array_equal(got, expect)
 
 
 def test_block_deterministic():
