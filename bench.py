@@ -119,6 +119,49 @@ def merge_bench(torch, rb, rows=4 * 16 * 512 * 64, d=64, iters=20):
             PEAK_HBM_GBS}
 
 
+def block_only(torch, rb, w, layout, steps, warmup):
+    """One hop of the workload through ra_block_fwd: the first computed rank's query shard
+    against the block of the same source rank (hop 0), packed V, fresh state."""
+    n, d = w.n, w.d
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed)
+    q = torch.randn(w.B, w.Hq, n, d, device="cuda", generator=g).to(tdt)
+    k = torch.randn(w.B, w.Hkv, n, d, device="cuda", generator=g).to(tdt)
+    v = torch.randn(w.B, w.Hkv, n, d, device="cuda", generator=g).to(tdt)
+    packed = w.dtype != "fp32"
+    if packed:
+        vp = torch.empty(rb.ra_packed_v_bytes(rb.dtype_code(v), w.B, w.Hkv, n, d) // 2,
+                         dtype=tdt, device="cuda")
+        rb.ra_pack_v(v, vp)
+        v = vp
+    o = torch.empty(w.B, w.Hq, n, d, device="cuda")
+    m = torch.empty(w.B, w.Hq, n, device="cuda")
+    l = torch.empty(w.B, w.Hq, n, device="cuda")
+    r = w.rank0
+    contig = layout == "contiguous"
+    g0, step = (r * n, 1) if contig else (r, w.R)
+
+    def go():
+        rb.ra_block_fwd(q, k, v, o, m, l, w.scale, w.causal, g0, step, g0, step, v_packed=packed)
+
+    for _ in range(warmup):
+        go()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        go()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    pairs = (n * (n + 1) // 2) if w.causal else n * n
+    flops = 4.0 * d * w.B * w.Hq * pairs
+    print(json.dumps({"mode": "block_only", "workload": w.name, "layout": layout, "ms": ms,
+                      "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+                      "frac_of_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +174,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge-bench", action="store_true")
+    ap.add_argument("--block-only", action="store_true",
+                    help="time only the block kernel on one hop of the workload (query shard x "
+                         "one K/V block, packed V), on seeded device-side random inputs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -154,6 +200,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     rb.lib()  # fail loudly if the HIP library is missing
+
+    if args.block_only:
+        block_only(torch, rb, w, layout, args.steps, args.warmup)
+        return
 
     log("workload %s layout %s: generating inputs" % (w.name, layout))
     t0 = time.perf_counter()
@@ -244,7 +294,7 @@ def main():
         "exact_pair_tflops": round(exact_flops / (ms_per_step * 1e-3) / 1e12, 3),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "attn_block16_kernel<128,bf16>",
+                     "traffic": None, "kernel": "attn_packed_kernel<128,bf16>" if w.dtype != "fp32" else "attn_block32_kernel",
                      "launches": R * K, "avg_launch_ms": round(float(hop_ms.mean()), 4),
                      "algorithmic_flops_per_launch": sum(flops_per_launch) / R},
         "hop_ms": [round(float(x), 3) for x in hop_ms.mean(axis=0)],
