@@ -11,11 +11,14 @@
 //    order the PV product consumes probabilities (see packed_n), so the V^T
 //    operand of O^T += V^T P^T is a plain 16-byte LDS read like the K operand
 //    (the LDS transpose read delivers ~1/3 of the bytes per clock).
-//  * K and V^T tiles go from HBM straight into LDS with global_load_lds
-//    (no staging registers), double-buffered with one barrier per tile; 16-byte
-//    chunks are XOR-swizzled by row so every LDS read pattern is conflict-free.
-//  * 8 waves x 32 queries per workgroup (256 rows), two waves per SIMD, so one
-//    wave's softmax VALU work overlaps the other's MFMAs.
+//  * K and V^T tiles are prefetched two tiles ahead: each wave loads its
+//    share into registers right after the tile's barrier and writes it to a
+//    free LDS stage after its compute (three stages, one barrier per tile);
+//    16-byte chunks are XOR-swizzled by row for gfx950's 64 LDS banks so every
+//    read pattern is conflict-free.
+//  * 8 waves x 32 queries per workgroup (256 rows), two waves per SIMD; QK of
+//    tile t+1 is interleaved with the exponentials of tile t and PV of tile t
+//    with the row max of tile t+1.
 #include <cfloat>
 #include <cmath>
 
@@ -26,18 +29,9 @@ namespace {
 
 using namespace attn;
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-
 constexpr int kPW = 8;          // waves per workgroup
 constexpr int kPBM = kPW * 32;  // query rows per workgroup
 constexpr int kPBN = 64;        // keys per tile
-
-// 16 bytes per lane from global memory straight into LDS at lds_wave_base +
-// 16*lane (the LDS base must be the same for the whole wave).
-__device__ __forceinline__ void dma16(const void *g, void *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((glb_void_t *)g, (lds_void_t *)lds_wave_base, 16, 0, 0);
-}
 
 // key held by packed position q (an involution: quads 1 and 2 of each 16 swap)
 __device__ __forceinline__ int perm16(int q) {
@@ -56,12 +50,6 @@ __device__ __forceinline__ int chunk_swz(int row) {
   return ROW_BYTES == 256 ? (row & 15) : ((row >> 1) & 7);
 }
 
-// s_waitcnt with only vmcnt limited (expcnt, lgkmcnt left at their maximum)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 template <int D, bool BF16>
 __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq) {
   using M = Mfma16<BF16>;
@@ -72,7 +60,7 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
   constexpr int VROW = kPBN * 2;         // bytes per V^T row (64 keys)
   constexpr int VTILE = D * VROW;        // bytes of a V^T tile
   constexpr int STAGE = KTILE + VTILE;
-  constexpr int NSTAGE = 4;              // LDS stages: tiles t, t+1 read; t+2, t+3 landing
+  constexpr int NSTAGE = 3;              // LDS stages: tiles t, t+1 read; t+2 being written
   constexpr int KINSTR = KTILE / 1024;   // 1 KB wave-instructions per K tile
   constexpr int VINSTR = VTILE / 1024;
   constexpr int KPW = KINSTR / kPW;      // per wave per tile
@@ -159,23 +147,39 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
       const int dr = idx * 8 + (lane >> 3);
       vsrc[u] = vp + (int64_t)dr * p.vs_t + (((lane & 7) ^ chunk_swz<VROW>(dr)) * 8);
     }
-    auto issue = [&](int t, int stage) {
-      char *st = lds + stage * STAGE;
-      const int64_t koffs = (int64_t)t * kPBN * p.ks_t;
-      const bool tail = (t + 1) * kPBN > p.nk;  // ragged last tile: clamp rows
+    // One wave's share of a tile is KPW + VPW 16-byte-per-lane pieces.
+    // fetch() loads them into registers (asynchronous; a wave may have many
+    // loads in flight), commit() writes them into an LDS stage.  gfx950's
+    // global_load_lds stalls the issuing wave until its data has landed, so
+    // it is not used for the per-tile prefetch.
+    // (returned by value: an array captured by the lambdas would be demoted
+    // to scratch memory)
+    struct Staged {
+      uint4 v[KPW + VPW];
+    };
+    auto fetch = [&](int t) {
+      Staged g;
+      const bool tail = (t + 1) * kPBN > p.nk;  // ragged last tile: clamp K rows
 #pragma unroll
       for (int u = 0; u < KPW; ++u) {
-        const short *src = ksrc[u] + koffs;
+        const short *src = ksrc[u] + (int64_t)t * kPBN * p.ks_t;
         if (tail) {
           int j = t * kPBN + krow[u];
           j = j < p.nk ? j : p.nk - 1;
           src = kp + (int64_t)j * p.ks_t + klch[u] * 8;
         }
-        dma16(src, st + (wave + kPW * u) * 1024);
+        g.v[u] = *(const uint4 *)src;
       }
 #pragma unroll
-      for (int u = 0; u < VPW; ++u)
-        dma16(vsrc[u] + t * kPBN, st + KTILE + (wave + kPW * u) * 1024);
+      for (int u = 0; u < VPW; ++u) g.v[KPW + u] = *(const uint4 *)(vsrc[u] + t * kPBN);
+      return g;
+    };
+    auto commit = [&](const Staged &g, int stage) {
+      char *st = lds + stage * STAGE + lane * 16;
+#pragma unroll
+      for (int u = 0; u < KPW; ++u) *(uint4 *)(st + (wave + kPW * u) * 1024) = g.v[u];
+#pragma unroll
+      for (int u = 0; u < VPW; ++u) *(uint4 *)(st + KTILE + (wave + kPW * u) * 1024) = g.v[KPW + u];
     };
 
     // Per-lane LDS read offsets within a stage.  Row kh*32 + c32 (K) and
@@ -212,16 +216,9 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
       return m;
     };
 
-    // Prologue: up to three tiles in flight, tile 0 resident.
-    issue(0, 0);
-    if (ntiles > 1) issue(1, 1);
-    if (ntiles > 2) issue(2, 2);
-    if (ntiles > 2)
-      wait_vmcnt<2 * (KPW + VPW)>();
-    else if (ntiles > 1)
-      wait_vmcnt<KPW + VPW>();
-    else
-      wait_vmcnt<0>();
+    // Prologue: tiles 0 and 1 resident.
+    commit(fetch(0), 0);
+    if (ntiles > 1) commit(fetch(1), 1);
     __syncthreads();
     f32x16 S[2];
     float mx = -INFINITY;  // row max of S (before masking)
@@ -238,15 +235,16 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
     f32x16 S1[2];
     auto tile = [&](const int t, const int u, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
       // u == t % NSTAGE
-      if (t + 1 < ntiles) {
-        if (t + 2 < ntiles)
-          wait_vmcnt<KPW + VPW>();  // tile t+1 landed; t+2 may be in flight
-        else
-          wait_vmcnt<0>();
-        __syncthreads();
-        if (t + 3 < ntiles) issue(t + 3, (u + 3) % NSTAGE);
+      // Tile t+1 was committed at the end of tile t-1; after this barrier it
+      // is visible, and stage (t+2) % 3 -- last read in tile t-1 -- is free.
+      if (t + 1 < ntiles && t > 0) __syncthreads();
+      const bool pre = t + 2 < ntiles;
+      Staged g;
+      if (pre) g = fetch(t + 2);  // in flight during this tile's compute
+      if (t >= ntiles_w) {
+        if (pre) commit(g, (u + 2) % NSTAGE);
+        return;
       }
-      if (t >= ntiles_w) return;
       if (t >= nfull_w) {  // causal diagonal or ragged end of the block
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
@@ -280,24 +278,21 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int r = 0; r < 16; ++r) Sn[kh][r] = 0.f;
+      // K fragments in a rolling window: those of k-step ks + 1 are read
+      // while k-step ks is multiplied
       s16x8 ka[KS][2];
 #pragma unroll
-      for (int ks = 0; ks < KS / 2; ++ks)
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-          ka[ks][kh] = *(const s16x8 *)(stn + koff[ks] + kh * 32 * KROW);
+      for (int kh = 0; kh < 2; ++kh) ka[0][kh] = *(const s16x8 *)(stn + koff[0] + kh * 32 * KROW);
       float ls = 0.f;
       f32x16 pbuf;
       s16x8 P[4];
 #pragma unroll
       for (int step = 0; step < NSTEP; ++step) {
         const int ks = step >> 1, kh = step & 1;
-        if (step == 2) {  // second half of the K fragments
+        if (kh == 0 && ks + 1 < KS) {
 #pragma unroll
-          for (int k2 = KS / 2; k2 < KS; ++k2)
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-              ka[k2][h2] = *(const s16x8 *)(stn + koff[k2] + h2 * 32 * KROW);
+          for (int h2 = 0; h2 < 2; ++h2)
+            ka[ks + 1][h2] = *(const s16x8 *)(stn + koff[ks + 1] + h2 * 32 * KROW);
         }
         Sn[kh] = M::mma(ka[ks][kh], qf[ks], Sn[kh]);
 #pragma unroll
@@ -329,11 +324,14 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
         __builtin_amdgcn_sched_barrier(0);
       }
       mx = mxn;
+      if (pre) commit(g, (u + 2) % NSTAGE);
     };
-    for (int t = 0; t < ntiles; ++t) {
+    // two tiles per iteration so the S register sets swap roles instead of
+    // being copied
+    for (int t = 0; t < ntiles; t += 2) {
       tile(t, t % NSTAGE, S, S1);
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) S[kh] = S1[kh];
+      if (t + 1 >= ntiles) break;
+      tile(t + 1, (t + 1) % NSTAGE, S1, S);
     }
   }
   store_state<D>(p, w, i, valid, O, m_run, m_top, lsum);
@@ -379,7 +377,7 @@ template <int D, bool BF16>
 hipError_t launch_packed(const BatchParams &p, hipStream_t s) {
   const int ntq = (p.nq + kPBM - 1) / kPBM;
   const int64_t nwg = (int64_t)ntq * p.nz * p.B * p.Hq;
-  const size_t lds = (size_t)4 * (kPBN * D * 2 + D * kPBN * 2);
+  const size_t lds = (size_t)3 * (kPBN * D * 2 + D * kPBN * 2);
   static bool attr_set = false;  // more than 64 KB of LDS per workgroup must be opted into
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void *)attn_packed_kernel<D, BF16>,
