@@ -150,6 +150,9 @@ ra_status check_ring(const ra_ring_args *a) {
   if (a->Hq % a->Hkv) return fail(RA_ERR_SHAPE, "Hq %% Hkv != 0 (%d, %d)", a->Hq, a->Hkv);
   if (a->d != 64 && a->d != 128) return fail(RA_ERR_SHAPE, "d must be 64 or 128 (got %d)", a->d);
   if (a->n < 0) return fail(RA_ERR_SHAPE, "n must be >= 0");
+  if (a->dtype != RA_DT_FP32 && a->n > kMaxPackedKeys)
+    return fail(RA_ERR_UNSUPPORTED, "16-bit ring blocks are limited to %lld tokens (got %d)",
+                (long long)kMaxPackedKeys, a->n);
   if ((int64_t)a->n * a->R > kMaxI32) return fail(RA_ERR_SHAPE, "S = n*R must be < 2^31");
   if (!(a->scale > 0.f) || !std::isfinite(a->scale))
     return fail(RA_ERR_INVALID_ARG, "scale must be finite and > 0");
@@ -192,6 +195,9 @@ ra_status check_block(const ra_block_args *a) {
         a->o_stride[i] < 0)
       return fail(RA_ERR_SHAPE, "negative stride");
   }
+  if (a->v_packed && (a->n_k > kMaxPackedKeys || a->k_stride[2] > kMaxKRowStride))
+    return fail(RA_ERR_UNSUPPORTED, "packed V: n_k <= %lld and K token stride <= %lld",
+                (long long)kMaxPackedKeys, (long long)kMaxKRowStride);
   if (a->q_stride[2] < a->d || a->o_stride[2] < a->d ||
       (a->n_k > 0 && (a->k_stride[2] < a->d || (!a->v_packed && a->v_stride[2] < a->d))))
     return fail(RA_ERR_SHAPE, "token stride smaller than d");
@@ -331,6 +337,7 @@ ra_status ra_block_fwd(const ra_block_args *a, ra_stream stream) {
   p.l = a->l;
   p.ml_zstride = 0;
   p.accumulate = 0;
+  p.exact_m = 1;
   RA_HIP(launch_block_fwd(p, a->dtype, (hipStream_t)stream), "block kernel");
   return RA_OK;
 }
@@ -530,6 +537,8 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
     p.m = into_acc ? m_acc : m_blk;
     p.l = into_acc ? l_acc : l_blk;
     p.accumulate = (a->merge_mode == RA_MERGE_FUSED && h > 0) ? 1 : 0;
+    // the fused state only needs m + ln l; a separate partial is merged by m
+    p.exact_m = a->merge_mode == RA_MERGE_FUSED ? 0 : 1;
     if (a->hop_events)
       RA_HIP(hipEventRecord((hipEvent_t)a->hop_events[2 * h], cs), "hipEventRecord");
     RA_HIP(launch_block_fwd(p, a->dtype, cs), "block kernel");

@@ -28,6 +28,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;  // lazy rescale threshold (log2 units)
+// A lane's sum of one tile's probabilities above this means some probability
+// may exceed 2^kTau: the running maximum must be raised first.
+constexpr float kSumLimit = 256.0f;
 
 template <bool BF16>
 struct Mfma16;

@@ -11,16 +11,20 @@
 //    order the PV product consumes probabilities (see packed_n), so the V^T
 //    operand of O^T += V^T P^T is a plain 16-byte LDS read like the K operand
 //    (the LDS transpose read delivers ~1/3 of the bytes per clock).
-//  * K and V^T tiles are prefetched two tiles ahead: each wave loads its
-//    share into registers right after the tile's barrier and writes it to a
-//    free LDS stage after its compute (three stages, one barrier per tile);
-//    16-byte chunks are XOR-swizzled by row for gfx950's 64 LDS banks so every
-//    read pattern is conflict-free.
+//  * K tiles are loaded two tiles ahead and V^T tiles one tile ahead, by
+//    buffer loads that write LDS directly (no staging registers); two K and
+//    two V^T stages, one barrier per tile, the loop unrolled by two so every
+//    LDS offset is an immediate.  16-byte chunks are XOR-swizzled by row for
+//    gfx950's 64 LDS banks so every read pattern is conflict-free.
 //  * 8 waves x 32 queries per workgroup (256 rows), two waves per SIMD; QK of
-//    tile t+1 is interleaved with the exponentials of tile t and PV of tile t
-//    with the row max of tile t+1.
+//    tile t+1 is interleaved with the exponentials of tile t; K fragments are
+//    read two k-steps ahead and V^T fragments one PV group ahead.
+//  * Between hops only m + ln l matters, so the fused ring skips the per-tile
+//    row max: exponentials use the running maximum and a tile whose
+//    probabilities grow too large is redone after raising it.
 #include <cfloat>
 #include <cmath>
+#include <type_traits>
 
 #include "attn_common.h"
 
@@ -50,7 +54,31 @@ __device__ __forceinline__ int chunk_swz(int row) {
   return ROW_BYTES == 256 ? (row & 15) : ((row >> 1) & 7);
 }
 
-template <int D, bool BF16>
+// Raw buffer descriptor word 3 for gfx9-family parts: 32-bit dword data, no
+// swizzle, no index stride.
+constexpr int kBufWord3 = 0x00020000;
+// s_waitcnt immediate waiting for vmcnt == 0 only (lgkmcnt, expcnt at max)
+constexpr int kWaitVm0 = 0x0F70;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a raw buffer straight into LDS: lane l's bytes land
+// at dst + 16 l (dst is wave-uniform; it goes to M0).  A plain device function:
+// used directly in the kernel template, the builtin keeps the host pass from
+// emitting the kernel's launch stub.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, lds_void *dst, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, soff, 0, 0);
+}
+
+// EXACT: track the exact row maximum so that the stored m is the row max of
+// this call's scores (a block partial's statistic).  Otherwise the stored m is
+// the running reference maximum the stored l is relative to (same m + ln l),
+// which is all a state carried from hop to hop needs; the exponentials are then
+// taken against the running maximum without a per-tile row max, and a tile
+// whose probabilities would exceed 2^kTau (a larger maximum arrived) is redone
+// after rescaling.
+template <int D, bool BF16, bool EXACT>
 __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq) {
   using M = Mfma16<BF16>;
   constexpr int KS = D / 16;             // k-steps of the QK product
@@ -59,15 +87,13 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
   constexpr int KTILE = kPBN * KROW;     // bytes of a K tile
   constexpr int VROW = kPBN * 2;         // bytes per V^T row (64 keys)
   constexpr int VTILE = D * VROW;        // bytes of a V^T tile
-  constexpr int STAGE = KTILE + VTILE;
-  constexpr int NSTAGE = 3;              // LDS stages: tiles t, t+1 read; t+2 being written
-  constexpr int KINSTR = KTILE / 1024;   // 1 KB wave-instructions per K tile
-  constexpr int VINSTR = VTILE / 1024;
-  constexpr int KPW = KINSTR / kPW;      // per wave per tile
-  constexpr int VPW = VINSTR / kPW;
-  constexpr int KRPI = 1024 / KROW;      // K rows per wave-instruction
+  constexpr int VBASE = 2 * KTILE;       // LDS: K stages 0, 1, then V^T stages 0, 1
+  constexpr int KPW = KTILE / 1024 / kPW;  // 1 KB wave-loads per wave per K tile
+  constexpr int VPW = VTILE / 1024 / kPW;
+  constexpr int KRPI = 1024 / KROW;      // K rows per wave-load
   constexpr int CPR = D / 8;             // 16-byte chunks per K row
-  static_assert(KINSTR % kPW == 0 && VINSTR % kPW == 0, "tile must split over the waves");
+  constexpr int KA = 2;                  // K fragment read-ahead (k-steps)
+  static_assert(KPW * kPW * 1024 == KTILE && VPW * kPW * 1024 == VTILE, "tile must split over the waves");
   extern __shared__ __attribute__((aligned(1024))) char lds[];
 
   const Work w = decode(p, ntq);
@@ -129,62 +155,49 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
       }
     }
 
-    // Per-lane DMA sources for tile 0 (later tiles add a uniform offset) and
-    // the matching LDS destinations (uniform per wave).
-    const short *ksrc[KPW];
-    int krow[KPW], klch[KPW];
+    // Tile loads go through buffer descriptors: the per-lane byte offsets are
+    // fixed, the tile moves the (scalar) base, and K rows past the end of the
+    // block read as zero (they are masked).  Offsets fit in 32 bits: the host
+    // bounds the K row stride and the packed V row length.
+    const uint32_t krow_b = (uint32_t)p.ks_t * 2;
+    uint32_t kvo[KPW];
 #pragma unroll
     for (int u = 0; u < KPW; ++u) {
       const int idx = wave + kPW * u;
-      krow[u] = idx * KRPI + lane / CPR;
-      klch[u] = (lane % CPR) ^ chunk_swz<KROW>(krow[u]);
-      ksrc[u] = kp + (int64_t)krow[u] * p.ks_t + klch[u] * 8;
+      const int row = idx * KRPI + lane / CPR;
+      const int ch = (lane % CPR) ^ chunk_swz<KROW>(row);
+      kvo[u] = row * krow_b + ch * 16;
     }
-    const short *vsrc[VPW];
+    uint32_t vvo[VPW];
 #pragma unroll
     for (int u = 0; u < VPW; ++u) {
       const int idx = wave + kPW * u;
       const int dr = idx * 8 + (lane >> 3);
-      vsrc[u] = vp + (int64_t)dr * p.vs_t + (((lane & 7) ^ chunk_swz<VROW>(dr)) * 8);
+      vvo[u] = dr * ((uint32_t)p.vs_t * 2) + (((lane & 7) ^ chunk_swz<VROW>(dr)) * 16);
     }
-    // One wave's share of a tile is KPW + VPW 16-byte-per-lane pieces.
-    // fetch() loads them into registers (asynchronous; a wave may have many
-    // loads in flight), commit() writes them into an LDS stage.  gfx950's
-    // global_load_lds stalls the issuing wave until its data has landed, so
-    // it is not used for the per-tile prefetch.
-    // (returned by value: an array captured by the lambdas would be demoted
-    // to scratch memory)
-    struct Staged {
-      uint4 v[KPW + VPW];
+    const auto vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)vp, 0, (int)((uint32_t)D * (uint32_t)p.vs_t * 2u), kBufWord3);
+    // One wave's share of K tile tk / V^T tile tv goes straight into an LDS
+    // stage (buffer loads with the LDS destination in M0: lane l's 16 bytes
+    // land at base + 16 l, so the swizzle is applied on the source side).
+    // Completion is awaited (vmcnt) before the barrier that publishes the stage.
+    auto load_k = [&](int tk, int kstage) {
+      const int rows = min(p.nk - tk * kPBN, kPBN);
+      const auto krsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(kp + (int64_t)tk * kPBN * p.ks_t), 0, (int)(rows * krow_b), kBufWord3);
+#pragma unroll
+      for (int u = 0; u < KPW; ++u)
+        dma16(krsrc, (lds_void *)(lds + kstage * KTILE + kPW * 1024 * u + wave * 1024), kvo[u], 0);
     };
-    auto fetch = [&](int t) {
-      Staged g;
-      const bool tail = (t + 1) * kPBN > p.nk;  // ragged last tile: clamp K rows
+    auto load_v = [&](int tv, int vstage) {
 #pragma unroll
-      for (int u = 0; u < KPW; ++u) {
-        const short *src = ksrc[u] + (int64_t)t * kPBN * p.ks_t;
-        if (tail) {
-          int j = t * kPBN + krow[u];
-          j = j < p.nk ? j : p.nk - 1;
-          src = kp + (int64_t)j * p.ks_t + klch[u] * 8;
-        }
-        g.v[u] = *(const uint4 *)src;
-      }
-#pragma unroll
-      for (int u = 0; u < VPW; ++u) g.v[KPW + u] = *(const uint4 *)(vsrc[u] + t * kPBN);
-      return g;
-    };
-    auto commit = [&](const Staged &g, int stage) {
-      char *st = lds + stage * STAGE + lane * 16;
-#pragma unroll
-      for (int u = 0; u < KPW; ++u) *(uint4 *)(st + (wave + kPW * u) * 1024) = g.v[u];
-#pragma unroll
-      for (int u = 0; u < VPW; ++u) *(uint4 *)(st + KTILE + (wave + kPW * u) * 1024) = g.v[KPW + u];
+      for (int u = 0; u < VPW; ++u)
+        dma16(vrsrc, (lds_void *)(lds + VBASE + vstage * VTILE + kPW * 1024 * u + wave * 1024),
+              vvo[u], tv * kPBN * 2);
     };
 
-    // Per-lane LDS read offsets within a stage.  Row kh*32 + c32 (K) and
-    // 32dt + c32 (V^T) share the swizzle of row c32, so kh and dt become
-    // immediate offsets.
+    // Per-lane LDS read offsets.  Row kh*32 + c32 (K) and 32dt + c32 (V^T)
+    // share the swizzle of row c32, so kh, dt and the stage are immediates.
     int koff[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -192,21 +205,8 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
     int voff[4];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4)  // q4 = 2*kh + cc -> logical chunk 2*q4 + hl
-      voff[q4] = KTILE + c32 * VROW + (((2 * q4 + hl) ^ chunk_swz<VROW>(c32)) << 4);
+      voff[q4] = VBASE + c32 * VROW + (((2 * q4 + hl) ^ chunk_swz<VROW>(c32)) << 4);
 
-    // S^T = K Q^T for tile t into dst (prologue only; the loop interleaves it)
-    auto qk = [&](int t, f32x16 (&dst)[2]) {
-      const char *st = lds + (t % NSTAGE) * STAGE;
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dst[kh][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-          dst[kh] = M::mma(*(const s16x8 *)(st + koff[ks] + kh * 32 * KROW), qf[ks], dst[kh]);
-    };
     auto rowmax = [&](const f32x16 (&x)[2]) {
       float m = -INFINITY;
 #pragma unroll
@@ -215,37 +215,76 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
         for (int r = 0; r < 16; ++r) m = fmaxf(m, x[kh][r]);
       return m;
     };
+    // probabilities of tile S against the running maximum, packed for the PV
+    // product; returns this lane's sum of them
+    auto probs = [&](const f32x16 (&S)[2], s16x8 (&P)[4]) {
+      const float nm = -m_run;
+      float ls = 0.f;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x16 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pb[e] = __builtin_amdgcn_exp2f(fmaf(S[q4 >> 1][8 * (q4 & 1) + e], c, nm));
+          ls += pb[e];
+        }
+        P[q4] = M::pack(pb, 0);
+      }
+      return ls;
+    };
+    auto rescale = [&](float mt) {  // running maximum -> max(m_run, mt)
+      const float mn = fmaxf(m_run, mt);
+      const float al = __builtin_amdgcn_exp2f(m_run - mn);
+      lsum *= al;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[dt][r] *= al;
+      m_run = mn;
+    };
 
-    // Prologue: tiles 0 and 1 resident.
-    commit(fetch(0), 0);
-    if (ntiles > 1) commit(fetch(1), 1);
+    // Prologue: K tiles 0 and 1, V^T tile 0 resident; S^T of tile 0.
+    load_k(0, 0);
+    if (ntiles > 1) load_k(1, 1);
+    load_v(0, 0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    f32x16 S[2];
-    float mx = -INFINITY;  // row max of S (before masking)
+    f32x16 S[2], S1[2];
+    float mx = -INFINITY;  // EXACT: row max of the next tile's S (before masking)
     if (0 < ntiles_w) {
-      qk(0, S);
-      mx = rowmax(S);
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[kh][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+          S[kh] = M::mma(*(const s16x8 *)(lds + koff[ks] + kh * 32 * KROW), qf[ks], S[kh]);
+      if (EXACT) mx = rowmax(S);
     }
 
-    // Iteration t: softmax and PV of tile t, overlapped with QK of tile t+1
-    // and the row max of tile t+1.  Stage (t+3) % 4 == (t-1) % 4 was last
-    // read in iteration t-1, so after the barrier it can receive tile t+3.
     constexpr int NSTEP = 2 * KS;      // QK MFMAs per tile (two 32-key halves)
     constexpr int EPS = 32 / NSTEP;    // exponentials per QK MFMA
-    f32x16 S1[2];
-    auto tile = [&](const int t, const int u, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
-      // u == t % NSTAGE
-      // Tile t+1 was committed at the end of tile t-1; after this barrier it
-      // is visible, and stage (t+2) % 3 -- last read in tile t-1 -- is free.
-      if (t + 1 < ntiles && t > 0) __syncthreads();
-      const bool pre = t + 2 < ntiles;
-      Staged g;
-      if (pre) g = fetch(t + 2);  // in flight during this tile's compute
+    // Tile t (PAR = t & 1): softmax and PV of tile t from V^T stage PAR,
+    // overlapped with QK of tile t+1 from K stage PAR ^ 1.  After the barrier
+    // at its start, K tile t+1 and V^T tile t (loaded during tile t-1) are
+    // visible, and K stage PAR (tile t, read in tile t-1) and V^T stage PAR ^ 1
+    // (tile t-1) are free for K tile t+2 and V^T tile t+1, loaded now and
+    // awaited at the end of this tile.
+    auto tile = [&](auto par_c, const int t, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
+      constexpr int PAR = decltype(par_c)::value;
+      // also at t = 0: K stage 0 is read by the prologue's QK of tile 0
+      __syncthreads();
+      // in flight during this tile's compute
+      if (t + 2 < ntiles) load_k(t + 2, PAR);
+      if (t + 1 < ntiles) load_v(t + 1, PAR ^ 1);
       if (t >= ntiles_w) {
-        if (pre) commit(g, (u + 2) % NSTAGE);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
         return;
       }
-      if (t >= nfull_w) {  // causal diagonal or ragged end of the block
+      const bool diag = t >= nfull_w;  // causal diagonal or ragged end of the block
+      if (diag) {
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -253,88 +292,97 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
             const int j = t * kPBN + kh * 32 + (r >> 2) * 8 + 4 * hl + (r & 3);
             if (j >= jlim) Sc[kh][r] = -INFINITY;
           }
-        mx = rowmax(Sc);
       }
-      mx = half_max(mx);
-      const float mt = mx * c;
-      m_top = fmaxf(m_top, mt);
-      if (wave_any(mt > m_run + kTau)) {
-        const float mn = fmaxf(m_run, mt);
-        const float al = __builtin_amdgcn_exp2f(m_run - mn);
-        lsum *= al;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) O[dt][r] *= al;
-        m_run = mn;
+      if (EXACT) {
+        if (diag) mx = rowmax(Sc);
+        mx = half_max(mx);
+        const float mt = mx * c;
+        m_top = fmaxf(m_top, mt);
+        if (wave_any(mt > m_run + kTau)) rescale(mt);
       }
       const float nm = -m_run;
 
-      // Part 1: QK of the next tile (from a resident stage; discarded when
-      // the wave has no next tile), one MFMA at a time, each followed by a
-      // share of this tile's exponentials.
-      const char *stn = lds + (t + 1 < ntiles ? (u + 1) % NSTAGE : u) * STAGE;
+      // Part 1: QK of the next tile (discarded when the wave has none), one
+      // MFMA at a time, each followed by a share of this tile's exponentials.
+      const char *stn = lds + (PAR ^ 1) * KTILE;
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int r = 0; r < 16; ++r) Sn[kh][r] = 0.f;
-      // K fragments in a rolling window: those of k-step ks + 1 are read
+      // K fragments in a rolling window: those of k-step ks + KA are read
       // while k-step ks is multiplied
       s16x8 ka[KS][2];
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) ka[0][kh] = *(const s16x8 *)(stn + koff[0] + kh * 32 * KROW);
+      for (int d = 0; d < KA; ++d)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) ka[d][kh] = *(const s16x8 *)(stn + koff[d] + kh * 32 * KROW);
       float ls = 0.f;
       f32x16 pbuf;
       s16x8 P[4];
+      s16x8 va[4][DT];  // V^T fragments, read one PV group ahead
 #pragma unroll
       for (int step = 0; step < NSTEP; ++step) {
         const int ks = step >> 1, kh = step & 1;
-        if (kh == 0 && ks + 1 < KS) {
+        if (kh == 0 && ks + KA < KS) {
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2)
-            ka[ks + 1][h2] = *(const s16x8 *)(stn + koff[ks + 1] + h2 * 32 * KROW);
+            ka[ks + KA][h2] = *(const s16x8 *)(stn + koff[ks + KA] + h2 * 32 * KROW);
+        }
+        if (step == NSTEP - 2) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            va[0][dt] = *(const s16x8 *)(lds + voff[0] + PAR * VTILE + dt * 32 * VROW);
         }
         Sn[kh] = M::mma(ka[ks][kh], qf[ks], Sn[kh]);
 #pragma unroll
         for (int v = 0; v < EPS; ++v) {
           const int e = EPS * step + v;  // element of S: half e/16, register e%16
           const float pv = __builtin_amdgcn_exp2f(fmaf(Sc[e >> 4][e & 15], c, nm));
-          ls += pv;
+          ls += pv;  // l sums the unrounded probabilities
           pbuf[e & 7] = pv;
           if ((e & 7) == 7) P[e >> 3] = M::pack(pbuf, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (!EXACT) {
+        // a probability above 2^kTau means a new maximum: rescale and redo
+        if (wave_any(ls > kSumLimit)) {
+          rescale(half_max(rowmax(Sc)) * c);
+          ls = probs(Sc, P);
+        }
+      }
       lsum += ls;
 
-      // Part 2: PV of this tile, each group of MFMAs followed by a share of
-      // the next tile's row max.
-      const char *st = lds + u * STAGE;
+      // Part 2: PV of this tile (EXACT: each group of MFMAs followed by a
+      // share of the next tile's row max).
       float mxn = -INFINITY;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        s16x8 a[DT];
+        if (q4 + 1 < 4) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          a[dt] = *(const s16x8 *)(st + voff[q4] + dt * 32 * VROW);
+          for (int dt = 0; dt < DT; ++dt)
+            va[q4 + 1][dt] = *(const s16x8 *)(lds + voff[q4 + 1] + PAR * VTILE + dt * 32 * VROW);
+        }
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) O[dt] = M::mma(a[dt], P[q4], O[dt]);
+        for (int dt = 0; dt < DT; ++dt) O[dt] = M::mma(va[q4][dt], P[q4], O[dt]);
+        if (EXACT) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) mxn = fmaxf(mxn, Sn[q4 >> 1][8 * (q4 & 1) + r]);
+          for (int r = 0; r < 8; ++r) mxn = fmaxf(mxn, Sn[q4 >> 1][8 * (q4 & 1) + r]);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
-      mx = mxn;
-      if (pre) commit(g, (u + 2) % NSTAGE);
+      if (EXACT) mx = mxn;
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's tile loads have landed
     };
-    // two tiles per iteration so the S register sets swap roles instead of
-    // being copied
+    // two tiles per iteration so the stages are immediates and the S
+    // register sets swap roles instead of being copied
     for (int t = 0; t < ntiles; t += 2) {
-      tile(t, t % NSTAGE, S, S1);
+      tile(std::integral_constant<int, 0>(), t, S, S1);
       if (t + 1 >= ntiles) break;
-      tile(t + 1, (t + 1) % NSTAGE, S1, S);
+      tile(std::integral_constant<int, 1>(), t + 1, S1, S);
     }
   }
-  store_state<D>(p, w, i, valid, O, m_run, m_top, lsum);
+  store_state<D>(p, w, i, valid, O, m_run, EXACT ? m_top : m_run, lsum);
 }
 
 // V rows [b][h][j][c] (strides) -> packed [bh][c][n_pad]; one workgroup per
@@ -373,28 +421,34 @@ __global__ void __launch_bounds__(256) pack_v_kernel(const short *__restrict__ v
   }
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool EXACT>
 hipError_t launch_packed(const BatchParams &p, hipStream_t s) {
   const int ntq = (p.nq + kPBM - 1) / kPBM;
   const int64_t nwg = (int64_t)ntq * p.nz * p.B * p.Hq;
-  const size_t lds = (size_t)3 * (kPBN * D * 2 + D * kPBN * 2);
+  const size_t lds = (size_t)2 * (kPBN * D * 2 + D * kPBN * 2);
   static bool attr_set = false;  // more than 64 KB of LDS per workgroup must be opted into
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)attn_packed_kernel<D, BF16>,
+  if (!attr_set && lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void *)attn_packed_kernel<D, BF16, EXACT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((attn_packed_kernel<D, BF16>), dim3((unsigned)nwg), dim3(512), lds, s, p,
-                     ntq);
+  hipLaunchKernelGGL((attn_packed_kernel<D, BF16, EXACT>), dim3((unsigned)nwg), dim3(512), lds, s,
+                     p, ntq);
   return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t launch_packed_m(const BatchParams &p, hipStream_t s) {
+  return p.exact_m ? launch_packed<D, BF16, true>(p, s) : launch_packed<D, BF16, false>(p, s);
 }
 
 }  // namespace
 
 hipError_t launch_block_fwd_packed(const BatchParams &p, int dtype, hipStream_t s) {
-  if (dtype == RA_DT_BF16) return p.d == 64 ? launch_packed<64, true>(p, s) : launch_packed<128, true>(p, s);
-  return p.d == 64 ? launch_packed<64, false>(p, s) : launch_packed<128, false>(p, s);
+  if (dtype == RA_DT_BF16)
+    return p.d == 64 ? launch_packed_m<64, true>(p, s) : launch_packed_m<128, true>(p, s);
+  return p.d == 64 ? launch_packed_m<64, false>(p, s) : launch_packed_m<128, false>(p, s);
 }
 
 hipError_t launch_pack_v(const void *v, void *vp, int elt, int64_t BH, int64_t H, int64_t n,

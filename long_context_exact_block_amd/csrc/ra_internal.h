@@ -43,6 +43,10 @@ struct BatchParams {
   // V layout: 0 = rows [token][d] (strides vs_*); 1 = packed transposed
   // blocks from pack_v (vs_b, vs_h as given, vs_t = the packed row length).
   int32_t v_packed;
+  // 1: the stored m is the exact row maximum of the scores seen (a block
+  // partial).  0: it may be any reference maximum the stored l is relative
+  // to (a running state between hops; m + ln l is the same).
+  int32_t exact_m;
 };
 
 // Packed V: for each (b, h) a [d][n_pad] array, n_pad = n rounded up to 64,
@@ -50,6 +54,10 @@ struct BatchParams {
 // keys of every 16 swapped) and zero past n.  This is the key order in which
 // the PV product consumes probabilities, so every operand read is 16 bytes.
 constexpr int kPackAlign = 64;
+// The packed-V kernel addresses a (b, h) slice of packed V and a 64-row K tile
+// with 32-bit byte offsets: bound the packed row length and the K row stride.
+constexpr int64_t kMaxPackedKeys = int64_t(1) << 23;
+constexpr int64_t kMaxKRowStride = int64_t(1) << 22;
 inline int64_t packed_n(int64_t n) { return (n + kPackAlign - 1) / kPackAlign * kPackAlign; }
 hipError_t launch_pack_v(const void *v, void *vp, int elt, int64_t BH, int64_t H, int64_t n,
                          int64_t d, int64_t vs_b, int64_t vs_h, int64_t vs_t, hipStream_t s);

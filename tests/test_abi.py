@@ -82,6 +82,22 @@ def test_block_fwd_packed_v_rules(lib):
     assert lib.ra_block_fwd(ctypes.byref(a), None) == 1  # fails on q, not on v_stride
 
 
+def test_block_fwd_packed_v_size_limits(lib):
+    # packed V addresses a (b, h) slice with 32-bit offsets: 2^23 keys, 2^22-element K rows
+    a = _block(v_packed=1, n_k=(1 << 23) + 1)
+    assert lib.ra_block_fwd(ctypes.byref(a), None) == 6
+    a = _block(v_packed=1)
+    a.k_stride[2] = (1 << 22) + 128
+    assert lib.ra_block_fwd(ctypes.byref(a), None) == 6
+    assert "packed V" in rb.last_error()
+
+
+def test_ring_block_length_limit(lib):
+    a = _ring(n=(1 << 23) + 64)
+    st = lib.ra_ring_fwd(ctypes.byref(a), ctypes.c_void_p(4096), 1 << 40, None, None)
+    assert st == 6, (st, rb.last_error())
+
+
 def test_pack_v_sizes_and_rejects(lib):
     assert lib.ra_packed_v_bytes(rb.DT_BF16, 2, 3, 100, 128) == 2 * 3 * 128 * 128 * 2
     assert lib.ra_packed_v_bytes(rb.DT_FP16, 1, 1, 64, 64) == 64 * 64 * 2

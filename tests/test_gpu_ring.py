@@ -104,6 +104,32 @@ def test_fused_and_separate_merge_agree(case):
     assert np.abs(parity.to_f64(o1) - parity.to_f64(o2))[:, :, tok].max() <= 2e-2
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("layout", ["striped", "contiguous"])
+def test_running_max_rises_across_tiles_and_hops(dtype, layout):
+    """Key magnitudes ramp over the token index (up by 13x) and queries are
+    sharp, so the running maximum keeps rising in processing order: tile by
+    tile inside a striped block (keys ordered by token, magnitudes growing),
+    hop by hop on a contiguous ring (each hop brings an earlier block, ramp
+    reversed).  The fused fold must raise it -- rescale and redo a tile --
+    many times, including after tiles whose probabilities were all tiny."""
+    B, Hq, Hkv, S, d, R = 1, 2, 2, 8 * 512, 128, 8
+    case = ("rising_max_" + layout, B, Hq, Hkv, S, d, R, layout, dtype, True, 0, R)
+    q32 = inputs.normal((B, Hq, S, d), 501, scale=2.0)
+    k32 = inputs.normal((B, Hkv, S, d), 502)
+    u = np.arange(S, dtype=np.float32) / S
+    ramp = 1.0 + 12.0 * (u if layout == "striped" else 1.0 - u)
+    k32 *= ramp[None, None, :, None]
+    v32 = inputs.normal((B, Hkv, S, d), 503)
+    x = {}
+    for name, t in (("q", q32), ("k", k32), ("v", v32)):
+        x[name], x[name + "32"] = inputs.to_dtype(t, dtype)
+    _, o, lse = run_ring(case, x)
+    ro, rl = oracle.attention_full(x["q32"], x["k32"], x["v32"], 1 / math.sqrt(d), True)
+    parity.check_o(parity.to_f64(o), ro, case[0])
+    parity.check_lse(parity.to_f64(lse), rl, case[0])
+
+
 def test_layouts_agree_after_unpermuting():
     """Contiguous and striped rings give the same outputs in the original order."""
     case_c = ("c", 1, 2, 2, 2048, 128, 8, "contiguous", "bf16", True, 0, 8)
