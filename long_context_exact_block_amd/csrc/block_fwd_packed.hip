@@ -13,12 +13,15 @@
 //    (the LDS transpose read delivers ~1/3 of the bytes per clock).
 //  * K tiles are loaded two tiles ahead and V^T tiles one tile ahead, by
 //    buffer loads that write LDS directly (no staging registers); two K and
-//    two V^T stages, one barrier per tile, the loop unrolled by two so every
-//    LDS offset is an immediate.  16-byte chunks are XOR-swizzled by row for
+//    three V^T stages, one barrier per tile, the loop unrolled by two so every
+//    K offset is an immediate.  16-byte chunks are XOR-swizzled by row for
 //    gfx950's 64 LDS banks so every read pattern is conflict-free.
 //  * 8 waves x 32 queries per workgroup (256 rows), two waves per SIMD; QK of
 //    tile t+1 is interleaved with the exponentials of tile t; K fragments are
-//    read two k-steps ahead and V^T fragments one PV group ahead.
+//    read two k-steps ahead and V^T fragments one PV group ahead.  In the
+//    fused ring the upper four waves run PV half a tile late (before instead
+//    of after the QK/exponential phase), so the waves sharing a SIMD are in
+//    opposite phases.
 //  * Between hops only m + ln l matters, so the fused ring skips the per-tile
 //    row max: exponentials use the running maximum and a tile whose
 //    probabilities grow too large is redone after raising it.
@@ -87,7 +90,7 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
   constexpr int KTILE = kPBN * KROW;     // bytes of a K tile
   constexpr int VROW = kPBN * 2;         // bytes per V^T row (64 keys)
   constexpr int VTILE = D * VROW;        // bytes of a V^T tile
-  constexpr int VBASE = 2 * KTILE;       // LDS: K stages 0, 1, then V^T stages 0, 1
+  constexpr int VBASE = 2 * KTILE;       // LDS: K stages 0, 1, then V^T stages 0, 1, 2
   constexpr int KPW = KTILE / 1024 / kPW;  // 1 KB wave-loads per wave per K tile
   constexpr int VPW = VTILE / 1024 / kPW;
   constexpr int KRPI = 1024 / KROW;      // K rows per wave-load
@@ -189,11 +192,11 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
       for (int u = 0; u < KPW; ++u)
         dma16(krsrc, (lds_void *)(lds + kstage * KTILE + kPW * 1024 * u + wave * 1024), kvo[u], 0);
     };
-    auto load_v = [&](int tv, int vstage) {
+    auto load_v = [&](int tv, int vso) {  // vso: byte offset of the V^T stage
 #pragma unroll
       for (int u = 0; u < VPW; ++u)
-        dma16(vrsrc, (lds_void *)(lds + VBASE + vstage * VTILE + kPW * 1024 * u + wave * 1024),
-              vvo[u], tv * kPBN * 2);
+        dma16(vrsrc, (lds_void *)(lds + VBASE + vso + kPW * 1024 * u + wave * 1024), vvo[u],
+              tv * kPBN * 2);
     };
 
     // Per-lane LDS read offsets.  Row kh*32 + c32 (K) and 32dt + c32 (V^T)
@@ -266,121 +269,144 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
 
     constexpr int NSTEP = 2 * KS;      // QK MFMAs per tile (two 32-key halves)
     constexpr int EPS = 32 / NSTEP;    // exponentials per QK MFMA
-    // Tile t (PAR = t & 1): softmax and PV of tile t from V^T stage PAR,
-    // overlapped with QK of tile t+1 from K stage PAR ^ 1.  After the barrier
-    // at its start, K tile t+1 and V^T tile t (loaded during tile t-1) are
-    // visible, and K stage PAR (tile t, read in tile t-1) and V^T stage PAR ^ 1
-    // (tile t-1) are free for K tile t+2 and V^T tile t+1, loaded now and
-    // awaited at the end of this tile.
-    auto tile = [&](auto par_c, const int t, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
-      constexpr int PAR = decltype(par_c)::value;
-      // also at t = 0: K stage 0 is read by the prologue's QK of tile 0
-      __syncthreads();
-      // in flight during this tile's compute
-      if (t + 2 < ntiles) load_k(t + 2, PAR);
-      if (t + 1 < ntiles) load_v(t + 1, PAR ^ 1);
-      if (t >= ntiles_w) {
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
-        return;
-      }
-      const bool diag = t >= nfull_w;  // causal diagonal or ragged end of the block
-      if (diag) {
+    // The two waves sharing a SIMD run the same work half a tile apart: a
+    // leading wave does [QK(t+1) with the exponentials of t, then PV(t)], a
+    // lagging wave [PV(t-1), then QK(t+1) with the exponentials of t], so
+    // while one issues MFMAs only, the other has VALU work to overlap.
+    // (the exact-max variant keeps all waves leading: its extra row-max state
+    // does not fit the registers of both orders)
+    const bool lag = !EXACT && wave >= kPW / 2;
+    s16x8 P[4];        // probabilities of the tile whose PV is pending
+    s16x8 va0[DT];     // its first group of V^T fragments, read ahead
+    int vst = 0;       // V^T stage of tile t (t % 3)
+    // O^T += V^T P^T for the V^T tile in stage offset vso (va0 read already);
+    // EXACT: returns the row max of Sm, computed in the MFMA shadow
+    auto pv = [&](int vso, const f32x16 (&Sm)[2]) {
+      s16x8 va[4][DT];
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = t * kPBN + kh * 32 + (r >> 2) * 8 + 4 * hl + (r & 3);
-            if (j >= jlim) Sc[kh][r] = -INFINITY;
-          }
-      }
-      if (EXACT) {
-        if (diag) mx = rowmax(Sc);
-        mx = half_max(mx);
-        const float mt = mx * c;
-        m_top = fmaxf(m_top, mt);
-        if (wave_any(mt > m_run + kTau)) rescale(mt);
-      }
-      const float nm = -m_run;
-
-      // Part 1: QK of the next tile (discarded when the wave has none), one
-      // MFMA at a time, each followed by a share of this tile's exponentials.
-      const char *stn = lds + (PAR ^ 1) * KTILE;
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Sn[kh][r] = 0.f;
-      // K fragments in a rolling window: those of k-step ks + KA are read
-      // while k-step ks is multiplied
-      s16x8 ka[KS][2];
-#pragma unroll
-      for (int d = 0; d < KA; ++d)
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) ka[d][kh] = *(const s16x8 *)(stn + koff[d] + kh * 32 * KROW);
-      float ls = 0.f;
-      f32x16 pbuf;
-      s16x8 P[4];
-      s16x8 va[4][DT];  // V^T fragments, read one PV group ahead
-#pragma unroll
-      for (int step = 0; step < NSTEP; ++step) {
-        const int ks = step >> 1, kh = step & 1;
-        if (kh == 0 && ks + KA < KS) {
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2)
-            ka[ks + KA][h2] = *(const s16x8 *)(stn + koff[ks + KA] + h2 * 32 * KROW);
-        }
-        if (step == NSTEP - 2) {
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            va[0][dt] = *(const s16x8 *)(lds + voff[0] + PAR * VTILE + dt * 32 * VROW);
-        }
-        Sn[kh] = M::mma(ka[ks][kh], qf[ks], Sn[kh]);
-#pragma unroll
-        for (int v = 0; v < EPS; ++v) {
-          const int e = EPS * step + v;  // element of S: half e/16, register e%16
-          const float pv = __builtin_amdgcn_exp2f(fmaf(Sc[e >> 4][e & 15], c, nm));
-          ls += pv;  // l sums the unrounded probabilities
-          pbuf[e & 7] = pv;
-          if ((e & 7) == 7) P[e >> 3] = M::pack(pbuf, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (!EXACT) {
-        // a probability above 2^kTau means a new maximum: rescale and redo
-        if (wave_any(ls > kSumLimit)) {
-          rescale(half_max(rowmax(Sc)) * c);
-          ls = probs(Sc, P);
-        }
-      }
-      lsum += ls;
-
-      // Part 2: PV of this tile (EXACT: each group of MFMAs followed by a
-      // share of the next tile's row max).
+      for (int dt = 0; dt < DT; ++dt) va[0][dt] = va0[dt];
       float mxn = -INFINITY;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         if (q4 + 1 < 4) {
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
-            va[q4 + 1][dt] = *(const s16x8 *)(lds + voff[q4 + 1] + PAR * VTILE + dt * 32 * VROW);
+            va[q4 + 1][dt] = *(const s16x8 *)(lds + voff[q4 + 1] + vso + dt * 32 * VROW);
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) O[dt] = M::mma(va[q4][dt], P[q4], O[dt]);
         if (EXACT) {
 #pragma unroll
-          for (int r = 0; r < 8; ++r) mxn = fmaxf(mxn, Sn[q4 >> 1][8 * (q4 & 1) + r]);
+          for (int r = 0; r < 8; ++r) mxn = fmaxf(mxn, Sm[q4 >> 1][8 * (q4 & 1) + r]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (EXACT) mx = mxn;
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's tile loads have landed
+      return mxn;
     };
-    // two tiles per iteration so the stages are immediates and the S
+    // Tile t (PAR = t & 1).  After the barrier at its start, K tile t+1 (K
+    // stage PAR ^ 1) and V^T tile t (stage t % 3), loaded during tile t-1, are
+    // visible; K stage PAR (tile t, read in tile t-1) and V^T stage (t+1) % 3
+    // (tile t-2, whose PV the lagging waves finished in tile t-1) are free for
+    // K tile t+2 and V^T tile t+1, loaded now and awaited at the end.
+    auto tile = [&](auto par_c, const int t, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
+      constexpr int PAR = decltype(par_c)::value;
+      // also at t = 0: K stage 0 is read by the prologue's QK of tile 0
+      __syncthreads();
+      const int vcur = vst * VTILE;
+      const int vnext = (vst == 2 ? 0 : vst + 1) * VTILE;
+      const int vprev = (vst == 0 ? 2 : vst - 1) * VTILE;
+      if (t + 2 < ntiles) load_k(t + 2, PAR);
+      if (t + 1 < ntiles) load_v(t + 1, vnext);
+      if (lag && t >= 1 && t - 1 < ntiles_w) {
+        const float m2 = pv(vprev, Sc);
+        if (EXACT) mx = m2;
+      }
+      if (t < ntiles_w) {
+        const bool diag = t >= nfull_w;  // causal diagonal or ragged end of the block
+        if (diag) {
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int j = t * kPBN + kh * 32 + (r >> 2) * 8 + 4 * hl + (r & 3);
+              if (j >= jlim) Sc[kh][r] = -INFINITY;
+            }
+        }
+        if (EXACT) {
+          if (diag) mx = rowmax(Sc);
+          mx = half_max(mx);
+          const float mt = mx * c;
+          m_top = fmaxf(m_top, mt);
+          if (wave_any(mt > m_run + kTau)) rescale(mt);
+        }
+        const float nm = -m_run;
+
+        // QK of the next tile (discarded when the wave has none), one MFMA at
+        // a time, each followed by a share of this tile's exponentials.
+        const char *stn = lds + (PAR ^ 1) * KTILE;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) Sn[kh][r] = 0.f;
+        // K fragments in a rolling window: those of k-step ks + KA are read
+        // while k-step ks is multiplied
+        s16x8 ka[KS][2];
+#pragma unroll
+        for (int d = 0; d < KA; ++d)
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+            ka[d][kh] = *(const s16x8 *)(stn + koff[d] + kh * 32 * KROW);
+        float ls = 0.f;
+        f32x16 pbuf;
+#pragma unroll
+        for (int step = 0; step < NSTEP; ++step) {
+          const int ks = step >> 1, kh = step & 1;
+          if (kh == 0 && ks + KA < KS) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+              ka[ks + KA][h2] = *(const s16x8 *)(stn + koff[ks + KA] + h2 * 32 * KROW);
+          }
+          if (step == NSTEP - 2) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+              va0[dt] = *(const s16x8 *)(lds + voff[0] + vcur + dt * 32 * VROW);
+          }
+          Sn[kh] = M::mma(ka[ks][kh], qf[ks], Sn[kh]);
+#pragma unroll
+          for (int v = 0; v < EPS; ++v) {
+            const int e = EPS * step + v;  // element of S: half e/16, register e%16
+            const float pv = __builtin_amdgcn_exp2f(fmaf(Sc[e >> 4][e & 15], c, nm));
+            ls += pv;  // l sums the unrounded probabilities
+            pbuf[e & 7] = pv;
+            if ((e & 7) == 7) P[e >> 3] = M::pack(pbuf, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (!EXACT) {
+          // a probability above 2^kTau means a new maximum: rescale and redo
+          if (wave_any(ls > kSumLimit)) {
+            rescale(half_max(rowmax(Sc)) * c);
+            ls = probs(Sc, P);
+          }
+        }
+        lsum += ls;
+        if (!lag) {
+          const float m2 = pv(vcur, Sn);
+          if (EXACT) mx = m2;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's tile loads have landed
+      vst = vnext / VTILE;
+    };
+    // two tiles per iteration so the K stages are immediates and the S
     // register sets swap roles instead of being copied
     for (int t = 0; t < ntiles; t += 2) {
       tile(std::integral_constant<int, 0>(), t, S, S1);
       if (t + 1 >= ntiles) break;
       tile(std::integral_constant<int, 1>(), t + 1, S1, S);
     }
+    // the lagging waves' PV of the last tile (no stage is reloaded any more)
+    if (lag && ntiles_w == ntiles) pv((vst == 0 ? 2 : vst - 1) * VTILE, S);
   }
   store_state<D>(p, w, i, valid, O, m_run, EXACT ? m_top : m_run, lsum);
 }
@@ -425,7 +451,7 @@ template <int D, bool BF16, bool EXACT>
 hipError_t launch_packed(const BatchParams &p, hipStream_t s) {
   const int ntq = (p.nq + kPBM - 1) / kPBM;
   const int64_t nwg = (int64_t)ntq * p.nz * p.B * p.Hq;
-  const size_t lds = (size_t)2 * (kPBN * D * 2 + D * kPBN * 2);
+  const size_t lds = (size_t)2 * kPBN * D * 2 + (size_t)3 * D * kPBN * 2;
   static bool attr_set = false;  // more than 64 KB of LDS per workgroup must be opted into
   if (!attr_set && lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void *)attn_packed_kernel<D, BF16, EXACT>,
