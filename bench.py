@@ -35,6 +35,24 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
+def traffic_from_profile(kernel_sources, summary):
+    """HBM bytes per block-kernel launch from the committed counter summary, or
+    None when the kernel sources changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, summary)) as f:
+            prof = json.load(f)
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for rel in kernel_sources:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != prof.get("kernel_sources_sha256"):
+        return None
+    return float(prof["hbm_bytes_per_launch"])
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -78,19 +96,34 @@ def cpu_baseline(w, data, layout_code, seconds_target, seed=4242):
         orc.attention_rows(qrows, b, hh, t, k32, v32, w.Hq, w.scale, w.causal)
         dt = time.perf_counter() - t0
         return dt, float(keys.sum())
-    dt0, k0 = run(max(orc.num_threads(), 8))
+    cores = orc.num_threads()
+    # single-thread rate on a small sample (per-core figure), then all cores
+    orc.set_threads(1)
+    dt1, k1 = run(4)
+    orc.set_threads(cores)
+    dt0, k0 = run(max(cores, 8))
     per_key = dt0 / max(k0, 1.0)
     avg_keys = (w.S / 2) if w.causal else w.S
-    rows = int(max(orc.num_threads(), min(4096, seconds_target / (per_key * avg_keys))))
+    rows = int(max(cores, min(4096, seconds_target / (per_key * avg_keys))))
     dt, keys = run(rows)
     flops = 4.0 * w.d * keys
     total_pairs = w.metric_flops() / (4.0 * w.d)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {
-        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
         "kind": "oracle",
         "sample": "%d seeded query rows of the same workload (all heads, tokens of the computed "
                   "rank), each against its full allowed key set: %.3g pairs in %.2f s; whole "
                   "workload extrapolates to %.0f s" % (rows, keys, dt, total_pairs / (keys / dt)),
+        "pairs_per_s": keys / dt,
+        "pairs_per_s_one_thread": k1 / dt1,
+        "extrapolated_full_s": total_pairs / (keys / dt),
+        "cpu_model": model,
     }
 
 
@@ -117,6 +150,47 @@ def merge_bench(torch, rb, rows=4 * 16 * 512 * 64, d=64, iters=20):
     return {"rows": rows, "d": d, "us_per_launch": ms * 1e3, "bytes_per_launch": nbytes,
             "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 /
             PEAK_HBM_GBS}
+
+
+def overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse, t_copy_ms,
+                  steps=3):
+    """How much of the K/V hand-off the compute hides: the same step with the
+    blocks read in place (SWAP, no transfer), and the hop copies alone (one
+    device-to-device copy of the hand-off bytes per hop, on one stream)."""
+    ra = RingAttention(w.B, w.Hq, w.Hkv, w.S, w.d, w.R, layout, tdt, w.causal, w.scale,
+                       rank0=w.rank0, n_ranks=w.ranks, handoff=rb.HANDOFF_SWAP)
+    ra.run(q, k, v, o, lse)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    e[0].record()
+    for s in range(steps):
+        ra.run(q, k, v, o, lse)
+        e[s + 1].record()
+    torch.cuda.synchronize()
+    t_swap = float(np.median([e[s].elapsed_time(e[s + 1]) for s in range(steps)]))
+    del ra
+    elt = 4 if w.dtype == "fp32" else 2
+    k_bytes = w.ranks * w.B * w.Hkv * w.n * w.d * elt
+    v_bytes = (w.ranks * w.B * w.Hkv * w.d * ((w.n + 63) // 64 * 64) * elt
+               if w.dtype != "fp32" else k_bytes)
+    per_hop = k_bytes + v_bytes
+    src = torch.empty(per_hop, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    c0.record()
+    for _ in range(w.R - 1):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    t_copies = c0.elapsed_time(c1)
+    del src, dst
+    moved = 2.0 * per_hop * (w.R - 1)  # read + write
+    return {"step_ms_copy": round(t_copy_ms, 3), "step_ms_swap": round(t_swap, 3),
+            "copies_alone_ms": round(t_copies, 3),
+            "bytes_per_hop": per_hop, "copy_GB/s": round(moved / (t_copies * 1e-3) / 1e9, 1),
+            "overlap": round(1.0 - (t_copy_ms - t_swap) / t_copies, 3) if t_copies > 0 else None}
 
 
 def block_only(torch, rb, w, layout, steps, warmup):
@@ -174,6 +248,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge-bench", action="store_true")
+    ap.add_argument("--no-overlap-bench", action="store_true",
+                    help="skip the hand-off overlap measurement (SWAP steps + copies alone)")
     ap.add_argument("--block-only", action="store_true",
                     help="time only the block kernel on one hop of the workload (query shard x "
                          "one K/V block, packed V), on seeded device-side random inputs")
@@ -235,16 +311,20 @@ def main():
     torch.cuda.synchronize()
     handles = [(ctypes.c_void_p * (2 * R))(*[evs[s * 2 * R + i].cuda_event for i in range(2 * R)])
                for s in range(K)]
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     log("timing %d steps" % K)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    step_ev[0].record()
     for s in range(K):
         ra.args.hop_events = ctypes.cast(handles[s], ctypes.POINTER(ctypes.c_void_p))
         ra.run(q, k, v, o, lse)
+        step_ev[s + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ra.args.hop_events = None
     ms_per_step = wall / K * 1e3
+    step_ms = np.array([step_ev[s].elapsed_time(step_ev[s + 1]) for s in range(K)])
     hop_ms = np.array([[evs[s * 2 * R + 2 * h].elapsed_time(evs[s * 2 * R + 2 * h + 1])
                         for h in range(R)] for s in range(K)])
     pairs = hop_pairs(w, lcode)
@@ -254,6 +334,10 @@ def main():
     exact_flops = 4.0 * w.d * w.B * w.Hq * sum(pairs)
     log("step %.2f ms, %.1f TFLOP/s; block kernel %.1f TFLOP/s" % (ms_per_step, value, achieved))
 
+    handoff = None
+    if args.handoff == "copy" and w.R > 1 and not args.no_overlap_bench:
+        handoff = overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse,
+                                float(np.median(step_ms)))
     merge = None if args.no_merge_bench else merge_bench(torch, rb)
     imbalance = {}
     for name, code in (("contiguous", 0), ("striped", 1)):
@@ -272,6 +356,14 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (~%.0f s)" % args.cpu_seconds)
         cpu = cpu_baseline(w, data, lcode, args.cpu_seconds)
+
+    traffic = None
+    if w.name == "rank3_of_8_share_1M_striped_bf16" and args.merge == "fused":
+        traffic = traffic_from_profile(
+            ["long_context_exact_block_amd/csrc/block_fwd_packed.hip",
+             "long_context_exact_block_amd/csrc/attn_common.h",
+             "long_context_exact_block_amd/csrc/ra_internal.h"],
+            "profiles/attn_packed_1M_share_traffic.json")
 
     line = {
         "metric": "causal ring-attention fwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak",
@@ -294,10 +386,13 @@ def main():
         "exact_pair_tflops": round(exact_flops / (ms_per_step * 1e-3) / 1e12, 3),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "attn_packed_kernel<128,bf16>" if w.dtype != "fp32" else "attn_block32_kernel",
+                     "traffic": traffic, "kernel": "attn_packed_kernel<128,bf16>" if w.dtype != "fp32" else "attn_block32_kernel",
                      "launches": R * K, "avg_launch_ms": round(float(hop_ms.mean()), 4),
                      "algorithmic_flops_per_launch": sum(flops_per_launch) / R},
+        "step_ms_median": round(float(np.median(step_ms)), 3),
+        "step_ms_min": round(float(step_ms.min()), 3),
         "hop_ms": [round(float(x), 3) for x in hop_ms.mean(axis=0)],
+        "handoff": handoff,
         "merge": merge,
         "causal_imbalance_max_over_mean": imbalance,
         "cpu_baseline": cpu,
