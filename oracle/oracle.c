@@ -23,6 +23,12 @@
  *        insight: running maximum, running normaliser, rescaling of earlier
  *        partial sums when a larger value appears.
  *
+ *
+ * Zig-zag: [ZZ] and [DE] "Zukunft" name a zig-zag variant of the assignment
+ * but print no definition beyond the interleaved one.  Read as the common
+ * 2R-chunk form: cut the sequence into 2R equal chunks; rank r keeps chunks
+ * r and 2R-1-r (one early, one late), so every rank gets the same causal work.
+ *
  * Readings where the pages are silent (each also listed in the design notes):
  *  - causal includes the diagonal (key j is allowed for query i iff j <= i);
  *  - a row with no allowed key in a block is the partial (O=0, m=-inf, l=0);
@@ -44,6 +50,7 @@
 
 #define ORA_LAYOUT_CONTIGUOUS 0
 #define ORA_LAYOUT_STRIPED 1
+#define ORA_LAYOUT_ZIGZAG 2
 
 int ora_num_threads(void) {
 #ifdef _OPENMP
@@ -67,18 +74,32 @@ void ora_set_threads(int n) {
  *      token = r*n + j
  *  striped/interleaved ([ZZ] worked example: rank r holds r, r+R, r+2R...):
  *      token = j*R + r
- * Returns 0 on success, -1 if the arguments do not describe an even split.
+ *  zig-zag (2R chunks of c = S/(2R) tokens; rank r holds chunk r, then
+ *  chunk 2R-1-r):
+ *      token = r*c + j              for j < c
+ *      token = (2R-1-r)*c + (j - c) for j >= c
+ * Returns 0 on success, -1 if the arguments do not describe an even split
+ * (zig-zag needs S divisible by 2R).
  */
 int ora_layout_maps(int layout, int64_t S, int32_t R, int32_t *fwd,
                     int32_t *inv) {
   if (R <= 0 || S < 0 || S % R != 0) return -1;
-  if (layout != ORA_LAYOUT_CONTIGUOUS && layout != ORA_LAYOUT_STRIPED)
+  if (layout != ORA_LAYOUT_CONTIGUOUS && layout != ORA_LAYOUT_STRIPED &&
+      layout != ORA_LAYOUT_ZIGZAG)
     return -1;
+  if (layout == ORA_LAYOUT_ZIGZAG && S % (2 * (int64_t)R) != 0) return -1;
   int64_t n = S / R;
+  int64_t c = n / 2;
   for (int64_t r = 0; r < R; ++r) {
     for (int64_t j = 0; j < n; ++j) {
       int64_t p = r * n + j;
-      int64_t t = (layout == ORA_LAYOUT_CONTIGUOUS) ? p : j * R + r;
+      int64_t t;
+      if (layout == ORA_LAYOUT_CONTIGUOUS)
+        t = p;
+      else if (layout == ORA_LAYOUT_STRIPED)
+        t = j * R + r;
+      else
+        t = (j < c) ? r * c + j : (2 * (int64_t)R - 1 - r) * c + (j - c);
       fwd[p] = (int32_t)t;
       if (inv) inv[t] = (int32_t)p;
     }
@@ -148,17 +169,17 @@ void ora_attention_rows(const float *q_rows, const int64_t *row_b,
  * arrives the rank computes a partial attention).
  *
  *   q [B][Hq][nq][d], k, v [B][Hkv][nk][d] (contiguous)
- *   global id of local query i: qg0 + i*qstep; of local key j: kg0 + j*kstep
- *   causal: key j allowed for query i iff gid(j) <= gid(i)
+ *   global token of local query i: qid[i]; of local key j: kid[j]
+ *   causal: key j allowed for query i iff kid[j] <= qid[i]
  *   out: o [B][Hq][nq][d] normalised (sum p v / l), m [B][Hq][nq] (natural
  *   units, scale included), l = sum exp(s - m).  A row with no allowed key
  *   gets (O = 0, m = -inf, l = 0).
  */
-void ora_block_partial(const float *q, const float *k, const float *v,
-                       int64_t B, int64_t Hq, int64_t Hkv, int64_t nq,
-                       int64_t nk, int64_t d, double scale, int causal,
-                       int64_t qg0, int64_t qstep, int64_t kg0, int64_t kstep,
-                       double *o, double *m_out, double *l_out) {
+static void block_partial_ids(const float *q, const float *k, const float *v,
+                              int64_t B, int64_t Hq, int64_t Hkv, int64_t nq,
+                              int64_t nk, int64_t d, double scale, int causal,
+                              const int64_t *qid, const int64_t *kid,
+                              double *o, double *m_out, double *l_out) {
   int64_t group = Hq / Hkv;
   int64_t rows = B * Hq * nq;
 #pragma omp parallel for schedule(dynamic, 16)
@@ -170,11 +191,11 @@ void ora_block_partial(const float *q, const float *k, const float *v,
     const float *qi = q + row * d;
     const float *kb = k + (b * Hkv + g) * nk * d;
     const float *vb = v + (b * Hkv + g) * nk * d;
-    int64_t gq = qg0 + i * qstep;
+    int64_t gq = qid[i];
     double m = -INFINITY;
     int any = 0;
     for (int64_t j = 0; j < nk; ++j) {
-      if (causal && kg0 + j * kstep > gq) continue;
+      if (causal && kid[j] > gq) continue;
       double s = 0.0;
       for (int64_t c = 0; c < d; ++c) s += (double)qi[c] * (double)kb[j * d + c];
       s *= scale;
@@ -190,7 +211,7 @@ void ora_block_partial(const float *q, const float *k, const float *v,
     }
     double l = 0.0;
     for (int64_t j = 0; j < nk; ++j) {
-      if (causal && kg0 + j * kstep > gq) continue;
+      if (causal && kid[j] > gq) continue;
       double s = 0.0;
       for (int64_t c = 0; c < d; ++c) s += (double)qi[c] * (double)kb[j * d + c];
       s *= scale;
@@ -202,6 +223,30 @@ void ora_block_partial(const float *q, const float *k, const float *v,
     m_out[row] = m;
     l_out[row] = l;
   }
+}
+
+/*
+ * The same with affine global ids, the form of one block of the contiguous or
+ * interleaved layouts: qid[i] = qg0 + i*qstep, kid[j] = kg0 + j*kstep.
+ */
+void ora_block_partial(const float *q, const float *k, const float *v,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t nq,
+                       int64_t nk, int64_t d, double scale, int causal,
+                       int64_t qg0, int64_t qstep, int64_t kg0, int64_t kstep,
+                       double *o, double *m_out, double *l_out) {
+  int64_t *qid = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nq > 0 ? nq : 1));
+  int64_t *kid = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nk > 0 ? nk : 1));
+  if (!qid || !kid) {
+    free(qid);
+    free(kid);
+    return;
+  }
+  for (int64_t i = 0; i < nq; ++i) qid[i] = qg0 + i * qstep;
+  for (int64_t j = 0; j < nk; ++j) kid[j] = kg0 + j * kstep;
+  block_partial_ids(q, k, v, B, Hq, Hkv, nq, nk, d, scale, causal, qid, kid, o, m_out,
+                    l_out);
+  free(qid);
+  free(kid);
 }
 
 /*
@@ -268,9 +313,11 @@ int ora_ring_emulate(const float *q, const float *k, const float *v,
   double *oblk = (double *)malloc(sizeof(double) * (size_t)(rows * d));
   double *mblk = (double *)malloc(sizeof(double) * (size_t)rows);
   double *lblk = (double *)malloc(sizeof(double) * (size_t)rows);
+  int64_t *qid = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
+  int64_t *kid = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
   int rc = 0;
   if (!fwd || !qs || !ks || !vs || !oacc || !macc || !lacc || !oblk || !mblk ||
-      !lblk || ora_layout_maps(layout, S, R, fwd, NULL) != 0) {
+      !lblk || !qid || !kid || ora_layout_maps(layout, S, R, fwd, NULL) != 0) {
     rc = -1;
     goto done;
   }
@@ -301,16 +348,15 @@ int ora_ring_emulate(const float *q, const float *k, const float *v,
       lacc[i] = 0.0;
     }
     for (int64_t i = 0; i < rows * d; ++i) oacc[i] = 0.0;
-    /* global ids are affine in the local index for both layouts */
-    int64_t step = (layout == ORA_LAYOUT_CONTIGUOUS) ? 1 : R;
-    int64_t qg0 = (layout == ORA_LAYOUT_CONTIGUOUS) ? r * n : r;
+    /* global ids of this rank's queries: the tokens its slots hold */
+    for (int64_t j = 0; j < n; ++j) qid[j] = fwd[r * n + j];
     for (int64_t hop = 0; hop < R; ++hop) {
       int64_t s = ((r - hop) % R + R) % R;
-      int64_t kg0 = (layout == ORA_LAYOUT_CONTIGUOUS) ? s * n : s;
+      for (int64_t j = 0; j < n; ++j) kid[j] = fwd[s * n + j];
       const float *kb = ks + s * B * Hkv * n * d;
       const float *vb = vs + s * B * Hkv * n * d;
-      ora_block_partial(qs, kb, vb, B, Hq, Hkv, n, n, d, scale, causal, qg0,
-                        step, kg0, step, oblk, mblk, lblk);
+      block_partial_ids(qs, kb, vb, B, Hq, Hkv, n, n, d, scale, causal, qid,
+                        kid, oblk, mblk, lblk);
       ora_merge(oacc, macc, lacc, oblk, mblk, lblk, rows, d);
     }
     for (int64_t b = 0; b < B; ++b)
@@ -334,6 +380,8 @@ done:
   free(oblk);
   free(mblk);
   free(lblk);
+  free(qid);
+  free(kid);
   return rc;
 }
 

@@ -20,7 +20,7 @@ import os
 import numpy as np
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-CONTIGUOUS, STRIPED = 0, 1
+CONTIGUOUS, STRIPED, ZIGZAG = 0, 1, 2
 
 
 # --------------------------------------------------------------------------- helpers
@@ -76,11 +76,20 @@ def read_interleave_golden():
 
 
 def closed_form_counts(layout, S, R):
-    """Per-rank causal pairs: contiguous r*n^2 + n(n+1)/2; striped R n^2/2 + n(2r+2-R)/2."""
+    """Per-rank causal pairs: contiguous r*n^2 + n(n+1)/2; striped R n^2/2 + n(2r+2-R)/2;
+    zig-zag (chunks r and 2R-1-r of c = S/2R tokens) c^2 (2R-1) + c(c+1) for every rank."""
     n = S // R
     if layout == CONTIGUOUS:
         return np.array([r * n * n + n * (n + 1) // 2 for r in range(R)], np.int64)
+    if layout == ZIGZAG:
+        c = n // 2
+        return np.full(R, c * c * (2 * R - 1) + c * (c + 1), np.int64)
     return np.array([(R * n * n + n * (2 * r + 2 - R)) // 2 for r in range(R)], np.int64)
+
+
+def layouts_for(S, R):
+    """Layouts that split S tokens over R ranks (zig-zag needs 2R equal chunks)."""
+    return (CONTIGUOUS, STRIPED, ZIGZAG) if S % (2 * R) == 0 else (CONTIGUOUS, STRIPED)
 
 
 # --------------------------------------------------------------------------- PIN-1
@@ -113,6 +122,31 @@ def check_layout_bijection(orc):
                 assert (fwd // R == p % n).all()          # local position
                 # within a rank tokens increase, so masks stay monotone
                 assert (np.diff(fwd.reshape(R, n), axis=1) > 0).all()
+
+
+def check_zigzag_layout(orc):
+    """Zig-zag reading (2R chunks, rank r holds chunk r then chunk 2R-1-r): the
+    four-rank, 16-token assignment written out by hand; bijection; each rank's
+    tokens increase (causal masks stay prefixes); one early and one late chunk."""
+    fwd, inv = orc.layout_maps(ZIGZAG, 16, 4)
+    assert fwd.reshape(4, 4).tolist() == [[0, 1, 14, 15], [2, 3, 12, 13], [4, 5, 10, 11],
+                                          [6, 7, 8, 9]]
+    for S, R in ((16, 4), (48, 3), (64, 8), (2, 1), (4096, 8), (128, 64)):
+        fwd, inv = orc.layout_maps(ZIGZAG, S, R)
+        n, c = S // R, S // (2 * R)
+        assert sorted(fwd.tolist()) == list(range(S))
+        assert (inv[fwd] == np.arange(S)).all()
+        f = fwd.reshape(R, n).astype(np.int64)
+        assert (np.diff(f, axis=1) > 0).all()
+        for r in range(R):
+            assert (f[r, :c] == r * c + np.arange(c)).all()
+            assert (f[r, c:] == (2 * R - 1 - r) * c + np.arange(c)).all()
+    for S, R in ((12, 4), (10, 4)):  # not 2R equal chunks
+        try:
+            orc.layout_maps(ZIGZAG, S, R)
+        except ValueError:
+            continue
+        raise AssertionError("zig-zag accepted S=%d R=%d" % (S, R))
 
 
 # --------------------------------------------------------------------------- PIN-2
@@ -288,7 +322,7 @@ def check_ring_equals_full(orc):
     for causal in (True, False):
         o, lse = orc.attention_full(q, k, v, scale, causal)
         for R in (1, 2, 3, 4, 8, 16, 48):
-            for layout in (CONTIGUOUS, STRIPED):
+            for layout in layouts_for(S, R):
                 ro, rl = orc.ring_emulate(q, k, v, R, layout, scale, causal)
                 _close(ro, o, 1e-12, 1e-13, "ring O R=%d L=%d" % (R, layout))
                 _close(rl, lse, 1e-12, 1e-13, "ring LSE R=%d L=%d" % (R, layout))
@@ -303,9 +337,10 @@ def check_layout_independence(orc):
     v = rng.standard_normal((B, H, S, d)).astype(np.float32)
     for R in (4, 8):
         a = orc.ring_emulate(q, k, v, R, CONTIGUOUS, 0.5, True)
-        b = orc.ring_emulate(q, k, v, R, STRIPED, 0.5, True)
-        _close(a[0], b[0], 1e-12, 1e-13, "layouts O")
-        _close(a[1], b[1], 1e-12, 1e-13, "layouts LSE")
+        for layout in (STRIPED, ZIGZAG):
+            b = orc.ring_emulate(q, k, v, R, layout, 0.5, True)
+            _close(a[0], b[0], 1e-12, 1e-13, "layouts O")
+            _close(a[1], b[1], 1e-12, 1e-13, "layouts LSE")
 
 
 # --------------------------------------------------------------------------- PIN-10
@@ -356,7 +391,7 @@ def check_pair_counts(orc):
     """Per-rank causal pair counts: brute force equals the closed forms, sums to
     S(S+1)/2; the striped layout is balanced to within one row per block ([ZZ])."""
     for S, R in ((8, 2), (16, 4), (24, 4), (32, 8), (64, 8), (60, 6), (48, 3), (128, 16)):
-        for layout in (CONTIGUOUS, STRIPED):
+        for layout in layouts_for(S, R):
             W = orc.pair_counts(layout, S, R)
             assert (W == closed_form_counts(layout, S, R)).all(), (S, R, layout, W)
             assert W.sum() == S * (S + 1) // 2
@@ -371,7 +406,7 @@ def check_coverage(orc):
     z = np.zeros((B, H, S, d), np.float32)
     v = np.ones((B, H, S, d), np.float32)
     for R in (1, 2, 4, 5, 8):
-        for layout in (CONTIGUOUS, STRIPED):
+        for layout in layouts_for(S, R):
             for causal in (True, False):
                 _, lse = orc.ring_emulate(z, z, v, R, layout, 1.0, causal)
                 seen = np.exp(lse[0, 0])
@@ -395,7 +430,7 @@ def check_gqa_equals_repeated_mha(orc):
 
 
 ALL_CHECKS = [
-    check_layout_golden, check_layout_bijection, check_brute_force, check_block_partial_brute,
+    check_layout_golden, check_layout_bijection, check_zigzag_layout, check_brute_force, check_block_partial_brute,
     check_identical_keys, check_dominant_logit, check_constant_values, check_key_shift,
     check_library_sdpa, check_ring_equals_full, check_layout_independence, check_merge_algebra,
     check_pair_counts, check_coverage, check_gqa_equals_repeated_mha,

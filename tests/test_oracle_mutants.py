@@ -15,12 +15,16 @@ MUTANTS = [
     ("scale dropped", "s *= scale;", "s *= 1.0;", 0),
     ("diagonal excluded", "int64_t last = causal ? t : S - 1;",
      "int64_t last = causal ? t - 1 : S - 1;", 1),
-    ("block mask off by one", "if (causal && kg0 + j * kstep > gq) continue;",
-     "if (causal && kg0 + j * kstep >= gq) continue;", 0),
+    ("block mask off by one", "if (causal && kid[j] > gq) continue;",
+     "if (causal && kid[j] >= gq) continue;", 0),
+    ("zig-zag late chunk mirrored wrong", ": (2 * (int64_t)R - 1 - r) * c + (j - c);",
+     ": (R + r) * c + (j - c);", 1),
+    ("ring key ids from the query rank", "for (int64_t j = 0; j < n; ++j) kid[j] = fwd[s * n + j];",
+     "for (int64_t j = 0; j < n; ++j) kid[j] = fwd[r * n + j];", 1),
     ("merge weight sign", "l_a[r] * exp(ma - m)", "l_a[r] * exp(m - ma)", 1),
     ("merge drops a weight", "(wa * o_a[r * d + c] + wb * o_b[r * d + c]) / l",
      "(o_a[r * d + c] + wb * o_b[r * d + c]) / l", 1),
-    ("striped equals contiguous", "? p : j * R + r;", "? p : r * n + j;", 1),
+    ("striped equals contiguous", "t = j * R + r;", "t = r * n + j;", 1),
     ("grouped head index", "int64_t g = h / group;\n    const float *kb = k + (b * Hkv + g) * S * d;",
      "int64_t g = h % Hkv;\n    const float *kb = k + (b * Hkv + g) * S * d;", 1),
     ("log base", "lse_rows[r] = m + log(l);", "lse_rows[r] = m + log2(l);", 1),
