@@ -69,8 +69,13 @@ def hop_pairs(w, layout_code):
                 tot += n * n
             elif layout_code == 0:  # contiguous: past block full, own block triangle, future none
                 tot += n * n if s < r else (n * (n + 1) // 2 if s == r else 0)
-            else:  # striped: key j allowed iff j*R+s <= i*R+r
+            elif layout_code == 1:  # striped: key j allowed iff j*R+s <= i*R+r
                 tot += n * (n + 1) // 2 if s <= r else n * (n - 1) // 2
+            else:  # zig-zag: chunks {r, 2R-1-r} x {s, 2R-1-s}, c tokens each
+                c = n // 2
+                for X in (r, 2 * R - 1 - r):
+                    for Y in (s, 2 * R - 1 - s):
+                        tot += c * c if Y < X else (c * (c + 1) // 2 if Y == X else 0)
         out.append(tot)
     return out
 
@@ -340,7 +345,9 @@ def main():
                                 float(np.median(step_ms)))
     merge = None if args.no_merge_bench else merge_bench(torch, rb)
     imbalance = {}
-    for name, code in (("contiguous", 0), ("striped", 1)):
+    for name, code in (("contiguous", 0), ("striped", 1), ("zigzag", 2)):
+        if code == 2 and w.S % (2 * w.R):
+            continue
         W = rb.ra_causal_work(code, w.S, w.R)
         imbalance[name] = float(W.max() / W.mean())
 
@@ -378,7 +385,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1))",
-        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "S": w.S,
+        "config": {"workload": w.name if layout in w.name else w.name.replace(w.layouts[0], layout),
+                   "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "S": w.S,
                    "R": w.R, "layout": layout, "causal": w.causal, "query_ranks":
                    list(range(w.rank0, w.rank0 + w.ranks)), "handoff": args.handoff,
                    "merge": args.merge},

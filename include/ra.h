@@ -61,7 +61,7 @@ typedef enum {
   RA_ERR_HIP = 7          /* a HIP runtime call failed                          */
 } ra_status;
 
-typedef enum { RA_LAYOUT_CONTIGUOUS = 0, RA_LAYOUT_STRIPED = 1 } ra_layout;
+typedef enum { RA_LAYOUT_CONTIGUOUS = 0, RA_LAYOUT_STRIPED = 1, RA_LAYOUT_ZIGZAG = 2 } ra_layout;
 typedef enum { RA_DT_BF16 = 0, RA_DT_FP16 = 1, RA_DT_FP32 = 2 } ra_dtype;
 /* How the next K/V block reaches a rank. COPY: an on-device copy on the copy
  * stream into the rank's receive buffer (the emulated link); SWAP: the rank
@@ -86,9 +86,15 @@ const char *ra_last_error(void);
  *     run of tokens):           fwd[p] = p
  *   RA_LAYOUT_STRIPED ([ZZ] interleaved assignment, rank r holds r, r+R,
  *     r+2R, ...):               fwd[r*n + j] = j*R + r
+ *   RA_LAYOUT_ZIGZAG ([ZZ] and [DE] "Zukunft" name a zig-zag assignment; read
+ *     as 2R chunks of c = S/(2R) tokens, rank r holding chunk r then chunk
+ *     2R-1-r, which gives every rank the same causal work):
+ *                               fwd[r*n + j] = r*c + j            (j < c)
+ *                               fwd[r*n + j] = (2R-1-r)*c + j - c  (j >= c)
  *   inv[fwd[p]] = p.
- * fwd, inv: device int32[S] (inv may be NULL).  Requires S % R == 0,
- * 1 <= R, S < 2^31.  Errors: RA_ERR_INVALID_ARG, RA_ERR_SHAPE, RA_ERR_HIP.
+ * fwd, inv: device int32[S] (inv may be NULL).  Requires S % R == 0 (S % 2R
+ * == 0 for zig-zag), 1 <= R, S < 2^31.  Errors: RA_ERR_INVALID_ARG,
+ * RA_ERR_SHAPE, RA_ERR_HIP.
  */
 ra_status ra_layout_permute(int32_t layout, int64_t S, int32_t R, int32_t *fwd,
                             int32_t *inv, ra_stream stream);
@@ -211,7 +217,8 @@ ra_status ra_finalize(const float *o_acc, const float *m, const float *l, void *
  * Computed query ranks r = rank0 .. rank0+n_ranks-1 (all R, or a single
  * rank's share; rank0 + n_ranks <= R).  At hop h = 0..R-1 rank r holds the block of source rank
  * s = (r - h) mod R.  Global token ids follow `layout` (contiguous: rank r,
- * local j -> r*n + j; striped: j*R + r).
+ * local j -> r*n + j; striped: j*R + r; zig-zag: the two chunks of
+ * ra_layout_permute, n even).
  *   q_sh  device [n_ranks][B][Hq][n][d]   query shards of the computed ranks
  *   k_sh, v_sh device [R][B][Hkv][n][d]   every source rank's K/V shard (on
  *         one GPU they stand in for the other ranks' memory)

@@ -16,12 +16,12 @@ RA_OK = 0
 STATUS_NAMES = {0: "RA_OK", 1: "RA_ERR_INVALID_ARG", 2: "RA_ERR_SHAPE", 3: "RA_ERR_DTYPE",
                 4: "RA_ERR_ALIGNMENT", 5: "RA_ERR_WORKSPACE", 6: "RA_ERR_UNSUPPORTED",
                 7: "RA_ERR_HIP"}
-LAYOUT_CONTIGUOUS, LAYOUT_STRIPED = 0, 1
+LAYOUT_CONTIGUOUS, LAYOUT_STRIPED, LAYOUT_ZIGZAG = 0, 1, 2
 DT_BF16, DT_FP16, DT_FP32 = 0, 1, 2
 HANDOFF_COPY, HANDOFF_SWAP = 0, 1
 MERGE_FUSED, MERGE_SEPARATE = 0, 1
 
-LAYOUTS = {"contiguous": LAYOUT_CONTIGUOUS, "striped": LAYOUT_STRIPED}
+LAYOUTS = {"contiguous": LAYOUT_CONTIGUOUS, "striped": LAYOUT_STRIPED, "zigzag": LAYOUT_ZIGZAG}
 
 EXPORTED = ("ra_version", "ra_status_string", "ra_last_error", "ra_layout_permute",
             "ra_layout_gather", "ra_layout_scatter", "ra_block_fwd", "ra_packed_v_bytes",

@@ -130,11 +130,24 @@ WsLayout ws_layout(const ra_ring_args *a) {
   return w;
 }
 
+bool known_layout(int32_t layout) {
+  return layout == RA_LAYOUT_CONTIGUOUS || layout == RA_LAYOUT_STRIPED ||
+         layout == RA_LAYOUT_ZIGZAG;
+}
+
+// Global token id of local position j of rank `rank` (the maps of
+// ra_layout_permute), n tokens per rank.
+int64_t layout_gid(int32_t layout, int32_t R, int64_t n, int32_t rank, int64_t j) {
+  if (layout == RA_LAYOUT_CONTIGUOUS) return (int64_t)rank * n + j;
+  if (layout == RA_LAYOUT_STRIPED) return j * R + rank;
+  const int64_t c = n / 2;
+  return j < c ? (int64_t)rank * c + j : (2 * (int64_t)R - 1 - rank) * c + (j - c);
+}
+
 ra_status check_ring(const ra_ring_args *a) {
   if (!a) return fail(RA_ERR_INVALID_ARG, "args is NULL");
   if (!elt_bytes(a->dtype)) return fail(RA_ERR_DTYPE, "unknown dtype %d", a->dtype);
-  if (a->layout != RA_LAYOUT_CONTIGUOUS && a->layout != RA_LAYOUT_STRIPED)
-    return fail(RA_ERR_INVALID_ARG, "unknown layout %d", a->layout);
+  if (!known_layout(a->layout)) return fail(RA_ERR_INVALID_ARG, "unknown layout %d", a->layout);
   if (a->handoff != RA_HANDOFF_COPY && a->handoff != RA_HANDOFF_SWAP)
     return fail(RA_ERR_INVALID_ARG, "unknown handoff %d", a->handoff);
   if (a->merge_mode != RA_MERGE_FUSED && a->merge_mode != RA_MERGE_SEPARATE)
@@ -150,6 +163,9 @@ ra_status check_ring(const ra_ring_args *a) {
   if (a->Hq % a->Hkv) return fail(RA_ERR_SHAPE, "Hq %% Hkv != 0 (%d, %d)", a->Hq, a->Hkv);
   if (a->d != 64 && a->d != 128) return fail(RA_ERR_SHAPE, "d must be 64 or 128 (got %d)", a->d);
   if (a->n < 0) return fail(RA_ERR_SHAPE, "n must be >= 0");
+  if (a->layout == RA_LAYOUT_ZIGZAG && a->n % 2)
+    return fail(RA_ERR_SHAPE, "zig-zag blocks hold two equal chunks: n must be even (got %d)",
+                a->n);
   if (a->dtype != RA_DT_FP32 && a->n > kMaxPackedKeys)
     return fail(RA_ERR_UNSUPPORTED, "16-bit ring blocks are limited to %lld tokens (got %d)",
                 (long long)kMaxPackedKeys, a->n);
@@ -240,9 +256,10 @@ const char *ra_last_error(void) { return g_err; }
 ra_status ra_layout_permute(int32_t layout, int64_t S, int32_t R, int32_t *fwd, int32_t *inv,
                             ra_stream stream) {
   clear_error();
-  if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED)
-    return fail(RA_ERR_INVALID_ARG, "unknown layout %d", layout);
+  if (!known_layout(layout)) return fail(RA_ERR_INVALID_ARG, "unknown layout %d", layout);
   if (R < 1 || S < 0 || S % R) return fail(RA_ERR_SHAPE, "need R >= 1, S >= 0, S %% R == 0");
+  if (layout == RA_LAYOUT_ZIGZAG && S % (2 * (int64_t)R))
+    return fail(RA_ERR_SHAPE, "zig-zag needs S %% 2R == 0");
   if (S > kMaxI32) return fail(RA_ERR_SHAPE, "S must be < 2^31");
   if (S > 0 && !fwd) return fail(RA_ERR_INVALID_ARG, "fwd is NULL");
   RA_HIP(launch_layout_permute(layout, S, R, fwd, inv, (hipStream_t)stream), "layout kernel");
@@ -506,6 +523,11 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
   p.kg_mult = contig ? n : 1;
   p.k_step = contig ? 1 : R;
   p.kg_smod = R;
+  if (a->layout == RA_LAYOUT_ZIGZAG) {  // two affine chunks per rank
+    p.zz_c = n / 2;
+    p.zz_R = R;
+    p.q_rank0 = r0;
+  }
   p.o_zstride = qz;
   p.os_b = p.qs_b;
   p.os_h = p.qs_h;
@@ -596,25 +618,29 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
 
 ra_status ra_causal_work(int32_t layout, int64_t S, int32_t R, int64_t *W) {
   clear_error();
-  if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED)
-    return fail(RA_ERR_INVALID_ARG, "unknown layout %d", layout);
+  if (!known_layout(layout)) return fail(RA_ERR_INVALID_ARG, "unknown layout %d", layout);
   if (R < 1 || S < 0 || S % R) return fail(RA_ERR_SHAPE, "need R >= 1, S >= 0, S %% R == 0");
+  if (layout == RA_LAYOUT_ZIGZAG && S % (2 * (int64_t)R))
+    return fail(RA_ERR_SHAPE, "zig-zag needs S %% 2R == 0");
   if (!W) return fail(RA_ERR_INVALID_ARG, "W is NULL");
   const int64_t n = S / R;
-  const bool contig = layout == RA_LAYOUT_CONTIGUOUS;
-  const int64_t step = contig ? 1 : R;
   for (int32_t r = 0; r < R; ++r) {
     int64_t total = 0;
-    const int64_t qg0 = contig ? (int64_t)r * n : r;
     for (int32_t h = 0; h < R; ++h) {
       const int32_t s = ((r - h) % R + R) % R;
-      const int64_t kg0 = contig ? (int64_t)s * n : s;
-      // allowed keys of query i form the prefix [0, (gq - kg0)/step + 1) of the block
+      // key ids increase along the block, so the allowed keys of query i
+      // form a prefix: count it by binary search over the block's ids
       for (int64_t i = 0; i < n; ++i) {
-        const int64_t gq = qg0 + i * step;
-        if (gq < kg0) continue;
-        const int64_t c = (gq - kg0) / step + 1;
-        total += c < n ? c : n;
+        const int64_t gq = layout_gid(layout, R, n, r, i);
+        int64_t lo = 0, hi = n;  // first key with id > gq
+        while (lo < hi) {
+          const int64_t mid = (lo + hi) / 2;
+          if (layout_gid(layout, R, n, s, mid) <= gq)
+            lo = mid + 1;
+          else
+            hi = mid;
+        }
+        total += lo;
       }
     }
     W[r] = total;

@@ -81,12 +81,61 @@ __device__ __forceinline__ bool wave_any(bool pred) {
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
+// Global token id of a local index: affine (contiguous and interleaved
+// layouts: b0 + j*step), or two affine chunks of c tokens (zig-zag: b0 + j,
+// then b1 + j - c).  Ids increase with j in every layout.
+struct IdMap {
+  int64_t b0, step, b1;
+  int32_t c;  // 0: affine
+  __device__ __forceinline__ int64_t operator()(int64_t j) const {
+    return (c == 0 || j < c) ? b0 + j * step : b1 + (j - c);
+  }
+};
+
+__device__ __forceinline__ IdMap zz_map(int64_t rank, const BatchParams &p) {
+  IdMap m;
+  m.b0 = rank * p.zz_c;
+  m.step = 1;
+  m.b1 = (2 * (int64_t)p.zz_R - 1 - rank) * p.zz_c;
+  m.c = p.zz_c;
+  return m;
+}
+
+// ids of the queries / keys of problem z of a batch
+__device__ __forceinline__ IdMap query_ids(const BatchParams &p, int z) {
+  if (p.zz_c) return zz_map(p.q_rank0 + z, p);
+  IdMap m;
+  m.b0 = p.qg_add + z * p.qg_z;
+  m.step = p.q_step;
+  m.b1 = 0;
+  m.c = 0;
+  return m;
+}
+__device__ __forceinline__ IdMap key_ids(const BatchParams &p, int z) {
+  const int64_t src = (p.kg_s0 + z) % p.kg_smod;
+  if (p.zz_c) return zz_map(src, p);
+  IdMap m;
+  m.b0 = p.kg_add + src * p.kg_mult;
+  m.step = p.k_step;
+  m.b1 = 0;
+  m.c = 0;
+  return m;
+}
+
 // Number of keys of the block allowed for a query with global id gq: the
 // allowed keys are always a prefix because key ids increase with j.
-__device__ __forceinline__ int key_prefix(const BatchParams &p, int64_t kg0, int64_t gq) {
+__device__ __forceinline__ int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+__device__ __forceinline__ int key_prefix(const BatchParams &p, const IdMap &k, int64_t gq) {
   if (!p.causal) return p.nk;
-  if (gq < kg0) return 0;
-  int64_t c = (gq - kg0) / p.k_step + 1;
+  if (k.c) {  // ids <= gq in each chunk: the chunks are runs of consecutive ids
+    const int64_t a = clamp64(gq - k.b0 + 1, 0, k.c);
+    const int64_t b = clamp64(gq - k.b1 + 1, 0, (int64_t)p.nk - k.c);
+    return (int)(a + b);
+  }
+  if (gq < k.b0) return 0;
+  int64_t c = (gq - k.b0) / k.step + 1;
   return c < p.nk ? (int)c : p.nk;
 }
 

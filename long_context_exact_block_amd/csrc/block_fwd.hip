@@ -79,8 +79,7 @@ __global__ void __launch_bounds__(256) attn_block16_kernel(BatchParams p, int nt
   const int kvi = (p.kv_idx0 + w.z) % p.kv_idx_mod;
   const short *kp = (const short *)p.k + kvi * p.kv_zstride + w.b * p.ks_b + w.kvh * p.ks_h;
   const short *vp = (const short *)p.v + kvi * p.kv_vzstride + w.b * p.vs_b + w.kvh * p.vs_h;
-  const int64_t qg0 = p.qg_add + w.z * p.qg_z;
-  const int64_t kg0 = p.kg_add + (int64_t)((p.kg_s0 + w.z) % p.kg_smod) * p.kg_mult;
+  const IdMap qid = query_ids(p, w.z), kid = key_ids(p, w.z);
   const float c = p.scale * kLog2e;
 
   const int i_wg0 = w.qtile * kBM;
@@ -89,10 +88,10 @@ __global__ void __launch_bounds__(256) attn_block16_kernel(BatchParams p, int nt
   const int iw1 = min(p.nq - 1, iw0 + kQB * 32 - 1);
   const bool wave_rows = iw0 < p.nq;
 
-  const int kv_wg = key_prefix(p, kg0, qg0 + (int64_t)i_wg1 * p.q_step);
+  const int kv_wg = key_prefix(p, kid, qid(i_wg1));
   const int ntiles = (kv_wg + kBN - 1) / kBN;
-  const int kv_wl = wave_rows ? key_prefix(p, kg0, qg0 + (int64_t)iw1 * p.q_step) : 0;
-  const int kv_wf = wave_rows ? key_prefix(p, kg0, qg0 + (int64_t)iw0 * p.q_step) : 0;
+  const int kv_wl = wave_rows ? key_prefix(p, kid, qid(iw1)) : 0;
+  const int kv_wf = wave_rows ? key_prefix(p, kid, qid(iw0)) : 0;
   const int ntiles_w = (kv_wl + kBN - 1) / kBN;
   const int nfull_w = kv_wf / kBN;
 
@@ -105,7 +104,7 @@ __global__ void __launch_bounds__(256) attn_block16_kernel(BatchParams p, int nt
   for (int qb = 0; qb < kQB; ++qb) {
     row[qb] = iw0 + qb * 32 + c32;
     valid[qb] = row[qb] < p.nq;
-    jlim[qb] = key_prefix(p, kg0, qg0 + (int64_t)row[qb] * p.q_step);
+    jlim[qb] = key_prefix(p, kid, qid(row[qb]));
   }
 
   f32x16 O[kQB][DT];
@@ -259,19 +258,18 @@ __global__ void __launch_bounds__(256) attn_block32_kernel(BatchParams p, int nt
   const int kvi = (p.kv_idx0 + w.z) % p.kv_idx_mod;
   const float *kp = (const float *)p.k + kvi * p.kv_zstride + w.b * p.ks_b + w.kvh * p.ks_h;
   const float *vp = (const float *)p.v + kvi * p.kv_vzstride + w.b * p.vs_b + w.kvh * p.vs_h;
-  const int64_t qg0 = p.qg_add + w.z * p.qg_z;
-  const int64_t kg0 = p.kg_add + (int64_t)((p.kg_s0 + w.z) % p.kg_smod) * p.kg_mult;
+  const IdMap qid = query_ids(p, w.z), kid = key_ids(p, w.z);
   const float c = p.scale * kLog2e;
 
   const int i_wg0 = w.qtile * kBM32;
   const int i_wg1 = min(p.nq, i_wg0 + kBM32) - 1;
-  const int kv_wg = key_prefix(p, kg0, qg0 + (int64_t)i_wg1 * p.q_step);
+  const int kv_wg = key_prefix(p, kid, qid(i_wg1));
   const int ntiles = (kv_wg + kBN32 - 1) / kBN32;
   if (ntiles == 0 && p.accumulate) return;
 
   const int i = i_wg0 + wave * 32 + c32;
   const bool valid = i < p.nq;
-  const int jl = key_prefix(p, kg0, qg0 + (int64_t)i * p.q_step);
+  const int jl = key_prefix(p, kid, qid(i));
 
   f32x16 O[DT];
   float m_run, m_top, lsum;

@@ -109,8 +109,7 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
   const int kvi = (p.kv_idx0 + w.z) % p.kv_idx_mod;
   const short *kp = (const short *)p.k + kvi * p.kv_zstride + w.b * p.ks_b + w.kvh * p.ks_h;
   const short *vp = (const short *)p.v + kvi * p.kv_vzstride + w.b * p.vs_b + w.kvh * p.vs_h;
-  const int64_t qg0 = p.qg_add + w.z * p.qg_z;
-  const int64_t kg0 = p.kg_add + (int64_t)((p.kg_s0 + w.z) % p.kg_smod) * p.kg_mult;
+  const IdMap qid = query_ids(p, w.z), kid = key_ids(p, w.z);
   const float c = p.scale * kLog2e;
 
   const int i_wg0 = w.qtile * kPBM;
@@ -121,13 +120,13 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
   const int i = iw0 + c32;
   const bool valid = i < p.nq;
 
-  const int kv_wg = key_prefix(p, kg0, qg0 + (int64_t)i_wg1 * p.q_step);
+  const int kv_wg = key_prefix(p, kid, qid(i_wg1));
   const int ntiles = (kv_wg + kPBN - 1) / kPBN;
-  const int kv_wl = wave_rows ? key_prefix(p, kg0, qg0 + (int64_t)iw1 * p.q_step) : 0;
-  const int kv_wf = wave_rows ? key_prefix(p, kg0, qg0 + (int64_t)iw0 * p.q_step) : 0;
+  const int kv_wl = wave_rows ? key_prefix(p, kid, qid(iw1)) : 0;
+  const int kv_wf = wave_rows ? key_prefix(p, kid, qid(iw0)) : 0;
   const int ntiles_w = (kv_wl + kPBN - 1) / kPBN;
   const int nfull_w = kv_wf / kPBN;
-  const int jlim = key_prefix(p, kg0, qg0 + (int64_t)i * p.q_step);
+  const int jlim = key_prefix(p, kid, qid(i));
 
   if (ntiles == 0 && p.accumulate) return;  // nothing to add to the running state
 

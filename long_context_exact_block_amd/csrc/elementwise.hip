@@ -104,7 +104,14 @@ __global__ void layout_kernel(int layout, int64_t S, int32_t R, int64_t n, int32
   const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (p >= S) return;
   const int64_t r = p / n, j = p - r * n;
-  const int64_t t = (layout == RA_LAYOUT_CONTIGUOUS) ? p : j * R + r;
+  const int64_t c = n >> 1;  // zig-zag chunk length
+  int64_t t;
+  if (layout == RA_LAYOUT_CONTIGUOUS)
+    t = p;
+  else if (layout == RA_LAYOUT_STRIPED)
+    t = j * R + r;
+  else
+    t = j < c ? r * c + j : (2 * (int64_t)R - 1 - r) * c + (j - c);
   fwd[p] = (int32_t)t;
   if (inv) inv[t] = (int32_t)p;
 }

@@ -16,6 +16,10 @@ namespace ra {
 //   v          = v + ((kv_idx0 + z) % kv_idx_mod) * kv_vzstride
 //   qgid(i)    = qg_add + z*qg_z + i*q_step
 //   kgid(j)    = kg_add + ((kg_s0 + z) % kg_smod)*kg_mult + j*k_step
+// or, when zz_c > 0 (zig-zag ids, two chunks of zz_c tokens per rank), with
+// rank = q_rank0 + z for queries and (kg_s0 + z) % kg_smod for keys:
+//   gid(j)     = rank*zz_c + j                    (j < zz_c)
+//              = (2*zz_R - 1 - rank)*zz_c + j - zz_c  (j >= zz_c)
 //   o, m, l    = + z*o_zstride / z*ml_zstride
 // which covers one public block call (nz = 1) and one ring hop over all
 // computed ranks (z = rank index, block index and key ids follow the ring).
@@ -47,6 +51,7 @@ struct BatchParams {
   // partial).  0: it may be any reference maximum the stored l is relative
   // to (a running state between hops; m + ln l is the same).
   int32_t exact_m;
+  int32_t zz_c, zz_R, q_rank0;
 };
 
 // Packed V: for each (b, h) a [d][n_pad] array, n_pad = n rounded up to 64,

@@ -155,6 +155,7 @@ def test_ring_workspace_checks(lib):
 
 def test_layout_rejects(lib):
     assert lib.ra_layout_permute(0, 10, 4, ctypes.c_void_p(4096), None, None) == 2
+    assert lib.ra_layout_permute(2, 12, 4, ctypes.c_void_p(4096), None, None) == 2  # S % 2R
     assert lib.ra_layout_permute(3, 8, 4, ctypes.c_void_p(4096), None, None) == 1
     assert lib.ra_layout_permute(1, 8, 4, None, None, None) == 1
     assert lib.ra_layout_gather(4096, 8192, 4096, 3, 1, 1, 8, 4, 4, 0, 4, None) == 1
@@ -172,13 +173,21 @@ def test_merge_finalize_reject(lib):
                                  (128, 16), (1024, 4), (512, 64)])
 def test_causal_work_matches_oracle_brute_force(lib, ora, S, R):
     """The library's per-rank causal work equals brute-force counting (bit-exact)."""
-    for layout in (rb.LAYOUT_CONTIGUOUS, rb.LAYOUT_STRIPED):
+    for layout in pins.layouts_for(S, R):
         assert np.array_equal(rb.ra_causal_work(layout, S, R), ora.pair_counts(layout, S, R))
 
 
 @pytest.mark.parametrize("S,R", [(32768, 8), (131072, 8), (1048576, 8), (32768, 64)])
 def test_causal_work_closed_forms_at_full_size(lib, S, R):
-    for layout in (rb.LAYOUT_CONTIGUOUS, rb.LAYOUT_STRIPED):
+    for layout in (rb.LAYOUT_CONTIGUOUS, rb.LAYOUT_STRIPED, rb.LAYOUT_ZIGZAG):
         W = rb.ra_causal_work(layout, S, R)
         assert np.array_equal(W, pins.closed_form_counts(layout, S, R))
         assert W.sum() == S * (S + 1) // 2
+    # zig-zag: every rank the same causal work
+    assert len(set(rb.ra_causal_work(rb.LAYOUT_ZIGZAG, S, R).tolist())) == 1
+
+
+def test_ring_rejects_odd_zigzag_blocks(lib):
+    a = _ring(layout=2, n=255)
+    st = lib.ra_ring_fwd(ctypes.byref(a), ctypes.c_void_p(4096), 1 << 40, None, None)
+    assert st == 2 and "even" in rb.last_error()

@@ -28,6 +28,12 @@ CASES = [
     ("fp16_contig_R16_short", 2, 2, 2, 2048, 64, 16, "contiguous", "fp16", False, 0, 16),
     ("bf16_striped_ragged_n", 1, 2, 2, 8 * 200, 128, 8, "striped", "bf16", True, 0, 8),
     ("fp32_contig_R2_d128", 1, 2, 1, 512, 128, 2, "contiguous", "fp32", True, 0, 2),
+    ("bf16_zigzag_R4_gqa", 1, 4, 2, 2048, 128, 4, "zigzag", "bf16", True, 0, 4),
+    ("fp16_zigzag_R8_d64", 2, 2, 2, 4096, 64, 8, "zigzag", "fp16", True, 0, 8),
+    ("bf16_zigzag_rank5_of_8", 1, 2, 2, 8192, 128, 8, "zigzag", "bf16", True, 5, 1),
+    ("bf16_zigzag_ragged_chunks", 1, 2, 2, 8 * 200, 128, 4, "zigzag", "bf16", True, 0, 4),
+    ("fp32_zigzag_R3", 1, 2, 2, 768, 64, 3, "zigzag", "fp32", True, 0, 3),
+    ("bf16_zigzag_noncausal", 1, 2, 2, 1024, 128, 4, "zigzag", "bf16", False, 0, 4),
 ]
 
 
@@ -131,14 +137,14 @@ def test_running_max_rises_across_tiles_and_hops(dtype, layout):
 
 
 def test_layouts_agree_after_unpermuting():
-    """Contiguous and striped rings give the same outputs in the original order."""
-    case_c = ("c", 1, 2, 2, 2048, 128, 8, "contiguous", "bf16", True, 0, 8)
-    case_s = ("s", 1, 2, 2, 2048, 128, 8, "striped", "bf16", True, 0, 8)
+    """Contiguous, striped and zig-zag rings give the same outputs in the original order."""
     x = make_inputs(1, 2, 2, 2048, 128, "bf16", 79)
+    case_c = ("c", 1, 2, 2, 2048, 128, 8, "contiguous", "bf16", True, 0, 8)
     _, oc, lc = run_ring(case_c, x)
-    _, os_, ls = run_ring(case_s, x)
-    assert np.abs(parity.to_f64(oc) - parity.to_f64(os_)).max() <= 2e-2
-    assert np.abs(parity.to_f64(lc) - parity.to_f64(ls)).max() <= 1e-3
+    for layout in ("striped", "zigzag"):
+        _, o2, l2 = run_ring(("s", 1, 2, 2, 2048, 128, 8, layout, "bf16", True, 0, 8), x)
+        assert np.abs(parity.to_f64(oc) - parity.to_f64(o2)).max() <= 2e-2
+        assert np.abs(parity.to_f64(lc) - parity.to_f64(l2)).max() <= 1e-3
 
 
 def test_repeated_calls_do_not_grow_memory():
