@@ -198,6 +198,48 @@ def overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse, t_c
             "overlap": round(1.0 - (t_copy_ms - t_swap) / t_copies, 3) if t_copies > 0 else None}
 
 
+def decode_bench(torch, rb, w, iters=20):
+    """ra_decode_fwd on the long-context decode step (w: DecodeWorkload): nq new
+    tokens against the whole KV cache, split contiguously over R ranks.  HBM
+    roofline: algorithmic bytes = the cache (K and V, each key once) + Q, O, LSE."""
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[w.dtype]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed)
+    n = w.n
+    q = torch.randn(w.B, w.Hq, w.nq, w.d, device="cuda", generator=g).to(tdt)
+    k = torch.randn(w.R, w.B, w.Hkv, n, w.d, device="cuda", generator=g).to(tdt)
+    v = torch.randn(w.R * w.B, w.Hkv, n, w.d, device="cuda", generator=g).to(tdt)
+    vp = torch.empty(rb.ra_packed_v_bytes(rb.dtype_code(v), w.R * w.B, w.Hkv, n, w.d) // 2,
+                     dtype=tdt, device="cuda")
+    rb.ra_pack_v(v, vp)
+    del v
+    o = torch.empty(w.B, w.Hq, w.nq, w.d, dtype=tdt, device="cuda")
+    lse = torch.empty(w.B, w.Hq, w.nq, dtype=torch.float32, device="cuda")
+    a = rb.decode_args(q, k, vp, o, lse, 1.0 / math.sqrt(w.d), w.causal, w.S - w.nq)
+    ws = torch.empty(rb.ra_decode_fwd_workspace_size(a), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        rb.ra_decode_fwd(a, ws)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(iters):
+        rb.ra_decode_fwd(a, ws)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(iters)])
+    med = float(np.median(ms))
+    nbytes = w.io_bytes()
+    gbs = nbytes / (med * 1e-3) / 1e9
+    del k, vp, ws
+    return {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "cache_tokens": w.S,
+            "R": w.R, "new_tokens": w.nq, "dtype": w.dtype,
+            "ms_median": round(med, 4), "ms_min": round(float(ms.min()), 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes_per_call": nbytes,
+                         "kernels": "decode_kernel<128,bf16> + decode_reduce_kernel"}}
+
+
 def block_only(torch, rb, w, layout, steps, warmup):
     """One hop of the workload through ra_block_fwd: the first computed rank's query shard
     against the block of the same source rank (hop 0), packed V, fresh state."""
@@ -253,6 +295,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge-bench", action="store_true")
+    ap.add_argument("--no-decode-bench", action="store_true",
+                    help="skip the long-context decode measurement (ra_decode_fwd)")
     ap.add_argument("--no-overlap-bench", action="store_true",
                     help="skip the hand-off overlap measurement (SWAP steps + copies alone)")
     ap.add_argument("--block-only", action="store_true",
@@ -344,6 +388,7 @@ def main():
         handoff = overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse,
                                 float(np.median(step_ms)))
     merge = None if args.no_merge_bench else merge_bench(torch, rb)
+    decode = None if args.no_decode_bench else decode_bench(torch, rb, configs.DECODE_1M)
     imbalance = {}
     for name, code in (("contiguous", 0), ("striped", 1), ("zigzag", 2)):
         if code == 2 and w.S % (2 * w.R):
@@ -402,6 +447,7 @@ def main():
         "hop_ms": [round(float(x), 3) for x in hop_ms.mean(axis=0)],
         "handoff": handoff,
         "merge": merge,
+        "decode": decode,
         "causal_imbalance_max_over_mean": imbalance,
         "cpu_baseline": cpu,
     }

@@ -172,11 +172,12 @@ ra_status ra_block_fwd(const ra_block_args *a, ra_stream stream);
  * ra_pack_v -- repack V rows for the fast PV path of ra_block_fwd (the ring
  * does this itself).  v: device [B][H][n][d] with element strides v_stride
  * (d contiguous, 16-byte aligned rows); vp: device, ra_packed_v_bytes bytes.
- * Packed layout: per (b, h) a [d][n_pad] array, n_pad = n rounded up to 64;
- * row c, position q holds V[b][h][key][c] with key = q except that within
- * every 16 positions the 2nd and 3rd groups of four keys are swapped (the
- * order in which the probability matrix feeds the PV product); zero where
- * key >= n.  bf16 / fp16 only.
+ * Packed layout: per (b, h), n_pad/64 tiles (n_pad = n rounded up to 64),
+ * each a [d][64] array: tile T, row c, position q holds V[b][h][key][c] with
+ * key = 64T + q except that within every 16 positions the 2nd and 3rd groups
+ * of four keys are swapped (the order in which the probability matrix feeds
+ * the PV product); zero where key >= n.  A 64-key tile of V^T is one
+ * contiguous d*128-byte block.  bf16 / fp16 only.
  * Errors: RA_ERR_INVALID_ARG, RA_ERR_SHAPE, RA_ERR_DTYPE, RA_ERR_ALIGNMENT,
  * RA_ERR_HIP.
  */
@@ -264,6 +265,43 @@ size_t ra_ring_fwd_workspace_size(const ra_ring_args *a);
 
 ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_bytes,
                       ra_stream compute, ra_stream copy);
+
+/*
+ * ra_decode_fwd -- nq new query tokens against a KV cache split over R ranks:
+ * rank r holds the contiguous run of tokens r*n .. r*n + n - 1 ([DE]
+ * "Tiefer Einblick": contiguous split; "Reale Umsetzung": serving long
+ * contexts).  Every rank's run yields partial attention of the new queries
+ * (several partials per run on one GPU), and all partials of a row are
+ * folded with the online-softmax combine of ra_merge ([TH]; [DE] FAQ).
+ *   q   device [B][Hq][nq][d]   new queries, contiguous
+ *   k   device [R][B][Hkv][n][d] the cache shards, contiguous
+ *   v   device, the shards' V in the packed layout: ra_pack_v applied to V
+ *       seen as [R*B][Hkv][n][d] (ra_packed_v_bytes(dtype, R*B, Hkv, n, d))
+ *   query i is token q_gid0 + i; causal: it attends to cache tokens <= its
+ *   own (the new tokens' own K/V are expected in the cache); otherwise to all
+ *   o   device [B][Hq][nq][d] in dtype; lse device fp32 [B][Hq][nq]
+ *   (natural log; a row that sees no key gets O = 0, LSE = -inf)
+ * Grouped heads: query head h uses K/V head h / (Hq/Hkv).  16-bit dtypes
+ * only; d in {64, 128}; 1 <= nq and (Hq/Hkv)*nq <= 256; n <= 2^23; R <= 512.
+ * The workspace (ra_decode_fwd_workspace_size bytes, 256-byte aligned)
+ * holds the fp32 partials.  Asynchronous on `stream`.
+ * Errors: RA_ERR_INVALID_ARG, RA_ERR_SHAPE, RA_ERR_DTYPE, RA_ERR_ALIGNMENT,
+ * RA_ERR_WORKSPACE, RA_ERR_UNSUPPORTED, RA_ERR_HIP.
+ */
+typedef struct {
+  const void *q, *k, *v;
+  int32_t dtype; /* ra_dtype: RA_DT_BF16 or RA_DT_FP16 */
+  int32_t R, B, Hq, Hkv, nq, n, d;
+  float scale;
+  int32_t causal;
+  int64_t q_gid0;
+  void *o;
+  float *lse;
+} ra_decode_args;
+
+size_t ra_decode_fwd_workspace_size(const ra_decode_args *a);
+ra_status ra_decode_fwd(const ra_decode_args *a, void *workspace, size_t workspace_bytes,
+                        ra_stream stream);
 
 /*
  * ra_causal_work -- per-rank count of allowed causal (query, key) pairs over

@@ -26,7 +26,7 @@ LAYOUTS = {"contiguous": LAYOUT_CONTIGUOUS, "striped": LAYOUT_STRIPED, "zigzag":
 EXPORTED = ("ra_version", "ra_status_string", "ra_last_error", "ra_layout_permute",
             "ra_layout_gather", "ra_layout_scatter", "ra_block_fwd", "ra_packed_v_bytes",
             "ra_pack_v", "ra_merge", "ra_finalize", "ra_ring_fwd_workspace_size", "ra_ring_fwd",
-            "ra_causal_work")
+            "ra_causal_work", "ra_decode_fwd_workspace_size", "ra_decode_fwd")
 
 
 class RAError(RuntimeError):
@@ -58,6 +58,12 @@ class RingArgs(ctypes.Structure):
                 ("hop_events", ctypes.POINTER(P))]
 
 
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("q", P), ("k", P), ("v", P), ("dtype", I32), ("R", I32), ("B", I32),
+                ("Hq", I32), ("Hkv", I32), ("nq", I32), ("n", I32), ("d", I32),
+                ("scale", ctypes.c_float), ("causal", I32), ("q_gid0", I64), ("o", P), ("lse", P)]
+
+
 _lib = None
 
 
@@ -78,6 +84,9 @@ def lib():
     L.ra_layout_gather.argtypes = [P, P, P, I32, I64, I64, I64, I64, I32, I32, I32, P]
     L.ra_layout_scatter.argtypes = [P, P, P, I32, I64, I64, I64, I64, I32, I32, I32, P]
     L.ra_block_fwd.argtypes = [ctypes.POINTER(BlockArgs), P]
+    L.ra_decode_fwd_workspace_size.argtypes = [ctypes.POINTER(DecodeArgs)]
+    L.ra_decode_fwd_workspace_size.restype = ctypes.c_size_t
+    L.ra_decode_fwd.argtypes = [ctypes.POINTER(DecodeArgs), P, ctypes.c_size_t, P]
     L.ra_packed_v_bytes.argtypes = [I32, I32, I32, I32, I32]
     L.ra_packed_v_bytes.restype = ctypes.c_size_t
     L.ra_pack_v.argtypes = [P, P, I32, I32, I32, I32, I32, ctypes.POINTER(I64), P]
@@ -241,6 +250,33 @@ def ra_ring_fwd(args: RingArgs, workspace, compute_stream=None, copy_stream=None
     cs = _stream(compute_stream)
     xs = _stream(copy_stream) if copy_stream is not None else cs
     _check(lib().ra_ring_fwd(ctypes.byref(args), ws_ptr, ws_bytes, cs, xs))
+
+
+def decode_args(q, k, vp, o, lse, scale, causal, q_gid0) -> DecodeArgs:
+    """q [B][Hq][nq][d]; k [R][B][Hkv][n][d]; vp: ra_pack_v of V as [R*B][Hkv][n][d];
+    o like q; lse fp32 [B][Hq][nq]."""
+    B, Hq, nq, d = q.shape
+    R, _, Hkv, n, _ = k.shape
+    a = DecodeArgs()
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(vp)
+    a.dtype = dtype_code(q)
+    a.R, a.B, a.Hq, a.Hkv, a.nq, a.n, a.d = R, B, Hq, Hkv, nq, n, d
+    a.scale, a.causal, a.q_gid0 = float(scale), int(bool(causal)), int(q_gid0)
+    a.o, a.lse = _ptr(o), _ptr(lse)
+    return a
+
+
+def ra_decode_fwd_workspace_size(args: DecodeArgs) -> int:
+    nb = lib().ra_decode_fwd_workspace_size(ctypes.byref(args))
+    if nb == 0:
+        raise RAError(1, last_error())
+    return nb
+
+
+def ra_decode_fwd(args: DecodeArgs, workspace, stream=None):
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().ra_decode_fwd(ctypes.byref(args), ws_ptr, ws_bytes, _stream(stream)))
 
 
 def ra_causal_work(layout: int, S: int, R: int):

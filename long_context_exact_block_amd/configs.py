@@ -65,3 +65,40 @@ SHORT_512 = Workload("noncausal_fp16_S32k_R64_512tok", 5, 4, 16, 16, 64, 32768, 
 
 ALL = (TINY, MHA_32K, GQA_128K, SHARE_1M, SHORT_512)
 BY_NAME = {w.name: w for w in ALL}
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """nq new query tokens against a KV cache of S tokens split contiguously over R ranks."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    S: int
+    R: int
+    nq: int
+    causal: bool
+    dtype: str
+    seed: int
+
+    @property
+    def n(self) -> int:
+        return self.S // self.R
+
+    def cache_bytes(self) -> int:
+        """K and V of the whole cache in the input dtype (each key read once)."""
+        elt = 4 if self.dtype == "fp32" else 2
+        return 2 * self.B * self.Hkv * self.S * self.d * elt
+
+    def io_bytes(self) -> int:
+        """Algorithmic bytes of one decode step: the cache, the new queries, O and LSE."""
+        elt = 4 if self.dtype == "fp32" else 2
+        rows = self.B * self.Hq * self.nq
+        return self.cache_bytes() + rows * self.d * elt * 2 + rows * 4
+
+
+# the long-context decode step: 4 new tokens (e.g. speculative decoding) against a
+# 1M-token cache sharded over 8 ranks, grouped heads 32 -> 8, bf16
+DECODE_1M = DecodeWorkload("decode_4tok_gqa_bf16_cache1M_R8", 1, 32, 8, 128, 1048576, 8, 4, True,
+                           "bf16", 6000)

@@ -11,6 +11,7 @@
 // "Tiefer Einblick", and its Thai version, technical-insight section.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -142,6 +143,69 @@ int64_t layout_gid(int32_t layout, int32_t R, int64_t n, int32_t rank, int64_t j
   if (layout == RA_LAYOUT_STRIPED) return j * R + rank;
   const int64_t c = n / 2;
   return j < c ? (int64_t)rank * c + j : (2 * (int64_t)R - 1 - rank) * c + (j - c);
+}
+
+ra_status check_decode(const ra_decode_args *a) {
+  if (!a) return fail(RA_ERR_INVALID_ARG, "args is NULL");
+  if (a->dtype != RA_DT_BF16 && a->dtype != RA_DT_FP16) {
+    if (a->dtype == RA_DT_FP32) return fail(RA_ERR_UNSUPPORTED, "decode reads packed 16-bit V");
+    return fail(RA_ERR_DTYPE, "unknown dtype %d", a->dtype);
+  }
+  if (a->R < 1 || a->R > 512) return fail(RA_ERR_SHAPE, "R must be in [1, 512] (got %d)", a->R);
+  if (a->B < 1 || a->Hq < 1 || a->Hkv < 1) return fail(RA_ERR_SHAPE, "B, Hq, Hkv must be >= 1");
+  if (a->Hq % a->Hkv) return fail(RA_ERR_SHAPE, "Hq %% Hkv != 0 (%d, %d)", a->Hq, a->Hkv);
+  if (a->d != 64 && a->d != 128) return fail(RA_ERR_SHAPE, "d must be 64 or 128 (got %d)", a->d);
+  if (a->nq < 1 || (int64_t)(a->Hq / a->Hkv) * a->nq > 256)
+    return fail(RA_ERR_SHAPE, "need 1 <= nq and (Hq/Hkv)*nq <= 256 (nq=%d)", a->nq);
+  if (a->n < 0) return fail(RA_ERR_SHAPE, "n must be >= 0");
+  if (a->n > kMaxPackedKeys)
+    return fail(RA_ERR_UNSUPPORTED, "cache shards are limited to %lld tokens",
+                (long long)kMaxPackedKeys);
+  if ((int64_t)a->n * a->R > kMaxI32) return fail(RA_ERR_SHAPE, "R*n must be < 2^31");
+  if (!(a->scale > 0.f) || !std::isfinite(a->scale))
+    return fail(RA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!a->q || !a->o || !a->lse || (a->n > 0 && (!a->k || !a->v)))
+    return fail(RA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned16(a->q) || !aligned16(a->o) || (a->n > 0 && (!aligned16(a->k) || !aligned16(a->v))))
+    return fail(RA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  return RA_OK;
+}
+
+// Work split of a decode call: enough workgroups to fill the GPU, every wave
+// a run of keys (a multiple of 32), one partial per workgroup, at most 4096
+// partials per row.
+DecodeParams decode_plan(const ra_decode_args *a) {
+  DecodeParams p{};
+  p.B = a->B;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.nq = a->nq;
+  p.n = a->n;
+  p.d = a->d;
+  p.R = a->R;
+  p.n_pad = packed_n(a->n);
+  p.scale = a->scale;
+  p.causal = a->causal ? 1 : 0;
+  p.q_gid0 = a->q_gid0;
+  p.col_blocks = ((a->Hq / a->Hkv) * a->nq + 31) / 32;
+  const int64_t groups = (int64_t)a->R * a->B * a->Hkv * p.col_blocks;
+  const int64_t W = kDecodeWaves;
+  const int64_t max_splits = std::max<int64_t>(1, (a->n + W * 32 - 1) / (W * 32));
+  const int64_t want = 1024;  // workgroups: four per CU keep the GPU busy to the end
+  int64_t splits = std::min<int64_t>(max_splits, std::max<int64_t>(1, (want + groups - 1) / groups));
+  splits = std::min<int64_t>(splits, std::max<int64_t>(1, 4096 / (int64_t)a->R));
+  int64_t wk = (a->n + splits * W - 1) / (splits * W);
+  wk = std::max<int64_t>(32, (wk + 31) / 32 * 32);
+  splits = std::max<int64_t>(1, (a->n + W * wk - 1) / (W * wk));
+  p.splits = (int32_t)splits;
+  p.wave_keys = (int32_t)wk;
+  p.P = (int32_t)(a->R * splits);
+  return p;
+}
+
+size_t decode_ws_bytes(const DecodeParams &p) {
+  const size_t rows = (size_t)p.B * p.Hq * p.nq;
+  return align256((size_t)p.P * rows * p.d * 4) + 2 * align256((size_t)p.P * rows * 4);
 }
 
 ra_status check_ring(const ra_ring_args *a) {
@@ -613,6 +677,33 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
   }
   RA_HIP(launch_finalize(o_acc, m_acc, l_acc, a->o, a->lse, a->dtype, rows, a->d, cs),
          "finalize kernel");
+  return RA_OK;
+}
+
+size_t ra_decode_fwd_workspace_size(const ra_decode_args *a) {
+  clear_error();
+  if (check_decode(a) != RA_OK) return 0;
+  return decode_ws_bytes(decode_plan(a));
+}
+
+ra_status ra_decode_fwd(const ra_decode_args *a, void *workspace, size_t workspace_bytes,
+                        ra_stream stream) {
+  clear_error();
+  ra_status st = check_decode(a);
+  if (st != RA_OK) return st;
+  DecodeParams p = decode_plan(a);
+  const size_t need = decode_ws_bytes(p);
+  if (!workspace || workspace_bytes < need || (uintptr_t)workspace % 256)
+    return fail(RA_ERR_WORKSPACE, "workspace must be >= %zu bytes, 256-byte aligned", need);
+  const size_t rows = (size_t)p.B * p.Hq * p.nq;
+  char *ws = (char *)workspace;
+  p.po = (float *)ws;
+  p.pm = (float *)(ws + align256((size_t)p.P * rows * p.d * 4));
+  p.pl = (float *)((char *)p.pm + align256((size_t)p.P * rows * 4));
+  p.q = a->q;
+  p.k = a->n > 0 ? a->k : a->q;  // never read when n == 0
+  p.v = a->n > 0 ? a->v : a->q;
+  RA_HIP(launch_decode(p, a->dtype, a->o, a->lse, (hipStream_t)stream), "decode kernels");
   return RA_OK;
 }
 

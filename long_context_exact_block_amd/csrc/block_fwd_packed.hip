@@ -175,8 +175,9 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
     for (int u = 0; u < VPW; ++u) {
       const int idx = wave + kPW * u;
       const int dr = idx * 8 + (lane >> 3);
-      vvo[u] = dr * ((uint32_t)p.vs_t * 2) + (((lane & 7) ^ chunk_swz<VROW>(dr)) * 16);
+      vvo[u] = dr * VROW + (((lane & 7) ^ chunk_swz<VROW>(dr)) * 16);  // within a V^T tile
     }
+    // the (b, h) slice of packed V: vs_t = n_pad, tiles of VTILE bytes
     const auto vrsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)vp, 0, (int)((uint32_t)D * (uint32_t)p.vs_t * 2u), kBufWord3);
     // One wave's share of K tile tk / V^T tile tv goes straight into an LDS
@@ -195,7 +196,7 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
 #pragma unroll
       for (int u = 0; u < VPW; ++u)
         dma16(vrsrc, (lds_void *)(lds + VBASE + vso + kPW * 1024 * u + wave * 1024), vvo[u],
-              tv * kPBN * 2);
+              tv * VTILE);
     };
 
     // Per-lane LDS read offsets.  Row kh*32 + c32 (K) and 32dt + c32 (V^T)
@@ -410,9 +411,9 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
   store_state<D>(p, w, i, valid, O, m_run, EXACT ? m_top : m_run, lsum);
 }
 
-// V rows [b][h][j][c] (strides) -> packed [bh][c][n_pad]; one workgroup per
-// (bh, 64-key window): coalesced 16-byte loads of key rows, LDS transpose,
-// coalesced 16-byte stores of 8 packed positions.
+// V rows [b][h][j][c] (strides) -> packed [bh][tile][c][64]; one workgroup
+// per (bh, 64-key tile): coalesced 16-byte loads of key rows, LDS transpose,
+// coalesced 16-byte stores of 8 packed positions (the tile is one block).
 __global__ void __launch_bounds__(256) pack_v_kernel(const short *__restrict__ v,
                                                      short *__restrict__ vp, int64_t H, int64_t n,
                                                      int64_t n_pad, int d, int64_t vs_b,
@@ -431,7 +432,7 @@ __global__ void __launch_bounds__(256) pack_v_kernel(const short *__restrict__ v
     *(uint4 *)&tile[key][c8 * 8] = val;
   }
   __syncthreads();
-  short *dst = vp + bh * (int64_t)d * n_pad + j0;
+  short *dst = vp + bh * (int64_t)d * n_pad + j0 * d;  // tile j0/64 of d x 64
   for (int e = threadIdx.x; e < d * (kPBN / 8); e += blockDim.x) {
     const int cidx = e / (kPBN / 8), g = e % (kPBN / 8);
     short out[8];
@@ -442,7 +443,7 @@ __global__ void __launch_bounds__(256) pack_v_kernel(const short *__restrict__ v
     val.y = (unsigned short)out[2] | ((unsigned)(unsigned short)out[3] << 16);
     val.z = (unsigned short)out[4] | ((unsigned)(unsigned short)out[5] << 16);
     val.w = (unsigned short)out[6] | ((unsigned)(unsigned short)out[7] << 16);
-    *(uint4 *)(dst + (int64_t)cidx * n_pad + g * 8) = val;
+    *(uint4 *)(dst + cidx * kPBN + g * 8) = val;
   }
 }
 

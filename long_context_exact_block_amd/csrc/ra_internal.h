@@ -54,10 +54,11 @@ struct BatchParams {
   int32_t zz_c, zz_R, q_rank0;
 };
 
-// Packed V: for each (b, h) a [d][n_pad] array, n_pad = n rounded up to 64,
-// position q of a row holding key perm16(q) (the 2nd and 3rd groups of four
-// keys of every 16 swapped) and zero past n.  This is the key order in which
-// the PV product consumes probabilities, so every operand read is 16 bytes.
+// Packed V: for each (b, h) n_pad/64 tiles of [d][64] (n_pad = n rounded up
+// to 64), position q of tile T's row c holding key 64T + perm16(q) (the 2nd
+// and 3rd groups of four keys of every 16 swapped), zero past n.  This is the
+// key order in which the PV product consumes probabilities, so every operand
+// read is 16 bytes, and a 64-key V^T tile is one contiguous block.
 constexpr int kPackAlign = 64;
 // The packed-V kernel addresses a (b, h) slice of packed V and a 64-row K tile
 // with 32-bit byte offsets: bound the packed row length and the K row stride.
@@ -69,6 +70,31 @@ hipError_t launch_pack_v(const void *v, void *vp, int elt, int64_t BH, int64_t H
 hipError_t launch_block_fwd_packed(const BatchParams &p, int dtype, hipStream_t s);
 
 hipError_t launch_block_fwd(const BatchParams &p, int dtype, hipStream_t s);
+
+// Decode: nq new queries per (b, query head) against a KV cache split over R
+// ranks, rank r holding tokens r*n .. r*n + n - 1.  Every wave streams its own
+// range of wave_keys keys of one (rank, b, kv head) for one block of 32 query
+// columns (column c = head-in-group * nq + query); the waves of a workgroup
+// fold their results into one partial (O normalised, m, l), and
+// decode_reduce folds the P partials of every row.
+constexpr int kDecodeWaves = 4;  // waves per decode workgroup (each streams its own keys)
+struct DecodeParams {
+  const void *q;  // [B][Hq][nq][d]
+  const void *k;  // [R][B][Hkv][n][d]
+  const void *v;  // packed: [R][B][Hkv][n_pad/64][d][64]
+  int32_t B, Hq, Hkv, nq, n, d, R;
+  int64_t n_pad;
+  float scale;
+  int32_t causal;
+  int64_t q_gid0;     // token of query i: q_gid0 + i
+  int32_t splits;     // key ranges per (rank, b, kv head), kDecodeWaves waves each
+  int32_t wave_keys;  // keys per wave (a multiple of 32)
+  int32_t col_blocks; // ceil(Hq/Hkv * nq / 32)
+  int32_t P;          // partials per row: R * splits
+  float *po, *pm, *pl;  // [P][rows][d], [P][rows], [P][rows]; rows = B*Hq*nq
+};
+hipError_t launch_decode(const DecodeParams &p, int dtype, void *o, float *lse,
+                         hipStream_t s);
 hipError_t launch_merge(float *o_acc, float *m_acc, float *l_acc, const float *o_blk,
                         const float *m_blk, const float *l_blk, int64_t rows, int32_t d,
                         hipStream_t s);

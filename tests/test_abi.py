@@ -191,3 +191,34 @@ def test_ring_rejects_odd_zigzag_blocks(lib):
     a = _ring(layout=2, n=255)
     st = lib.ra_ring_fwd(ctypes.byref(a), ctypes.c_void_p(4096), 1 << 40, None, None)
     assert st == 2 and "even" in rb.last_error()
+
+
+def _decode(**kw):
+    a = rb.DecodeArgs()
+    a.q = a.k = a.v = a.o = a.lse = 4096
+    a.dtype, a.R, a.B, a.Hq, a.Hkv, a.nq, a.n, a.d = rb.DT_BF16, 8, 1, 32, 8, 4, 131072, 128
+    a.scale, a.causal, a.q_gid0 = 0.088, 1, 8 * 131072 - 4
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dtype", rb.DT_FP32, 6), ("dtype", 7, 3), ("d", 96, 2), ("Hkv", 5, 2), ("nq", 0, 2),
+    ("nq", 65, 2), ("R", 0, 2), ("n", -1, 2), ("n", (1 << 23) + 1, 6), ("scale", 0.0, 1),
+    ("q", 0, 1), ("k", 4100, 4),
+])
+def test_decode_rejects(lib, field, value, status):
+    a = _decode(**{field: value})
+    st = lib.ra_decode_fwd(ctypes.byref(a), ctypes.c_void_p(4096), 1 << 40, None)
+    assert st == status, (st, rb.last_error())
+    assert lib.ra_decode_fwd_workspace_size(ctypes.byref(a)) == 0
+
+
+def test_decode_workspace(lib):
+    a = _decode()
+    need = lib.ra_decode_fwd_workspace_size(ctypes.byref(a))
+    rows = 1 * 32 * 4
+    assert need >= 8 * 8 * rows * (128 + 2) * 4  # at least one partial per wave of each rank
+    assert lib.ra_decode_fwd(ctypes.byref(a), ctypes.c_void_p(4096), need - 1, None) == 5
+    assert lib.ra_decode_fwd(ctypes.byref(a), ctypes.c_void_p(4096 + 16), need, None) == 5

@@ -111,13 +111,15 @@ def test_pack_v_layout_bit_exact(n, d):
     assert nbytes == B * H * d * n_pad * 2
     vp = torch.full((nbytes // 2,), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
     rb.ra_pack_v(v, vp)
-    got = vp.view(torch.int16).cpu().numpy().reshape(B, H, d, n_pad)
+    # tile-major: [B][H][n_pad/64][d][64], position q of tile T holds key 64T + perm16(q)
+    got = vp.view(torch.int16).cpu().numpy().reshape(B, H, n_pad // 64, d, 64)
     src = v.view(torch.int16).cpu().numpy()
-    expect = np.zeros((B, H, d, n_pad), np.int16)
-    for q in range(n_pad):
-        key = perm16(q)
-        if key < n:
-            expect[:, :, :, q] = src[:, :, key, :]
+    expect = np.zeros((B, H, n_pad // 64, d, 64), np.int16)
+    for T in range(n_pad // 64):
+        for q in range(64):
+            key = 64 * T + perm16(q)
+            if key < n:
+                expect[:, :, T, :, q] = src[:, :, key, :]
     assert np.array_equal(got, expect)
 
 
