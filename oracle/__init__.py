@@ -73,6 +73,10 @@ class Oracle:
         lib.ora_ring_emulate.restype = C
         lib.ora_pair_counts.argtypes = [C, I64, I32, P]
         lib.ora_pair_counts.restype = C
+        lib.ora_attention_bwd.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, D, C, P, P, P]
+        lib.ora_attention_bwd.restype = C
+        lib.ora_block_bwd.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, D, C, P, P,
+                                      P, P, P]
         self.lib = lib
         self.path = path
 
@@ -181,6 +185,42 @@ class Oracle:
         return W
 
 
+    def attention_bwd(self, q, k, v, dout, scale: float, causal: bool):
+        """Gradients of exact attention (original token order), float64:
+        q, dout [B][Hq][S][d]; k, v [B][Hkv][S][d] -> (dq, dk, dv)."""
+        q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+        B, Hq, S, d = q.shape
+        Hkv = k.shape[1]
+        dq = np.empty((B, Hq, S, d), np.float64)
+        dk = np.empty((B, Hkv, S, d), np.float64)
+        dv = np.empty((B, Hkv, S, d), np.float64)
+        rc = self.lib.ora_attention_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, Hq, Hkv, S, d,
+                                        float(scale), int(bool(causal)), _ptr(dq), _ptr(dk),
+                                        _ptr(dv))
+        if rc != 0:
+            raise MemoryError("attention_bwd")
+        return dq, dk, dv
+
+    def block_bwd(self, q, k, v, dout, lse, Dv, scale: float, causal: bool, qid, kid):
+        """One (query shard, key block) pair's gradient contributions, given the
+        global lse and D = <dO, O> per row: q, dout [B][Hq][nq][d]; k, v
+        [B][Hkv][nk][d]; lse, Dv [B][Hq][nq]; qid [nq], kid [nk] global tokens."""
+        q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+        lse = np.ascontiguousarray(lse, np.float64)
+        Dv = np.ascontiguousarray(Dv, np.float64)
+        qid = np.ascontiguousarray(qid, np.int64)
+        kid = np.ascontiguousarray(kid, np.int64)
+        B, Hq, nq, d = q.shape
+        _, Hkv, nk, _ = k.shape
+        dq = np.empty((B, Hq, nq, d), np.float64)
+        dk = np.empty((B, Hkv, nk, d), np.float64)
+        dv = np.empty((B, Hkv, nk, d), np.float64)
+        self.lib.ora_block_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(Dv), B, Hq,
+                               Hkv, nq, nk, d, float(scale), int(bool(causal)), _ptr(qid),
+                               _ptr(kid), _ptr(dq), _ptr(dk), _ptr(dv))
+        return dq, dk, dv
+
+
 def _f32(x):
     return np.ascontiguousarray(x, dtype=np.float32)
 
@@ -234,6 +274,14 @@ def attention_rows(*a, **kw):
 
 def attention_full(*a, **kw):
     return default().attention_full(*a, **kw)
+
+
+def attention_bwd(*a, **kw):
+    return default().attention_bwd(*a, **kw)
+
+
+def block_bwd(*a, **kw):
+    return default().block_bwd(*a, **kw)
 
 
 def block_partial(*a, **kw):

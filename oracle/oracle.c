@@ -386,6 +386,142 @@ done:
 }
 
 /*
+ * Gradients of exact attention: the backward pass that training over the ring
+ * needs (the pages' headline use is training on long contexts; they give no
+ * backward algorithm, so this is the derivative of the forward definition).
+ * For a loss with upstream gradient dO, per row (b, h, i) with allowed keys A:
+ *   p_j  = exp(s_j - lse),  lse = ln sum_{j in A} exp(s_j)
+ *   dP_j = <dO, v_j>,       D = sum_j p_j dP_j  (= <dO, O>)
+ *   dS_j = p_j (dP_j - D)
+ *   dq   = scale sum_j dS_j k_j
+ *   dk_j += scale dS_j q,   dv_j += p_j dO      (summed over the query heads
+ *                                                that read this K/V head)
+ * q, dout [B][Hq][S][d]; k, v [B][Hkv][S][d] (original token order);
+ * dq [B][Hq][S][d], dk, dv [B][Hkv][S][d] written (double).
+ * One thread per (b, K/V head): its dk/dv sums are accumulated in a fixed
+ * order.  Returns 0, or -1 on allocation failure.
+ */
+int ora_attention_bwd(const float *q, const float *k, const float *v,
+                      const float *dout, int64_t B, int64_t Hq, int64_t Hkv,
+                      int64_t S, int64_t d, double scale, int causal, double *dq,
+                      double *dk, double *dv) {
+  int64_t group = Hq / Hkv;
+  int fail = 0;
+  for (int64_t i = 0; i < B * Hkv * S * d; ++i) {
+    dk[i] = 0.0;
+    dv[i] = 0.0;
+  }
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : fail)
+  for (int64_t bg = 0; bg < B * Hkv; ++bg) {
+    int64_t b = bg / Hkv, g = bg % Hkv;
+    const float *kb = k + (b * Hkv + g) * S * d;
+    const float *vb = v + (b * Hkv + g) * S * d;
+    double *dkb = dk + (b * Hkv + g) * S * d;
+    double *dvb = dv + (b * Hkv + g) * S * d;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+    double *dp = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+    if (!s || !dp) {
+      free(s);
+      free(dp);
+      fail = 1;
+      continue;
+    }
+    for (int64_t h = g * group; h < (g + 1) * group; ++h) {
+      for (int64_t t = 0; t < S; ++t) {
+        const float *qi = q + ((b * Hq + h) * S + t) * d;
+        const float *gi = dout + ((b * Hq + h) * S + t) * d;
+        double *dqi = dq + ((b * Hq + h) * S + t) * d;
+        int64_t last = causal ? t : S - 1; /* allowed keys are 0..last */
+        double m = -INFINITY;
+        for (int64_t j = 0; j <= last; ++j) {
+          double acc = 0.0;
+          for (int64_t c = 0; c < d; ++c) acc += (double)qi[c] * (double)kb[j * d + c];
+          s[j] = acc * scale;
+          if (s[j] > m) m = s[j];
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j <= last; ++j) l += exp(s[j] - m);
+        double lse = m + log(l);
+        double D = 0.0;
+        for (int64_t j = 0; j <= last; ++j) {
+          double acc = 0.0;
+          for (int64_t c = 0; c < d; ++c) acc += (double)gi[c] * (double)vb[j * d + c];
+          dp[j] = acc;
+          D += exp(s[j] - lse) * acc;
+        }
+        for (int64_t c = 0; c < d; ++c) dqi[c] = 0.0;
+        for (int64_t j = 0; j <= last; ++j) {
+          double pj = exp(s[j] - lse);
+          double ds = pj * (dp[j] - D);
+          for (int64_t c = 0; c < d; ++c) {
+            dqi[c] += scale * ds * (double)kb[j * d + c];
+            dkb[j * d + c] += scale * ds * (double)qi[c];
+            dvb[j * d + c] += pj * (double)gi[c];
+          }
+        }
+      }
+    }
+    free(s);
+    free(dp);
+  }
+  return fail ? -1 : 0;
+}
+
+/*
+ * The same gradients restricted to one (query shard, key/value block) pair:
+ * the unit of work of one hop of the backward ring.  The softmax statistics
+ * are global (the forward's lse per query row and D = <dO, O>), so the
+ * contributions of the blocks simply add up to the full gradients.
+ *   q, dout [B][Hq][nq][d]; k, v [B][Hkv][nk][d]; lse, Dv [B][Hq][nq]
+ *   qid[i], kid[j]: global tokens; causal: key j allowed iff kid[j] <= qid[i]
+ *   dq [B][Hq][nq][d], dk, dv [B][Hkv][nk][d]: the block's contributions
+ *   (written, double).
+ */
+void ora_block_bwd(const float *q, const float *k, const float *v,
+                   const float *dout, const double *lse, const double *Dv,
+                   int64_t B, int64_t Hq, int64_t Hkv, int64_t nq, int64_t nk,
+                   int64_t d, double scale, int causal, const int64_t *qid,
+                   const int64_t *kid, double *dq, double *dk, double *dv) {
+  int64_t group = Hq / Hkv;
+  for (int64_t i = 0; i < B * Hkv * nk * d; ++i) {
+    dk[i] = 0.0;
+    dv[i] = 0.0;
+  }
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bg = 0; bg < B * Hkv; ++bg) {
+    int64_t b = bg / Hkv, g = bg % Hkv;
+    const float *kb = k + (b * Hkv + g) * nk * d;
+    const float *vb = v + (b * Hkv + g) * nk * d;
+    double *dkb = dk + (b * Hkv + g) * nk * d;
+    double *dvb = dv + (b * Hkv + g) * nk * d;
+    for (int64_t h = g * group; h < (g + 1) * group; ++h) {
+      for (int64_t i = 0; i < nq; ++i) {
+        int64_t row = (b * Hq + h) * nq + i;
+        const float *qi = q + row * d;
+        const float *gi = dout + row * d;
+        double *dqi = dq + row * d;
+        for (int64_t c = 0; c < d; ++c) dqi[c] = 0.0;
+        for (int64_t j = 0; j < nk; ++j) {
+          if (causal && kid[j] > qid[i]) continue;
+          double sj = 0.0, dpj = 0.0;
+          for (int64_t c = 0; c < d; ++c) {
+            sj += (double)qi[c] * (double)kb[j * d + c];
+            dpj += (double)gi[c] * (double)vb[j * d + c];
+          }
+          double pj = exp(sj * scale - lse[row]);
+          double ds = pj * (dpj - Dv[row]);
+          for (int64_t c = 0; c < d; ++c) {
+            dqi[c] += scale * ds * (double)kb[j * d + c];
+            dkb[j * d + c] += scale * ds * (double)qi[c];
+            dvb[j * d + c] += pj * (double)gi[c];
+          }
+        }
+      }
+    }
+  }
+}
+
+/*
  * Causal work per rank by brute force: W[r] = number of (query of rank r,
  * key) pairs with key token <= query token, over the whole sequence.
  * O(S^2): for the small sequences of the tests ([ZZ]: the interleaved

@@ -429,9 +429,100 @@ def check_gqa_equals_repeated_mha(orc):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+# --------------------------------------------------------------------------- backward
+def _brute_loss(q, k, v, g, scale, causal, group):
+    """sum over rows of <dO, O> with O from the pure-Python brute force (fp64)."""
+    B, Hq = len(q), len(q[0])
+    total = 0.0
+    for b in range(B):
+        for h in range(Hq):
+            o, _ = brute_head(q[b][h], k[b][h // group], v[b][h // group], scale, causal)
+            total += math.fsum(g[b][h][i][c] * o[i][c] for i in range(len(o))
+                               for c in range(len(o[0])))
+    return total
+
+
+def check_bwd_finite_differences(orc):
+    """The analytic gradients equal central finite differences of L = sum <dO, O>,
+    with O from the pure-Python brute force in fp64, for every element of q, k, v
+    (grouped heads, both masks)."""
+    rng = _rng(31)
+    B, Hq, Hkv, S, d = 1, 2, 1, 5, 3
+    group = Hq // Hkv
+    q = rng.standard_normal((B, Hq, S, d)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, S, d)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, S, d)).astype(np.float32)
+    g = rng.standard_normal((B, Hq, S, d)).astype(np.float32)
+    scale = 0.7
+    eps = 1e-5
+    for causal in (True, False):
+        dq, dk, dv = orc.attention_bwd(q, k, v, g, scale, causal)
+        base = [x.astype(np.float64).tolist() for x in (q, k, v)]
+        gl = g.astype(np.float64).tolist()
+        for which, grad in ((0, dq), (1, dk), (2, dv)):
+            shape = grad.shape
+            for idx in np.ndindex(*shape):
+                vals = []
+                for sgn in (1.0, -1.0):
+                    t = [copy_nested(x) for x in base]
+                    b_, h_, i_, c_ = idx
+                    t[which][b_][h_][i_][c_] += sgn * eps
+                    vals.append(_brute_loss(t[0], t[1], t[2], gl, scale, causal, group))
+                fd = (vals[0] - vals[1]) / (2 * eps)
+                assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (which, idx, fd, grad[idx])
+
+
+def copy_nested(x):
+    return [copy_nested(y) for y in x] if isinstance(x, list) else x
+
+
+def check_bwd_block_partition(orc):
+    """Block contributions with the global lse and D = <dO, O> add up to the full
+    gradients, for a partition of the keys and of the queries into uneven blocks."""
+    rng = _rng(32)
+    B, Hq, Hkv, S, d = 1, 4, 2, 23, 6
+    q = rng.standard_normal((B, Hq, S, d)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, S, d)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, S, d)).astype(np.float32)
+    g = rng.standard_normal((B, Hq, S, d)).astype(np.float32)
+    scale = 0.45
+    for causal in (True, False):
+        dq, dk, dv = orc.attention_bwd(q, k, v, g, scale, causal)
+        o, lse = orc.attention_full(q, k, v, scale, causal)
+        Dv = (g.astype(np.float64) * o).sum(-1)
+        aq, ak, av = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
+        qcuts, kcuts = [0, 9, 10, 23], [0, 4, 17, 23]
+        for q0, q1 in zip(qcuts[:-1], qcuts[1:]):
+            for k0, k1 in zip(kcuts[:-1], kcuts[1:]):
+                bq, bk, bv = orc.block_bwd(q[:, :, q0:q1], k[:, :, k0:k1], v[:, :, k0:k1],
+                                           g[:, :, q0:q1], lse[:, :, q0:q1], Dv[:, :, q0:q1],
+                                           scale, causal, np.arange(q0, q1), np.arange(k0, k1))
+                aq[:, :, q0:q1] += bq
+                ak[:, :, k0:k1] += bk
+                av[:, :, k0:k1] += bv
+        _close(aq, dq, 1e-11, 1e-12, "partition dq")
+        _close(ak, dk, 1e-11, 1e-12, "partition dk")
+        _close(av, dv, 1e-11, 1e-12, "partition dv")
+
+
+def check_bwd_constant_values(orc):
+    """All value rows equal: O no longer depends on q or k, so dq = dk = 0, and
+    the value gradients of a query row sum to its dO (probabilities sum to 1)."""
+    rng = _rng(33)
+    B, Hq, Hkv, S, d = 1, 2, 2, 9, 4
+    q = rng.standard_normal((B, Hq, S, d)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, S, d)).astype(np.float32)
+    v = np.broadcast_to(rng.standard_normal(d).astype(np.float32), (B, Hkv, S, d)).copy()
+    g = rng.standard_normal((B, Hq, S, d)).astype(np.float32)
+    dq, dk, dv = orc.attention_bwd(q, k, v, g, 0.8, True)
+    assert np.abs(dq).max() < 1e-12 and np.abs(dk).max() < 1e-12
+    _close(dv.sum(axis=2), g.astype(np.float64).sum(axis=2), 1e-12, 1e-12, "dv sums")
+
+
 ALL_CHECKS = [
     check_layout_golden, check_layout_bijection, check_zigzag_layout, check_brute_force, check_block_partial_brute,
     check_identical_keys, check_dominant_logit, check_constant_values, check_key_shift,
     check_library_sdpa, check_ring_equals_full, check_layout_independence, check_merge_algebra,
     check_pair_counts, check_coverage, check_gqa_equals_repeated_mha,
+    check_bwd_finite_differences, check_bwd_block_partition, check_bwd_constant_values,
 ]

@@ -34,6 +34,15 @@ MUTANTS = [
      "o[c] += p * (double)kb[j * d + c];", 1),
     ("max never updated", "      if (s > m) m = s;\n", "", 1),
     ("merge forgets the normaliser", "double l = wa + wb;", "double l = wa + wb + 1.0;", 1),
+    ("backward drops D", "double ds = pj * (dp[j] - D);", "double ds = pj * dp[j];", 1),
+    ("backward dk unscaled", "dkb[j * d + c] += scale * ds * (double)qi[c];",
+     "dkb[j * d + c] += ds * (double)qi[c];", 0),
+    ("backward dv from dS", "dvb[j * d + c] += pj * (double)gi[c];",
+     "dvb[j * d + c] += ds * (double)gi[c];", 0),
+    ("block backward mask off by one", "if (causal && kid[j] > qid[i]) continue;",
+     "if (causal && kid[j] >= qid[i]) continue;", 1),
+    ("block backward uses row max for lse", "double pj = exp(sj * scale - lse[row]);",
+     "double pj = exp(sj * scale - lse[row] + 0.1);", 1),
 ]
 
 
