@@ -198,6 +198,43 @@ def overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse, t_c
             "overlap": round(1.0 - (t_copy_ms - t_swap) / t_copies, 3) if t_copies > 0 else None}
 
 
+def backward_bench(torch, ra, w, layout_code, q, k, v, iters=2):
+    """ra_ring_bwd after the forward ring (same shards): MFMA roofline with the
+    algorithmic count of the backward, 10*d FLOP per allowed pair per query head
+    (S = QK^T, dP = dO V^T, dV, dK, dQ; recomputing S and dP for dQ is not credited)."""
+    tdt = q.dtype
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed + 7)
+    dout = torch.randn(q.shape, device="cuda", generator=g).to(tdt)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ra.backward(dout, dq, dk, dv)  # warm-up, allocates the workspace
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(iters):
+        rb_ring_bwd(ra)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(iters)])
+    pairs = sum(hop_pairs(w, layout_code))
+    flops = 10.0 * w.d * w.B * w.Hq * pairs
+    med = float(np.median(ms))
+    tf = flops / (med * 1e-3) / 1e12
+    del dout, dq, dk, dv
+    return {"ms_median": round(med, 3), "ms_min": round(float(ms.min()), 3),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "algorithmic_flops": flops,
+                         "kernels": "bwd_dkdv_kernel + bwd_dq_kernel (+ packing, D, casts)"}}
+
+
+def rb_ring_bwd(ra):
+    from long_context_exact_block_amd import binding as rb
+    rb.ra_ring_bwd(ra.bargs, ra.bworkspace)
+
+
 def decode_bench(torch, rb, w, iters=20):
     """ra_decode_fwd on the long-context decode step (w: DecodeWorkload): nq new
     tokens against the whole KV cache, split contiguously over R ranks.  HBM
@@ -295,6 +332,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge-bench", action="store_true")
+    ap.add_argument("--no-bwd-bench", action="store_true",
+                    help="skip the backward-ring measurement (ra_ring_bwd)")
     ap.add_argument("--no-decode-bench", action="store_true",
                     help="skip the long-context decode measurement (ra_decode_fwd)")
     ap.add_argument("--no-overlap-bench", action="store_true",
@@ -388,6 +427,10 @@ def main():
         handoff = overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse,
                                 float(np.median(step_ms)))
     merge = None if args.no_merge_bench else merge_bench(torch, rb)
+    backward = None
+    if not args.no_bwd_bench and w.dtype != "fp32":
+        log("backward")
+        backward = backward_bench(torch, ra, w, lcode, q, k, v)
     decode = None if args.no_decode_bench else decode_bench(torch, rb, configs.DECODE_1M)
     imbalance = {}
     for name, code in (("contiguous", 0), ("striped", 1), ("zigzag", 2)):
@@ -447,6 +490,7 @@ def main():
         "hop_ms": [round(float(x), 3) for x in hop_ms.mean(axis=0)],
         "handoff": handoff,
         "merge": merge,
+        "backward": backward,
         "decode": decode,
         "causal_imbalance_max_over_mean": imbalance,
         "cpu_baseline": cpu,

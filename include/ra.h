@@ -267,6 +267,77 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
                       ra_stream compute, ra_stream copy);
 
 /*
+ * ra_block_bwd -- gradient contributions of one query shard x one K/V block:
+ * the unit of work of one hop of the backward ring (training is the pages'
+ * headline use; they give no backward algorithm, so this is the derivative
+ * of the forward: p = exp(s - lse), dP = dO v, D = <dO, O>, dS = p(dP - D),
+ * dQ += scale dS k, dK += scale dS^T q, dV += p^T dO).  lse and O are the
+ * forward's outputs over the WHOLE sequence (not this block's partial), so
+ * the contributions of all blocks add up to the full gradients.
+ *   q, o, dout  device [B][Hq][n_q][d] in dtype, contiguous
+ *   k, v        device [B][Hkv][n_k][d] in dtype, contiguous
+ *   lse         device fp32 [B][Hq][n_q] (natural log, as ra_finalize writes)
+ *   ids, scale, causal as in ra_block_args
+ *   dq          device fp32 [B][Hq][n_q][d]; dk, dv device fp32 [B][Hkv][n_k][d]:
+ *               the call ADDS this pair's contributions (dk, dv summed over
+ *               the query heads of a K/V head)
+ * 16-bit dtypes, d in {64, 128}.  The workspace (ra_block_bwd_workspace_size
+ * bytes, 256-byte aligned) holds transposed copies of q, dout, k and D.
+ * Deterministic (no atomics).  Asynchronous on `stream`.
+ * Errors: RA_ERR_INVALID_ARG, RA_ERR_SHAPE, RA_ERR_DTYPE, RA_ERR_ALIGNMENT,
+ * RA_ERR_WORKSPACE, RA_ERR_UNSUPPORTED, RA_ERR_HIP.
+ */
+typedef struct {
+  const void *q, *k, *v, *o, *dout;
+  int32_t dtype;
+  int32_t B, Hq, Hkv, n_q, n_k, d;
+  float scale;
+  int32_t causal;
+  int64_t q_gid0, q_gid_step, k_gid0, k_gid_step;
+  const float *lse;
+  float *dq, *dk, *dv;
+} ra_block_bwd_args;
+
+size_t ra_block_bwd_workspace_size(const ra_block_bwd_args *a);
+ra_status ra_block_bwd(const ra_block_bwd_args *a, void *workspace, size_t workspace_bytes,
+                       ra_stream stream);
+
+/*
+ * ra_ring_bwd -- the backward pass over the whole ring on one GPU: every
+ * computed query rank r meets the block of source rank s = (r - h) mod R at
+ * hop h (as in ra_ring_fwd) and adds that pair's gradient contributions; dQ
+ * stays with its rank, dK/dV belong to the block (on several GPUs they
+ * travel with K and V and arrive home after R hops; here the blocks are read
+ * in place and their gradients accumulated in place).
+ *   q_sh, k_sh, v_sh, R, rank0, n_ranks, B, Hq, Hkv, n, d, scale, causal,
+ *   layout: as in ra_ring_args (16-bit dtypes only)
+ *   o_sh, dout_sh  device [n_ranks][B][Hq][n][d]: the forward's O and the
+ *                  upstream gradient of the computed ranks
+ *   lse            device fp32 [n_ranks][B][Hq][n]: the forward's LSE
+ *   dq_sh          device [n_ranks][B][Hq][n][d] in dtype (written)
+ *   dk_sh, dv_sh   device [R][B][Hkv][n][d] in dtype (written): gradients of
+ *                  every source block from the computed query ranks
+ * Workspace: ra_ring_bwd_workspace_size bytes, 256-byte aligned (transposed
+ * copies of Q, dO, K, D and fp32 accumulators).  Asynchronous on `stream`.
+ * Errors: as ra_ring_fwd, plus RA_ERR_UNSUPPORTED for fp32.
+ */
+typedef struct {
+  const void *q_sh, *k_sh, *v_sh, *o_sh, *dout_sh;
+  const float *lse;
+  int32_t dtype;
+  int32_t R, rank0, n_ranks;
+  int32_t B, Hq, Hkv, n, d;
+  float scale;
+  int32_t causal;
+  int32_t layout;
+  void *dq_sh, *dk_sh, *dv_sh;
+} ra_ring_bwd_args;
+
+size_t ra_ring_bwd_workspace_size(const ra_ring_bwd_args *a);
+ra_status ra_ring_bwd(const ra_ring_bwd_args *a, void *workspace, size_t workspace_bytes,
+                      ra_stream stream);
+
+/*
  * ra_decode_fwd -- nq new query tokens against a KV cache split over R ranks:
  * rank r holds the contiguous run of tokens r*n .. r*n + n - 1 ([DE]
  * "Tiefer Einblick": contiguous split; "Reale Umsetzung": serving long

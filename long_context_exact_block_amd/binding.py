@@ -26,7 +26,9 @@ LAYOUTS = {"contiguous": LAYOUT_CONTIGUOUS, "striped": LAYOUT_STRIPED, "zigzag":
 EXPORTED = ("ra_version", "ra_status_string", "ra_last_error", "ra_layout_permute",
             "ra_layout_gather", "ra_layout_scatter", "ra_block_fwd", "ra_packed_v_bytes",
             "ra_pack_v", "ra_merge", "ra_finalize", "ra_ring_fwd_workspace_size", "ra_ring_fwd",
-            "ra_causal_work", "ra_decode_fwd_workspace_size", "ra_decode_fwd")
+            "ra_causal_work", "ra_decode_fwd_workspace_size", "ra_decode_fwd",
+            "ra_block_bwd_workspace_size", "ra_block_bwd", "ra_ring_bwd_workspace_size",
+            "ra_ring_bwd")
 
 
 class RAError(RuntimeError):
@@ -64,6 +66,20 @@ class DecodeArgs(ctypes.Structure):
                 ("scale", ctypes.c_float), ("causal", I32), ("q_gid0", I64), ("o", P), ("lse", P)]
 
 
+class BlockBwdArgs(ctypes.Structure):
+    _fields_ = [("q", P), ("k", P), ("v", P), ("o", P), ("dout", P), ("dtype", I32), ("B", I32),
+                ("Hq", I32), ("Hkv", I32), ("n_q", I32), ("n_k", I32), ("d", I32),
+                ("scale", ctypes.c_float), ("causal", I32), ("q_gid0", I64), ("q_gid_step", I64),
+                ("k_gid0", I64), ("k_gid_step", I64), ("lse", P), ("dq", P), ("dk", P), ("dv", P)]
+
+
+class RingBwdArgs(ctypes.Structure):
+    _fields_ = [("q_sh", P), ("k_sh", P), ("v_sh", P), ("o_sh", P), ("dout_sh", P), ("lse", P),
+                ("dtype", I32), ("R", I32), ("rank0", I32), ("n_ranks", I32), ("B", I32),
+                ("Hq", I32), ("Hkv", I32), ("n", I32), ("d", I32), ("scale", ctypes.c_float),
+                ("causal", I32), ("layout", I32), ("dq_sh", P), ("dk_sh", P), ("dv_sh", P)]
+
+
 _lib = None
 
 
@@ -84,6 +100,12 @@ def lib():
     L.ra_layout_gather.argtypes = [P, P, P, I32, I64, I64, I64, I64, I32, I32, I32, P]
     L.ra_layout_scatter.argtypes = [P, P, P, I32, I64, I64, I64, I64, I32, I32, I32, P]
     L.ra_block_fwd.argtypes = [ctypes.POINTER(BlockArgs), P]
+    L.ra_block_bwd_workspace_size.argtypes = [ctypes.POINTER(BlockBwdArgs)]
+    L.ra_block_bwd_workspace_size.restype = ctypes.c_size_t
+    L.ra_block_bwd.argtypes = [ctypes.POINTER(BlockBwdArgs), P, ctypes.c_size_t, P]
+    L.ra_ring_bwd_workspace_size.argtypes = [ctypes.POINTER(RingBwdArgs)]
+    L.ra_ring_bwd_workspace_size.restype = ctypes.c_size_t
+    L.ra_ring_bwd.argtypes = [ctypes.POINTER(RingBwdArgs), P, ctypes.c_size_t, P]
     L.ra_decode_fwd_workspace_size.argtypes = [ctypes.POINTER(DecodeArgs)]
     L.ra_decode_fwd_workspace_size.restype = ctypes.c_size_t
     L.ra_decode_fwd.argtypes = [ctypes.POINTER(DecodeArgs), P, ctypes.c_size_t, P]
@@ -250,6 +272,66 @@ def ra_ring_fwd(args: RingArgs, workspace, compute_stream=None, copy_stream=None
     cs = _stream(compute_stream)
     xs = _stream(copy_stream) if copy_stream is not None else cs
     _check(lib().ra_ring_fwd(ctypes.byref(args), ws_ptr, ws_bytes, cs, xs))
+
+
+def block_bwd_args(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, q_gid0=0, q_step=1,
+                   k_gid0=0, k_step=1) -> BlockBwdArgs:
+    """q, o, dout [B][Hq][nq][d]; k, v [B][Hkv][nk][d] (16-bit, contiguous); lse fp32
+    [B][Hq][nq]; dq, dk, dv fp32 accumulators shaped like q, k, v."""
+    B, Hq, nq, d = q.shape
+    _, Hkv, nk, _ = k.shape
+    a = BlockBwdArgs()
+    a.q, a.k, a.v, a.o, a.dout = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout)
+    a.dtype = dtype_code(q)
+    a.B, a.Hq, a.Hkv, a.n_q, a.n_k, a.d = B, Hq, Hkv, nq, nk, d
+    a.scale, a.causal = float(scale), int(bool(causal))
+    a.q_gid0, a.q_gid_step, a.k_gid0, a.k_gid_step = int(q_gid0), int(q_step), int(k_gid0), int(k_step)
+    a.lse, a.dq, a.dk, a.dv = _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv)
+    return a
+
+
+def ra_block_bwd_workspace_size(args: BlockBwdArgs) -> int:
+    nb = lib().ra_block_bwd_workspace_size(ctypes.byref(args))
+    if nb == 0 and args.n_q > 0:
+        raise RAError(1, last_error())
+    return nb
+
+
+def ra_block_bwd(args: BlockBwdArgs, workspace, stream=None):
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().ra_block_bwd(ctypes.byref(args), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def ring_bwd_args(q_sh, k_sh, v_sh, o_sh, dout_sh, lse, dq_sh, dk_sh, dv_sh, R, rank0, n_ranks,
+                  scale, causal, layout) -> RingBwdArgs:
+    """Shards as for ra_ring_fwd: q_sh, o_sh, dout_sh, dq_sh [n_ranks][B][Hq][n][d];
+    k_sh, v_sh, dk_sh, dv_sh [R][B][Hkv][n][d]; lse fp32 [n_ranks][B][Hq][n]."""
+    _, B, Hq, n, d = q_sh.shape
+    Hkv = k_sh.shape[2]
+    a = RingBwdArgs()
+    a.q_sh, a.k_sh, a.v_sh, a.o_sh, a.dout_sh = (_ptr(x) for x in (q_sh, k_sh, v_sh, o_sh, dout_sh))
+    a.lse = _ptr(lse)
+    a.dtype = dtype_code(q_sh)
+    a.R, a.rank0, a.n_ranks = R, rank0, n_ranks
+    a.B, a.Hq, a.Hkv, a.n, a.d = B, Hq, Hkv, n, d
+    a.scale, a.causal = float(scale), int(bool(causal))
+    a.layout = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    a.dq_sh, a.dk_sh, a.dv_sh = _ptr(dq_sh), _ptr(dk_sh), _ptr(dv_sh)
+    return a
+
+
+def ra_ring_bwd_workspace_size(args: RingBwdArgs) -> int:
+    nb = lib().ra_ring_bwd_workspace_size(ctypes.byref(args))
+    if nb == 0 and args.n > 0:
+        raise RAError(1, last_error())
+    return nb
+
+
+def ra_ring_bwd(args: RingBwdArgs, workspace, stream=None):
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().ra_ring_bwd(ctypes.byref(args), ws_ptr, ws_bytes, _stream(stream)))
 
 
 def decode_args(q, k, vp, o, lse, scale, causal, q_gid0) -> DecodeArgs:

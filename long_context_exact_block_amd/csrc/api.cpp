@@ -145,6 +145,111 @@ int64_t layout_gid(int32_t layout, int32_t R, int64_t n, int32_t rank, int64_t j
   return j < c ? (int64_t)rank * c + j : (2 * (int64_t)R - 1 - rank) * c + (j - c);
 }
 
+ra_status check_block_bwd(const ra_block_bwd_args *a) {
+  if (!a) return fail(RA_ERR_INVALID_ARG, "args is NULL");
+  if (a->dtype != RA_DT_BF16 && a->dtype != RA_DT_FP16) {
+    if (a->dtype == RA_DT_FP32) return fail(RA_ERR_UNSUPPORTED, "backward is for 16-bit inputs");
+    return fail(RA_ERR_DTYPE, "unknown dtype %d", a->dtype);
+  }
+  if (a->B < 1 || a->Hq < 1 || a->Hkv < 1) return fail(RA_ERR_SHAPE, "B, Hq, Hkv must be >= 1");
+  if (a->Hq % a->Hkv) return fail(RA_ERR_SHAPE, "Hq %% Hkv != 0 (%d, %d)", a->Hq, a->Hkv);
+  if (a->d != 64 && a->d != 128) return fail(RA_ERR_SHAPE, "d must be 64 or 128 (got %d)", a->d);
+  if (a->n_q < 0 || a->n_k < 0) return fail(RA_ERR_SHAPE, "n_q, n_k must be >= 0");
+  if (a->n_q > kMaxPackedKeys || a->n_k > kMaxPackedKeys)
+    return fail(RA_ERR_UNSUPPORTED, "n_q, n_k are limited to %lld", (long long)kMaxPackedKeys);
+  if (a->q_gid_step < 1 || a->k_gid_step < 1)
+    return fail(RA_ERR_INVALID_ARG, "global-id steps must be >= 1");
+  if (!(a->scale > 0.f) || !std::isfinite(a->scale))
+    return fail(RA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (a->n_q == 0) return RA_OK;
+  if (!a->q || !a->o || !a->dout || !a->lse || !a->dq || (a->n_k > 0 && (!a->k || !a->v ||
+                                                                        !a->dk || !a->dv)))
+    return fail(RA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned16(a->q) || !aligned16(a->o) || !aligned16(a->dout) || !aligned16(a->dq) ||
+      (a->n_k > 0 && (!aligned16(a->k) || !aligned16(a->v) || !aligned16(a->dk) ||
+                      !aligned16(a->dv))))
+    return fail(RA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  return RA_OK;
+}
+
+struct BwdWs {
+  size_t qT, doT, kT, dv, total;
+};
+BwdWs block_bwd_ws(const ra_block_bwd_args *a) {
+  BwdWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  const size_t qbytes = (size_t)a->B * a->Hq * a->d * packed_n(a->n_q) * 2;
+  w.qT = take(qbytes);
+  w.doT = take(qbytes);
+  w.kT = take((size_t)a->B * a->Hkv * a->d * packed_n(a->n_k) * 2);
+  w.dv = take((size_t)a->B * a->Hq * a->n_q * 4);
+  w.total = off;
+  return w;
+}
+
+ra_status check_ring_bwd(const ra_ring_bwd_args *a) {
+  if (!a) return fail(RA_ERR_INVALID_ARG, "args is NULL");
+  if (a->dtype != RA_DT_BF16 && a->dtype != RA_DT_FP16) {
+    if (a->dtype == RA_DT_FP32) return fail(RA_ERR_UNSUPPORTED, "backward is for 16-bit inputs");
+    return fail(RA_ERR_DTYPE, "unknown dtype %d", a->dtype);
+  }
+  if (!known_layout(a->layout)) return fail(RA_ERR_INVALID_ARG, "unknown layout %d", a->layout);
+  if (a->R < 1) return fail(RA_ERR_SHAPE, "R must be >= 1 (got %d)", a->R);
+  if (a->n_ranks < 1 || a->n_ranks > a->R || a->rank0 < 0 || a->rank0 + a->n_ranks > a->R)
+    return fail(RA_ERR_SHAPE, "ranks [rank0, rank0+n_ranks) must lie in [0, R)");
+  if (a->B < 1 || a->Hq < 1 || a->Hkv < 1) return fail(RA_ERR_SHAPE, "B, Hq, Hkv must be >= 1");
+  if (a->Hq % a->Hkv) return fail(RA_ERR_SHAPE, "Hq %% Hkv != 0 (%d, %d)", a->Hq, a->Hkv);
+  if (a->d != 64 && a->d != 128) return fail(RA_ERR_SHAPE, "d must be 64 or 128 (got %d)", a->d);
+  if (a->n < 0) return fail(RA_ERR_SHAPE, "n must be >= 0");
+  if (a->layout == RA_LAYOUT_ZIGZAG && a->n % 2)
+    return fail(RA_ERR_SHAPE, "zig-zag blocks hold two equal chunks: n must be even");
+  if (a->n > kMaxPackedKeys)
+    return fail(RA_ERR_UNSUPPORTED, "blocks are limited to %lld tokens", (long long)kMaxPackedKeys);
+  if ((int64_t)a->n * a->R > kMaxI32) return fail(RA_ERR_SHAPE, "S = n*R must be < 2^31");
+  if (!(a->scale > 0.f) || !std::isfinite(a->scale))
+    return fail(RA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (a->n > 0) {
+    if (!a->q_sh || !a->k_sh || !a->v_sh || !a->o_sh || !a->dout_sh || !a->lse || !a->dq_sh ||
+        !a->dk_sh || !a->dv_sh)
+      return fail(RA_ERR_INVALID_ARG, "null tensor pointer");
+    const void *ptrs[] = {a->q_sh, a->k_sh, a->v_sh, a->o_sh, a->dout_sh, a->dq_sh, a->dk_sh,
+                          a->dv_sh};
+    for (const void *x : ptrs)
+      if (!aligned16(x)) return fail(RA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  }
+  return RA_OK;
+}
+
+struct RingBwdWs {
+  size_t qT, doT, kT, D, dq, dk, dv, total;
+};
+RingBwdWs ring_bwd_ws(const ra_ring_bwd_args *a) {
+  RingBwdWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  const size_t np = (size_t)packed_n(a->n);
+  const size_t qrows = (size_t)a->n_ranks * a->B * a->Hq;
+  const size_t kblocks = (size_t)a->R * a->B * a->Hkv;
+  w.qT = take(qrows * a->d * np * 2);
+  w.doT = take(qrows * a->d * np * 2);
+  w.kT = take(kblocks * a->d * np * 2);
+  w.D = take(qrows * a->n * 4);
+  w.dq = take(qrows * a->n * a->d * 4);
+  w.dk = take(kblocks * a->n * a->d * 4);
+  w.dv = take(kblocks * a->n * a->d * 4);
+  w.total = off;
+  return w;
+}
+
 ra_status check_decode(const ra_decode_args *a) {
   if (!a) return fail(RA_ERR_INVALID_ARG, "args is NULL");
   if (a->dtype != RA_DT_BF16 && a->dtype != RA_DT_FP16) {
@@ -677,6 +782,173 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
   }
   RA_HIP(launch_finalize(o_acc, m_acc, l_acc, a->o, a->lse, a->dtype, rows, a->d, cs),
          "finalize kernel");
+  return RA_OK;
+}
+
+size_t ra_block_bwd_workspace_size(const ra_block_bwd_args *a) {
+  clear_error();
+  if (check_block_bwd(a) != RA_OK) return 0;
+  return block_bwd_ws(a).total;
+}
+
+ra_status ra_block_bwd(const ra_block_bwd_args *a, void *workspace, size_t workspace_bytes,
+                       ra_stream stream) {
+  clear_error();
+  ra_status st = check_block_bwd(a);
+  if (st != RA_OK) return st;
+  if (a->n_q == 0) return RA_OK;
+  const BwdWs L = block_bwd_ws(a);
+  if (!workspace || workspace_bytes < L.total || (uintptr_t)workspace % 256)
+    return fail(RA_ERR_WORKSPACE, "workspace must be >= %zu bytes, 256-byte aligned", L.total);
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  const int64_t d = a->d;
+  const int64_t qs[3] = {(int64_t)a->Hq * a->n_q * d, (int64_t)a->n_q * d, d};
+  const int64_t ks[3] = {(int64_t)a->Hkv * a->n_k * d, (int64_t)a->n_k * d, d};
+  RA_HIP(launch_bwd_prep(a->o, a->dout, (float *)(ws + L.dv), a->dtype,
+                         (int64_t)a->B * a->Hq * a->n_q, a->d, s), "bwd prep");
+  RA_HIP(launch_pack_v(a->q, ws + L.qT, 2, (int64_t)a->B * a->Hq, a->Hq, a->n_q, d, qs[0], qs[1],
+                       qs[2], s), "pack q");
+  RA_HIP(launch_pack_v(a->dout, ws + L.doT, 2, (int64_t)a->B * a->Hq, a->Hq, a->n_q, d, qs[0],
+                       qs[1], qs[2], s), "pack dout");
+  if (a->n_k > 0)
+    RA_HIP(launch_pack_v(a->k, ws + L.kT, 2, (int64_t)a->B * a->Hkv, a->Hkv, a->n_k, d, ks[0],
+                         ks[1], ks[2], s), "pack k");
+  BwdParams P{};
+  BatchParams &p = P.a;
+  p.q = a->q;
+  p.k = a->n_k > 0 ? a->k : a->q;
+  p.v = a->n_k > 0 ? a->v : a->q;
+  p.kv_idx0 = 0;
+  p.kv_idx_mod = 1;
+  p.qs_b = qs[0];
+  p.qs_h = qs[1];
+  p.qs_t = qs[2];
+  p.ks_b = p.vs_b = ks[0];
+  p.ks_h = p.vs_h = ks[1];
+  p.ks_t = p.vs_t = ks[2];
+  p.B = a->B;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.nq = a->n_q;
+  p.nk = a->n_k;
+  p.d = a->d;
+  p.nz = 1;
+  p.scale = a->scale;
+  p.causal = a->causal ? 1 : 0;
+  p.qg_add = a->q_gid0;
+  p.q_step = a->q_gid_step;
+  p.kg_add = a->k_gid0;
+  p.k_step = a->k_gid_step;
+  p.kg_smod = 1;
+  P.dout = a->dout;
+  P.qT = ws + L.qT;
+  P.doT = ws + L.doT;
+  P.kT = ws + L.kT;
+  P.lse = a->lse;
+  P.Dv = (const float *)(ws + L.dv);
+  P.dq = a->dq;
+  P.dk = a->dk;
+  P.dv = a->dv;
+  RA_HIP(launch_bwd(P, a->dtype, s), "backward kernels");
+  return RA_OK;
+}
+
+size_t ra_ring_bwd_workspace_size(const ra_ring_bwd_args *a) {
+  clear_error();
+  if (check_ring_bwd(a) != RA_OK) return 0;
+  return ring_bwd_ws(a).total;
+}
+
+ra_status ra_ring_bwd(const ra_ring_bwd_args *a, void *workspace, size_t workspace_bytes,
+                      ra_stream stream) {
+  clear_error();
+  ra_status st = check_ring_bwd(a);
+  if (st != RA_OK) return st;
+  if (a->n == 0) return RA_OK;
+  const RingBwdWs L = ring_bwd_ws(a);
+  if (!workspace || workspace_bytes < L.total || (uintptr_t)workspace % 256)
+    return fail(RA_ERR_WORKSPACE, "workspace must be >= %zu bytes, 256-byte aligned", L.total);
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  const int R = a->R, n = a->n, nr = a->n_ranks, r0 = a->rank0;
+  const int64_t d = a->d;
+  const bool contig = a->layout == RA_LAYOUT_CONTIGUOUS;
+  const int64_t qz = (int64_t)a->B * a->Hq * n * d;   // elements of one query shard
+  const int64_t kz = (int64_t)a->B * a->Hkv * n * d;  // elements of one K/V block
+  const int64_t n_pad = packed_n(n);
+  float *dq = (float *)(ws + L.dq), *dk = (float *)(ws + L.dk), *dv = (float *)(ws + L.dv);
+  RA_HIP(launch_zero(dq, nr * qz, s), "zero dq");
+  RA_HIP(launch_zero(dk, R * kz, s), "zero dk");
+  RA_HIP(launch_zero(dv, R * kz, s), "zero dv");
+  RA_HIP(launch_bwd_prep(a->o_sh, a->dout_sh, (float *)(ws + L.D), a->dtype,
+                         (int64_t)nr * a->B * a->Hq * n, a->d, s), "bwd prep");
+  RA_HIP(launch_pack_v(a->q_sh, ws + L.qT, 2, (int64_t)nr * a->B * a->Hq, a->Hq, n, d,
+                       (int64_t)a->Hq * n * d, (int64_t)n * d, d, s), "pack q");
+  RA_HIP(launch_pack_v(a->dout_sh, ws + L.doT, 2, (int64_t)nr * a->B * a->Hq, a->Hq, n, d,
+                       (int64_t)a->Hq * n * d, (int64_t)n * d, d, s), "pack dout");
+  RA_HIP(launch_pack_v(a->k_sh, ws + L.kT, 2, (int64_t)R * a->B * a->Hkv, a->Hkv, n, d,
+                       (int64_t)a->Hkv * n * d, (int64_t)n * d, d, s), "pack k");
+  BwdParams P{};
+  BatchParams &p = P.a;
+  p.q = a->q_sh;
+  p.k = a->k_sh;
+  p.v = a->v_sh;
+  p.q_zstride = qz;
+  p.kv_zstride = kz;
+  p.kv_vzstride = kz;
+  p.qs_b = (int64_t)a->Hq * n * d;
+  p.qs_h = (int64_t)n * d;
+  p.qs_t = d;
+  p.ks_b = p.vs_b = (int64_t)a->Hkv * n * d;
+  p.ks_h = p.vs_h = (int64_t)n * d;
+  p.ks_t = p.vs_t = d;
+  p.B = a->B;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.nq = n;
+  p.nk = n;
+  p.d = a->d;
+  p.nz = nr;
+  p.scale = a->scale;
+  p.causal = a->causal ? 1 : 0;
+  p.qg_add = contig ? (int64_t)r0 * n : r0;
+  p.qg_z = contig ? n : 1;
+  p.q_step = contig ? 1 : R;
+  p.kg_add = 0;
+  p.kg_mult = contig ? n : 1;
+  p.k_step = contig ? 1 : R;
+  p.kg_smod = R;
+  p.kv_idx_mod = R;
+  if (a->layout == RA_LAYOUT_ZIGZAG) {
+    p.zz_c = n / 2;
+    p.zz_R = R;
+    p.q_rank0 = r0;
+  }
+  p.ml_zstride = (int64_t)a->B * a->Hq * n;
+  P.dout = a->dout_sh;
+  P.qT = ws + L.qT;
+  P.doT = ws + L.doT;
+  P.kT = ws + L.kT;
+  P.qT_zstride = (int64_t)a->B * a->Hq * d * n_pad;
+  P.kT_zstride = (int64_t)a->B * a->Hkv * d * n_pad;
+  P.lse = a->lse;
+  P.Dv = (const float *)(ws + L.D);
+  P.dq = dq;
+  P.dk = dk;
+  P.dv = dv;
+  P.dq_zstride = qz;
+  P.dk_zstride = kz;
+  for (int h = 0; h < R; ++h) {
+    // hop h: computed rank r0 + z meets the block of source (r0 + z - h) mod R;
+    // within a hop every rank reads (and accumulates into) a different block
+    p.kg_s0 = ((r0 - h) % R + R) % R;
+    p.kv_idx0 = p.kg_s0;
+    RA_HIP(launch_bwd(P, a->dtype, s), "backward kernels");
+  }
+  RA_HIP(launch_cast(dq, a->dq_sh, a->dtype, nr * qz, s), "cast dq");
+  RA_HIP(launch_cast(dk, a->dk_sh, a->dtype, R * kz, s), "cast dk");
+  RA_HIP(launch_cast(dv, a->dv_sh, a->dtype, R * kz, s), "cast dv");
   return RA_OK;
 }
 

@@ -1,0 +1,545 @@
+// bwd.hip -- gradients of exact attention for one batch of (query shard,
+// K/V block) problems: the unit of work of one hop of the backward ring.
+//
+// Training on long contexts is the headline use of ring attention
+// (highthink.cn article, introduction; aiunderstanding.org guide, "Reale
+// Umsetzung"); the pages give no backward algorithm, so the kernels compute
+// the derivative of the forward definition, with the forward's softmax
+// statistics (LSE per query row) and D = <dO, O>:
+//   p = exp(s - lse), dP = dO v^T, dS = p (dP - D),
+//   dV += p^T dO, dK += scale dS^T q, dQ += scale dS k.
+// Blocks contribute additively, so every hop adds its block's share.
+//
+// gfx950 design.  The two MFMA operands of a 32x32x16 product both want
+// their reduction dimension contiguous per lane, so each product picks the
+// orientation whose operands are plain 16-byte reads:
+//  * bwd_dkdv_kernel (a workgroup owns 128 keys, a wave 32; loops over the
+//    query heads of its K/V head and 64-query tiles): S = Q K^T and
+//    dP = dO V^T with Q, dO rows from LDS and K, V rows in registers, so a
+//    lane owns a key column; dV^T += dO^T P and dK^T += Q^T dS then read
+//    dO^T and Q^T from the packed transposed layout (the one V uses in the
+//    forward), whose key order matches how P and dS sit in the registers.
+//  * bwd_dq_kernel (a workgroup owns 128 queries, a wave 32; loops over
+//    64-key tiles): S^T = K Q^T and dP^T = V dO^T as in the forward (a lane
+//    owns a query), dQ^T += K^T dS^T with K^T packed.
+// Each workgroup owns its output tile, so the fp32 accumulation is plain
+// read-add-write: no atomics, deterministic.
+#include <cfloat>
+#include <cmath>
+
+#include "attn_common.h"
+
+namespace ra {
+namespace {
+
+using namespace attn;
+
+constexpr int kBW = 4;       // waves per workgroup (one per SIMD: up to 512 registers)
+constexpr int kBT = 64;      // rows of a staged tile (queries in dkdv, keys in dq)
+
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz16(int row) {  // 16-byte chunk swizzle, 64 LDS banks
+  return ROW_BYTES == 256 ? (row & 15) : ((row >> 1) & 7);
+}
+
+// 16-byte operand read of row `row`, logical chunk `ch`, of a swizzled LDS tile
+template <int ROW_BYTES>
+__device__ __forceinline__ s16x8 rd(const char *base, int row, int ch) {
+  return *(const s16x8 *)(base + row * ROW_BYTES + ((ch ^ swz16<ROW_BYTES>(row)) << 4));
+}
+
+constexpr int kBufWord3B = 0x00020000;  // raw buffer descriptor word 3 (gfx9 family)
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer loads that write LDS directly: lane l's bytes land at dst + size*l
+// (dst is wave-uniform, it goes to M0).  Plain device functions: written in a
+// kernel template, the builtin keeps the host pass from emitting the launch stub.
+__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, lds_void *dst, uint32_t voff,
+                                       uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4b(__amdgpu_buffer_rsrc_t r, lds_void *dst, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, voff, soff, 0, 0);
+}
+// num_records is an unsigned 32-bit byte count; the host bounds every slice to 4 GiB
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
+  const int64_t lim = bytes < 0xffffffffll ? bytes : 0xffffffffll;
+  return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, (int)(uint32_t)lim, kBufWord3B);
+}
+
+// One 64-row tile of rows x ROW_BYTES into a swizzled LDS tile by the 4
+// waves: wave-load u covers rows (wave + 4u) * RPI .. + RPI - 1; lane l lands
+// at LDS chunk l % CPR of its row and fetches the chunk that belongs there
+// (the swizzle is an involution).  soff: byte offset of the tile's first row.
+template <int ROW_BYTES, int ROWS>
+__device__ __forceinline__ void load_tile(char *dst, __amdgpu_buffer_rsrc_t r, uint32_t row_bytes,
+                                          uint32_t soff, int wave, int lane) {
+  constexpr int CPR = ROW_BYTES / 16, RPI = 1024 / ROW_BYTES;
+  constexpr int NU = ROWS * ROW_BYTES / 1024 / kBW;
+  static_assert(NU * kBW * 1024 == ROWS * ROW_BYTES, "tile must split over the waves");
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int idx = wave + kBW * u;
+    const int row = idx * RPI + lane / CPR;
+    const int ch = (lane % CPR) ^ swz16<ROW_BYTES>(row);
+    dma16b(r, (lds_void *)(dst + idx * 1024), row * row_bytes + ch * 16, soff);
+  }
+}
+
+// first local query index i with qid(i) >= kg (nq if none); ids increase with i
+__device__ __forceinline__ int first_query(const IdMap &q, int nq, int64_t kg) {
+  int lo = 0, hi = nq;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (q(mid) >= kg)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  return lo;
+}
+
+template <int D>
+constexpr size_t dkdv_stage_bytes() {
+  return (size_t)4 * kBT * D * 2 + 2 * kBT * 4;  // Q, dO rows, Q^T, dO^T tiles, lse, D
+}
+template <int D>
+constexpr size_t dq_stage_bytes() {
+  return (size_t)3 * kBT * D * 2;  // K, V rows, K^T tile
+}
+
+template <int D, bool BF16>
+__global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
+  using M = Mfma16<BF16>;
+  const BatchParams &p = P.a;
+  constexpr int KS = D / 16, DT = D / 32;
+  constexpr int RB = D * 2;          // bytes of a Q / dO row
+  constexpr int TB = kBT * 2;        // bytes of a packed Q^T / dO^T row (64 queries)
+  constexpr int TQ = kBT * RB;       // bytes of a row tile
+  constexpr int TT = D * TB;         // bytes of a packed tile
+  constexpr size_t ST = dkdv_stage_bytes<D>();
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  // stage layout: sQ | sdO | sQT | sdOT | lse[64] | D[64]
+
+  // workgroup -> (key tile, problem, batch, K/V head); key tile slowest so the
+  // heaviest causal tiles (most queries after them) start first
+  const int nkt = (p.nk + 127) / 128;
+  const int per_kt = p.nz * p.B * p.Hkv;
+  int idx = blockIdx.x;
+  const int kt = idx / per_kt;
+  idx -= kt * per_kt;
+  const int kvh = idx % p.Hkv;
+  idx /= p.Hkv;
+  const int b = idx % p.B;
+  const int z = idx / p.B;
+  (void)nkt;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int hl = lane >> 5, c32 = lane & 31;
+  const IdMap qid = query_ids(p, z), kid = key_ids(p, z);
+  const int kvi = (p.kv_idx0 + z) % p.kv_idx_mod;
+  const short *kp = (const short *)p.k + kvi * p.kv_zstride + b * p.ks_b + kvh * p.ks_h;
+  const short *vp = (const short *)p.v + kvi * p.kv_vzstride + b * p.vs_b + kvh * p.vs_h;
+  const int G = p.Hq / p.Hkv;
+  const float c = p.scale * kLog2e;
+
+  // this wave's 32 keys and this lane's key column
+  const int j0w = kt * 128 + wave * 32;
+  const int jw = j0w + c32;
+  const bool kvalid = jw < p.nk;
+  const bool wave_keys = j0w < p.nk;
+  const int64_t kj = kvalid ? kid(jw) : INT64_MAX;
+  const int64_t kfirst = wave_keys ? kid(j0w) : INT64_MAX;
+  const int64_t klast = wave_keys ? kid(min(j0w + 31, p.nk - 1)) : INT64_MAX;
+
+  // B operands of S = Q K^T and dP = dO V^T: K^T, V^T columns = this lane's key row
+  s16x8 kB[KS], vB[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    s16x8 x = (s16x8){0, 0, 0, 0, 0, 0, 0, 0}, y = x;
+    if (kvalid) {
+      x = *(const s16x8 *)(kp + (int64_t)jw * p.ks_t + 16 * ks + 8 * hl);
+      y = *(const s16x8 *)(vp + (int64_t)jw * p.vs_t + 16 * ks + 8 * hl);
+    }
+    kB[ks] = x;
+    vB[ks] = y;
+  }
+  f32x16 dKt[DT], dVt[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dKt[dt][e] = 0.f;
+      dVt[dt][e] = 0.f;
+    }
+
+  // query tiles that can see any key of this workgroup, for every query head
+  // of the K/V head: iteration f = hq * per + (qt - qt0)
+  const int64_t kwg = kid(min(kt * 128, p.nk - 1));
+  const int qt0 = (p.causal ? first_query(qid, p.nq, kwg) : 0) / kBT;
+  const int per = (p.nq + kBT - 1) / kBT - qt0;
+  const int nf = per > 0 ? G * per : 0;
+  const int nq_pad = (p.nq + 63) / 64 * 64;
+  const uint32_t rowb = (uint32_t)p.qs_t * 2;
+  auto issue = [&](int f, int stage) {
+    const int hq = f / per, qt = qt0 + f % per;
+    const int h = kvh * G + hq;
+    const int64_t qoff = p.q_zstride * z + b * p.qs_b + h * p.qs_h;
+    const int64_t rows_bytes = (int64_t)p.nq * rowb;
+    char *st = lds + stage * ST;
+    load_tile<RB, kBT>(st, rsrc((const short *)p.q + qoff, rows_bytes), rowb, qt * kBT * rowb,
+                       wave, lane);
+    load_tile<RB, kBT>(st + TQ, rsrc((const short *)P.dout + qoff, rows_bytes), rowb,
+                       qt * kBT * rowb, wave, lane);
+    const int64_t toff = P.qT_zstride * z + ((int64_t)b * p.Hq + h) * D * nq_pad;
+    const int64_t tbytes = (int64_t)D * nq_pad * 2;
+    load_tile<TB, D>(st + 2 * TQ, rsrc((const short *)P.qT + toff, tbytes), TB, qt * TT, wave,
+                     lane);
+    load_tile<TB, D>(st + 2 * TQ + TT, rsrc((const short *)P.doT + toff, tbytes), TB, qt * TT,
+                     wave, lane);
+    if (wave == 0) {
+      const int64_t moff = p.ml_zstride * z + ((int64_t)b * p.Hq + h) * p.nq;
+      const int64_t mbytes = (int64_t)p.nq * 4;
+      dma4b(rsrc(P.lse + moff, mbytes), (lds_void *)(st + 2 * TQ + 2 * TT), lane * 4,
+            qt * kBT * 4);
+      dma4b(rsrc(P.Dv + moff, mbytes), (lds_void *)(st + 2 * TQ + 2 * TT + kBT * 4), lane * 4,
+            qt * kBT * 4);
+    }
+  };
+
+  if (nf > 0) issue(0, 0);
+  for (int f = 0; f < nf; ++f) {
+    // tile f has landed (this wave's loads, then everyone's); stage (f+1)&1 was
+    // last read in iteration f-1
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (f + 1 < nf) issue(f + 1, (f + 1) & 1);
+    const char *st = lds + (f & 1) * ST;
+    const char *sQ = st, *sdO = st + TQ, *sQT = st + 2 * TQ, *sdOT = st + 2 * TQ + TT;
+    const float *sLse = (const float *)(st + 2 * TQ + 2 * TT);
+    const float *sDv = sLse + kBT;
+    const int i0 = (qt0 + f % per) * kBT;
+    const int ilast = min(i0 + kBT, p.nq) - 1;
+    if (!wave_keys || (p.causal && kfirst > qid(ilast))) continue;  // nothing allowed
+    // no mask when every query of the tile is valid and sees every key of the wave
+    const bool full = !p.causal ? (i0 + kBT <= p.nq) : (i0 + kBT <= p.nq && klast <= qid(i0));
+
+    f32x16 S[2], dP[2];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        S[ib][e] = 0.f;
+        dP[ib][e] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        S[ib] = M::mma(rd<RB>(sQ, 32 * ib + c32, 2 * ks + hl), kB[ks], S[ib]);
+        dP[ib] = M::mma(rd<RB>(sdO, 32 * ib + c32, 2 * ks + hl), vB[ks], dP[ib]);
+      }
+    }
+    // element e of S[ib]: query 32ib + 8(e/4) + 4hl + e%4 of the tile, key column jw
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int il = 32 * ib + 8 * rg + 4 * hl;
+        const float4 l4 = *(const float4 *)(sLse + il);
+        const float4 d4 = *(const float4 *)(sDv + il);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int e = 4 * rg + u;
+          bool ok = kvalid && lv[u] > -INFINITY;  // a row with no key at all has no gradient
+          if (!full) ok = ok && (i0 + il + u < p.nq) && (!p.causal || kj <= qid(i0 + il + u));
+          const float pe = ok ? __builtin_amdgcn_exp2f(fmaf(S[ib][e], c, -lv[u] * kLog2e)) : 0.f;
+          S[ib][e] = pe;                        // P
+          dP[ib][e] = pe * (dP[ib][e] - dv[u]);  // dS
+        }
+      }
+    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 64 queries
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) {
+      const s16x8 pp = M::pack(S[kq >> 1], 8 * (kq & 1));
+      const s16x8 ds = M::pack(dP[kq >> 1], 8 * (kq & 1));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dVt[dt] = M::mma(rd<TB>(sdOT, 32 * dt + c32, 2 * kq + hl), pp, dVt[dt]);
+        dKt[dt] = M::mma(rd<TB>(sQT, 32 * dt + c32, 2 * kq + hl), ds, dKt[dt]);
+      }
+    }
+  }
+  if (!kvalid) return;
+  // element e of dKt[dt]: d = 32dt + 8(e/4) + 4hl + e%4 of key jw
+  const int64_t ko = P.dk_zstride * kvi + ((int64_t)(b * p.Hkv + kvh) * p.nk + jw) * D;
+  float *dk = P.dk + ko;
+  float *dv = P.dv + ko;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int dd = 32 * dt + 8 * rg + 4 * hl;
+      float4 a = *(float4 *)(dk + dd), v = *(float4 *)(dv + dd);
+      a.x += p.scale * dKt[dt][4 * rg + 0];
+      a.y += p.scale * dKt[dt][4 * rg + 1];
+      a.z += p.scale * dKt[dt][4 * rg + 2];
+      a.w += p.scale * dKt[dt][4 * rg + 3];
+      v.x += dVt[dt][4 * rg + 0];
+      v.y += dVt[dt][4 * rg + 1];
+      v.z += dVt[dt][4 * rg + 2];
+      v.w += dVt[dt][4 * rg + 3];
+      *(float4 *)(dk + dd) = a;
+      *(float4 *)(dv + dd) = v;
+    }
+}
+
+template <int D, bool BF16>
+__global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
+  using M = Mfma16<BF16>;
+  const BatchParams &p = P.a;
+  constexpr int KS = D / 16, DT = D / 32;
+  constexpr int RB = D * 2;    // bytes of a K / V row
+  constexpr int TB = kBT * 2;  // bytes of a packed K^T row (64 keys)
+  constexpr int TQ = kBT * RB;
+  constexpr int TT = D * TB;
+  constexpr size_t ST = dq_stage_bytes<D>();
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  // stage layout: sK | sV | sKT
+
+  // workgroup -> (query tile, problem, batch, query head); query tile slowest,
+  // last tiles (most keys before them) first
+  const int nqt = (p.nq + 127) / 128;
+  const int per_qt = p.nz * p.B * p.Hq;
+  int idx = blockIdx.x;
+  const int qtr = idx / per_qt;
+  idx -= qtr * per_qt;
+  const int qt = p.causal ? nqt - 1 - qtr : qtr;
+  const int h = idx % p.Hq;
+  idx /= p.Hq;
+  const int b = idx % p.B;
+  const int z = idx / p.B;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int hl = lane >> 5, c32 = lane & 31;
+  const IdMap qid = query_ids(p, z), kid = key_ids(p, z);
+  const int kvh = h / (p.Hq / p.Hkv);
+  const int kvi = (p.kv_idx0 + z) % p.kv_idx_mod;
+  const short *kp = (const short *)p.k + kvi * p.kv_zstride + b * p.ks_b + kvh * p.ks_h;
+  const short *vp = (const short *)p.v + kvi * p.kv_vzstride + b * p.vs_b + kvh * p.vs_h;
+  const int nk_pad = (p.nk + 63) / 64 * 64;
+  const short *kT = (const short *)P.kT + P.kT_zstride * kvi + ((int64_t)b * p.Hkv + kvh) * D * nk_pad;
+  const float c = p.scale * kLog2e;
+
+  // this wave's 32 queries and this lane's query
+  const int iw0 = qt * 128 + wave * 32;
+  const int iw = iw0 + c32;
+  const bool valid = iw < p.nq;
+  const int64_t qoff = p.q_zstride * z + b * p.qs_b + h * p.qs_h;
+  s16x8 qB[KS], dB[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    s16x8 x = (s16x8){0, 0, 0, 0, 0, 0, 0, 0}, y = x;
+    if (valid) {
+      x = *(const s16x8 *)((const short *)p.q + qoff + (int64_t)iw * p.qs_t + 16 * ks + 8 * hl);
+      y = *(const s16x8 *)((const short *)P.dout + qoff + (int64_t)iw * p.qs_t + 16 * ks + 8 * hl);
+    }
+    qB[ks] = x;
+    dB[ks] = y;
+  }
+  const int64_t moff = p.ml_zstride * z + ((int64_t)b * p.Hq + h) * p.nq;
+  float l2 = INFINITY, dd = 0.f;
+  if (valid) {
+    const float lse = P.lse[moff + iw];
+    if (lse > -INFINITY) l2 = lse * kLog2e;
+    dd = P.Dv[moff + iw];
+  }
+  const int jlim = valid ? key_prefix(p, kid, qid(iw)) : 0;
+  const int iw_last = min(iw0 + 31, p.nq - 1), i_wg_last = min(qt * 128 + 127, p.nq - 1);
+  const bool wave_rows = iw0 < p.nq;
+  const int ntiles = (key_prefix(p, kid, qid(i_wg_last)) + kBT - 1) / kBT;
+  const int ntiles_w = wave_rows ? (key_prefix(p, kid, qid(iw_last)) + kBT - 1) / kBT : 0;
+  const int nfull_w = wave_rows ? key_prefix(p, kid, qid(iw0)) / kBT : 0;
+
+  const uint32_t rowb = (uint32_t)p.ks_t * 2;
+  const int64_t kbytes = (int64_t)p.nk * rowb;
+  const auto kr = rsrc(kp, kbytes), vr = rsrc(vp, (int64_t)p.nk * p.vs_t * 2),
+             tr = rsrc(kT, (int64_t)D * nk_pad * 2);
+  auto issue = [&](int t, int stage) {
+    char *st = lds + stage * ST;
+    load_tile<RB, kBT>(st, kr, rowb, t * kBT * rowb, wave, lane);
+    load_tile<RB, kBT>(st + TQ, vr, (uint32_t)p.vs_t * 2, t * kBT * (uint32_t)p.vs_t * 2, wave,
+                       lane);
+    load_tile<TB, D>(st + 2 * TQ, tr, TB, t * TT, wave, lane);
+  };
+
+  f32x16 dQt[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dQt[dt][e] = 0.f;
+
+  if (ntiles > 0) issue(0, 0);
+  for (int t = 0; t < ntiles; ++t) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
+    if (t >= ntiles_w) continue;
+    const char *st = lds + (t & 1) * ST;
+    const char *sK = st, *sV = st + TQ, *sKT = st + 2 * TQ;
+    const int j0 = t * kBT;
+    f32x16 S[2], dP[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        S[kb][e] = 0.f;
+        dP[kb][e] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        S[kb] = M::mma(rd<RB>(sK, 32 * kb + c32, 2 * ks + hl), qB[ks], S[kb]);
+        dP[kb] = M::mma(rd<RB>(sV, 32 * kb + c32, 2 * ks + hl), dB[ks], dP[kb]);
+      }
+    }
+    const bool diag = t >= nfull_w || !valid;
+    // element e of S^T[kb]: key j0 + 32kb + 8(e/4) + 4hl + e%4 of this lane's query
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = j0 + 32 * kb + (e >> 2) * 8 + 4 * hl + (e & 3);
+        const bool ok = !diag || j < jlim;
+        const float pe = ok ? __builtin_amdgcn_exp2f(fmaf(S[kb][e], c, -l2)) : 0.f;
+        dP[kb][e] = pe * (dP[kb][e] - dd);  // dS^T
+      }
+    // dQ^T += K^T dS^T over the tile's 64 keys
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) {
+      const s16x8 ds = M::pack(dP[kq >> 1], 8 * (kq & 1));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        dQt[dt] = M::mma(rd<TB>(sKT, 32 * dt + c32, 2 * kq + hl), ds, dQt[dt]);
+    }
+  }
+  if (!valid) return;
+  float *dq = P.dq + P.dq_zstride * z + (((int64_t)b * p.Hq + h) * p.nq + iw) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = 32 * dt + 8 * rg + 4 * hl;
+      float4 a = *(float4 *)(dq + d0);
+      a.x += p.scale * dQt[dt][4 * rg + 0];
+      a.y += p.scale * dQt[dt][4 * rg + 1];
+      a.z += p.scale * dQt[dt][4 * rg + 2];
+      a.w += p.scale * dQt[dt][4 * rg + 3];
+      *(float4 *)(dq + d0) = a;
+    }
+}
+
+// D = <dO, O> per row (16-bit inputs), one wave per row
+template <typename T>
+__global__ void __launch_bounds__(256) bwd_prep_kernel(const T *__restrict__ o,
+                                                       const T *__restrict__ dout,
+                                                       float *__restrict__ Dv, int64_t rows,
+                                                       int d) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float acc = 0.f;
+  for (int c = lane; c < d; c += 64)
+    acc += (float)o[row * d + c] * (float)dout[row * d + c];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) Dv[row] = acc;
+}
+
+__global__ void __launch_bounds__(256) zero_kernel(float4 *__restrict__ x, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n4) x[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) cast_kernel(const float4 *__restrict__ x,
+                                                   T *__restrict__ y, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  const float4 v = x[i];
+  T *o = y + 4 * i;
+  o[0] = (T)v.x;
+  o[1] = (T)v.y;
+  o[2] = (T)v.z;
+  o[3] = (T)v.w;
+}
+
+template <int D, bool BF16>
+hipError_t launch_bwd_d(const BwdParams &P, hipStream_t s) {
+  const BatchParams &p = P.a;
+  const int64_t groups = (int64_t)p.nz * p.B;
+  constexpr size_t l1 = 2 * dkdv_stage_bytes<D>(), l2 = 2 * dq_stage_bytes<D>();
+  static bool attr_set = false;  // more than 64 KB of LDS per workgroup must be opted into
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)bwd_dkdv_kernel<D, BF16>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)l1);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void *)bwd_dq_kernel<D, BF16>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)l2);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  if (p.nk > 0) {
+    const int64_t n1 = groups * p.Hkv * ((p.nk + 127) / 128);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16>), dim3((unsigned)n1), dim3(kBW * 64), l1, s, P);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t n2 = groups * p.Hq * ((p.nq + 127) / 128);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BF16>), dim3((unsigned)n2), dim3(kBW * 64), l2, s, P);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_prep(const void *o, const void *dout, float *Dv, int dtype, int64_t rows,
+                           int32_t d, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((rows + 3) / 4);
+  if (dtype == RA_DT_BF16)
+    hipLaunchKernelGGL(bwd_prep_kernel<__bf16>, dim3(blocks), dim3(256), 0, s,
+                       (const __bf16 *)o, (const __bf16 *)dout, Dv, rows, d);
+  else
+    hipLaunchKernelGGL(bwd_prep_kernel<_Float16>, dim3(blocks), dim3(256), 0, s,
+                       (const _Float16 *)o, (const _Float16 *)dout, Dv, rows, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(float *x, int64_t n, hipStream_t s) {
+  const int64_t n4 = n / 4;  // callers pass multiples of 4 (rows of d floats)
+  if (n4 == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                     (float4 *)x, n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast(const float *x, void *y, int dtype, int64_t n, hipStream_t s) {
+  const int64_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  const dim3 g((unsigned)((n4 + 255) / 256));
+  if (dtype == RA_DT_BF16)
+    hipLaunchKernelGGL(cast_kernel<__bf16>, g, dim3(256), 0, s, (const float4 *)x, (__bf16 *)y, n4);
+  else
+    hipLaunchKernelGGL(cast_kernel<_Float16>, g, dim3(256), 0, s, (const float4 *)x,
+                       (_Float16 *)y, n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdParams &p, int dtype, hipStream_t s) {
+  if (p.a.nq == 0) return hipSuccess;
+  if (dtype == RA_DT_BF16)
+    return p.a.d == 64 ? launch_bwd_d<64, true>(p, s) : launch_bwd_d<128, true>(p, s);
+  return p.a.d == 64 ? launch_bwd_d<64, false>(p, s) : launch_bwd_d<128, false>(p, s);
+}
+
+}  // namespace ra

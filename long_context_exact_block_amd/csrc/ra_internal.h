@@ -106,6 +106,32 @@ hipError_t launch_layout_move(bool gather, const void *src, void *dst, const int
                               int32_t elem_bytes, int64_t B, int64_t H, int64_t S, int64_t d,
                               int32_t R, int32_t rank0, int32_t n_ranks, hipStream_t s);
 
+// Backward of a batch of (query shard, K/V block) problems.  `a` carries the
+// forward's addressing (q, k, v rows, contiguous per problem, global ids, z
+// batching); the rest:
+//   dout        like q (same strides)
+//   qT, doT     packed (ra_pack_v layout) per query problem z: q_zstride_p
+//   kT          packed per K/V block (block index as for k): kT_zstride
+//   lse, Dv     fp32 per query row: + z*ml_zstride, [b][h][i]
+//   dq          fp32 accumulator like q rows: + z*dq_zstride, [b][h][i][d]
+//   dk, dv      fp32 accumulators per K/V block: + kv*dk_zstride, [b][kvh][j][d]
+// Each problem z adds its contributions; within a launch no two problems
+// share a K/V block or a query shard.
+struct BwdParams {
+  BatchParams a;
+  const void *dout;
+  const void *qT, *doT, *kT;
+  int64_t qT_zstride, kT_zstride;
+  const float *lse, *Dv;
+  float *dq, *dk, *dv;
+  int64_t dq_zstride, dk_zstride;
+};
+hipError_t launch_bwd_prep(const void *o, const void *dout, float *Dv, int dtype, int64_t rows,
+                           int32_t d, hipStream_t s);
+hipError_t launch_bwd(const BwdParams &p, int dtype, hipStream_t s);
+hipError_t launch_zero(float *x, int64_t n, hipStream_t s);  // n % 4 == 0
+hipError_t launch_cast(const float *x, void *y, int dtype, int64_t n, hipStream_t s);
+
 // Per-thread detail text for ra_last_error().
 void set_error(const char *fmt, ...);
 void clear_error();

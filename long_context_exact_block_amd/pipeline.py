@@ -77,3 +77,26 @@ class RingAttention:
         self.gather(q, k, v, stream)
         self.ring(stream)
         self.scatter(o, lse, stream)
+
+    def backward(self, dout, dq, dk, dv, stream=None):
+        """Gradients after ``run`` (same inputs still gathered): dout [B][Hq][S][d] in the
+        original order; writes dq (rows of the computed ranks) and dk, dv [B][Hkv][S][d]
+        (contributions of the computed ranks' queries), original order, in dtype."""
+        torch = self.torch
+        nr, R, n = self.n_ranks, self.R, self.n
+        if not hasattr(self, "do_sh"):
+            dev = self.q_sh.device
+            self.do_sh = torch.empty_like(self.q_sh)
+            self.dq_sh = torch.empty_like(self.q_sh)
+            self.dk_sh = torch.empty_like(self.k_sh)
+            self.dv_sh = torch.empty_like(self.v_sh)
+            self.bargs = rb.ring_bwd_args(self.q_sh, self.k_sh, self.v_sh, self.o_sh, self.do_sh,
+                                          self.lse_sh, self.dq_sh, self.dk_sh, self.dv_sh, R,
+                                          self.rank0, nr, self.scale, self.causal, self.layout)
+            nb = rb.ra_ring_bwd_workspace_size(self.bargs)
+            self.bworkspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        rb.ra_layout_gather(dout, self.do_sh, self.fwd, R, self.rank0, nr, stream)
+        rb.ra_ring_bwd(self.bargs, self.bworkspace, stream)
+        rb.ra_layout_scatter(self.dq_sh, dq, self.fwd, R, self.rank0, nr, stream)
+        rb.ra_layout_scatter(self.dk_sh, dk, self.fwd, R, 0, R, stream)
+        rb.ra_layout_scatter(self.dv_sh, dv, self.fwd, R, 0, R, stream)
