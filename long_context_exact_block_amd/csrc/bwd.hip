@@ -225,50 +225,95 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
     // no mask when every query of the tile is valid and sees every key of the wave
     const bool full = !p.causal ? (i0 + kBT <= p.nq) : (i0 + kBT <= p.nq && klast <= qid(i0));
 
+    // S = Q K^T and dP = dO V^T: four independent accumulators, the A
+    // operands of k-step ks + 1 read from LDS while k-step ks is multiplied
     f32x16 S[2], dP[2];
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
+    for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         S[ib][e] = 0.f;
         dP[ib][e] = 0.f;
       }
+    s16x8 aq[KS][2], ao[KS][2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        S[ib] = M::mma(rd<RB>(sQ, 32 * ib + c32, 2 * ks + hl), kB[ks], S[ib]);
-        dP[ib] = M::mma(rd<RB>(sdO, 32 * ib + c32, 2 * ks + hl), vB[ks], dP[ib]);
-      }
+    for (int ib = 0; ib < 2; ++ib) {
+      aq[0][ib] = rd<RB>(sQ, 32 * ib + c32, hl);
+      ao[0][ib] = rd<RB>(sdO, 32 * ib + c32, hl);
     }
-    // element e of S[ib]: query 32ib + 8(e/4) + 4hl + e%4 of the tile, key column jw
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) {
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int il = 32 * ib + 8 * rg + 4 * hl;
+        for (int ib = 0; ib < 2; ++ib) {
+          aq[ks + 1][ib] = rd<RB>(sQ, 32 * ib + c32, 2 * (ks + 1) + hl);
+          ao[ks + 1][ib] = rd<RB>(sdO, 32 * ib + c32, 2 * (ks + 1) + hl);
+        }
+      }
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+        S[ib] = M::mma(aq[ks][ib], kB[ks], S[ib]);
+        dP[ib] = M::mma(ao[ks][ib], vB[ks], dP[ib]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Group kq (16 queries: half kq/2, registers 8(kq%2) .. +7) of the tile:
+    // P and dS packed as B operands.  Element e of S[ib] is query
+    // 32ib + 8(e/4) + 4hl + e%4 of the tile, key column jw.
+    struct PdS {
+      s16x8 p, ds;
+    };
+    auto elem = [&](int kq) {
+      const int ib = kq >> 1, e0 = 8 * (kq & 1);
+      f32x16 pv, dv;
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) {
+        const int il = 32 * ib + 8 * ((e0 >> 2) + rg) + 4 * hl;
         const float4 l4 = *(const float4 *)(sLse + il);
         const float4 d4 = *(const float4 *)(sDv + il);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int e = 4 * rg + u;
+          const int e = e0 + 4 * rg + u;
           bool ok = kvalid && lv[u] > -INFINITY;  // a row with no key at all has no gradient
           if (!full) ok = ok && (i0 + il + u < p.nq) && (!p.causal || kj <= qid(i0 + il + u));
           const float pe = ok ? __builtin_amdgcn_exp2f(fmaf(S[ib][e], c, -lv[u] * kLog2e)) : 0.f;
-          S[ib][e] = pe;                        // P
-          dP[ib][e] = pe * (dP[ib][e] - dv[u]);  // dS
+          pv[4 * rg + u] = pe;
+          dv[4 * rg + u] = pe * (dP[ib][e] - dd[u]);
         }
       }
-    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 64 queries
+      PdS r;
+      r.p = M::pack(pv, 0);
+      r.ds = M::pack(dv, 0);
+      return r;
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 64 queries: the
+    // operands of group kq + 1 are read and its P, dS computed while the
+    // MFMAs of group kq run
+    s16x8 ct[4][DT][2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      ct[0][dt][0] = rd<TB>(sdOT, 32 * dt + c32, hl);
+      ct[0][dt][1] = rd<TB>(sQT, 32 * dt + c32, hl);
+    }
+    PdS cur = elem(0);
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq) {
-      const s16x8 pp = M::pack(S[kq >> 1], 8 * (kq & 1));
-      const s16x8 ds = M::pack(dP[kq >> 1], 8 * (kq & 1));
+      if (kq + 1 < 4) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          ct[kq + 1][dt][0] = rd<TB>(sdOT, 32 * dt + c32, 2 * (kq + 1) + hl);
+          ct[kq + 1][dt][1] = rd<TB>(sQT, 32 * dt + c32, 2 * (kq + 1) + hl);
+        }
+      }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        dVt[dt] = M::mma(rd<TB>(sdOT, 32 * dt + c32, 2 * kq + hl), pp, dVt[dt]);
-        dKt[dt] = M::mma(rd<TB>(sQT, 32 * dt + c32, 2 * kq + hl), ds, dKt[dt]);
+        dVt[dt] = M::mma(ct[kq][dt][0], cur.p, dVt[dt]);
+        dKt[dt] = M::mma(ct[kq][dt][1], cur.ds, dKt[dt]);
       }
+      if (kq + 1 < 4) cur = elem(kq + 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   if (!kvalid) return;
@@ -389,38 +434,69 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
     const char *st = lds + (t & 1) * ST;
     const char *sK = st, *sV = st + TQ, *sKT = st + 2 * TQ;
     const int j0 = t * kBT;
+    // S^T = K Q^T and dP^T = V dO^T, A operands one k-step ahead
     f32x16 S[2], dP[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         S[kb][e] = 0.f;
         dP[kb][e] = 0.f;
       }
+    s16x8 ak[KS][2], av[KS][2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        S[kb] = M::mma(rd<RB>(sK, 32 * kb + c32, 2 * ks + hl), qB[ks], S[kb]);
-        dP[kb] = M::mma(rd<RB>(sV, 32 * kb + c32, 2 * ks + hl), dB[ks], dP[kb]);
+    for (int kb = 0; kb < 2; ++kb) {
+      ak[0][kb] = rd<RB>(sK, 32 * kb + c32, hl);
+      av[0][kb] = rd<RB>(sV, 32 * kb + c32, hl);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          ak[ks + 1][kb] = rd<RB>(sK, 32 * kb + c32, 2 * (ks + 1) + hl);
+          av[ks + 1][kb] = rd<RB>(sV, 32 * kb + c32, 2 * (ks + 1) + hl);
+        }
       }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        S[kb] = M::mma(ak[ks][kb], qB[ks], S[kb]);
+        dP[kb] = M::mma(av[ks][kb], dB[ks], dP[kb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     const bool diag = t >= nfull_w || !valid;
-    // element e of S^T[kb]: key j0 + 32kb + 8(e/4) + 4hl + e%4 of this lane's query
+    // group kq (16 keys: half kq/2, registers 8(kq%2) .. +7): dS^T packed.
+    // Element e of S^T[kb] is key j0 + 32kb + 8(e/4) + 4hl + e%4 of this lane's query.
+    auto elem = [&](int kq) {
+      const int kb = kq >> 1, e0 = 8 * (kq & 1);
+      f32x16 dv;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u;
         const int j = j0 + 32 * kb + (e >> 2) * 8 + 4 * hl + (e & 3);
         const bool ok = !diag || j < jlim;
         const float pe = ok ? __builtin_amdgcn_exp2f(fmaf(S[kb][e], c, -l2)) : 0.f;
-        dP[kb][e] = pe * (dP[kb][e] - dd);  // dS^T
+        dv[u] = pe * (dP[kb][e] - dd);
       }
-    // dQ^T += K^T dS^T over the tile's 64 keys
+      return M::pack(dv, 0);
+    };
+    // dQ^T += K^T dS^T over the tile's 64 keys, group kq + 1 prepared while
+    // the MFMAs of group kq run
+    s16x8 ct[4][DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) ct[0][dt] = rd<TB>(sKT, 32 * dt + c32, hl);
+    s16x8 cur = elem(0);
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq) {
-      const s16x8 ds = M::pack(dP[kq >> 1], 8 * (kq & 1));
+      if (kq + 1 < 4) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        dQt[dt] = M::mma(rd<TB>(sKT, 32 * dt + c32, 2 * kq + hl), ds, dQt[dt]);
+        for (int dt = 0; dt < DT; ++dt) ct[kq + 1][dt] = rd<TB>(sKT, 32 * dt + c32, 2 * (kq + 1) + hl);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dQt[dt] = M::mma(ct[kq][dt], cur, dQt[dt]);
+      if (kq + 1 < 4) cur = elem(kq + 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   if (!valid) return;
