@@ -456,8 +456,7 @@ def main():
     if w.name == "rank3_of_8_share_1M_striped_bf16" and args.merge == "fused":
         traffic = traffic_from_profile(
             ["long_context_exact_block_amd/csrc/block_fwd_packed.hip",
-             "long_context_exact_block_amd/csrc/attn_common.h",
-             "long_context_exact_block_amd/csrc/ra_internal.h"],
+             "long_context_exact_block_amd/csrc/attn_common.h"],
             "profiles/attn_packed_1M_share_traffic.json")
 
     line = {
