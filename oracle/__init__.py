@@ -73,6 +73,10 @@ class Oracle:
         lib.ora_ring_emulate.restype = C
         lib.ora_pair_counts.argtypes = [C, I64, I32, P]
         lib.ora_pair_counts.restype = C
+        lib.ora_bwd_query_rows.argtypes = [P, P, P, P, P, I64, P, P, I64, I64, I64, I64, D, C,
+                                           P, P, P]
+        lib.ora_bwd_keys.argtypes = [P, P, P, P, P, P, P, I64, P, P, P, I64, P, P, I64, I64, I64,
+                                     I64, D, C, P, P]
         lib.ora_attention_bwd.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, D, C, P, P, P]
         lib.ora_attention_bwd.restype = C
         lib.ora_block_bwd.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, D, C, P, P,
@@ -201,6 +205,39 @@ class Oracle:
             raise MemoryError("attention_bwd")
         return dq, dk, dv
 
+    def bwd_query_rows(self, q_rows, dout_rows, row_b, row_h, row_t, k, v, Hq: int,
+                       scale: float, causal: bool):
+        """dq, lse, D of listed query rows (original token order) over their whole key set."""
+        q_rows, dout_rows, k, v = _f32(q_rows), _f32(dout_rows), _f32(k), _f32(v)
+        rb, rh, rt = (np.ascontiguousarray(x, np.int64) for x in (row_b, row_h, row_t))
+        nrows, d = q_rows.shape
+        _, Hkv, S, _ = k.shape
+        dq = np.empty((nrows, d), np.float64)
+        lse = np.empty(nrows, np.float64)
+        Dv = np.empty(nrows, np.float64)
+        self.lib.ora_bwd_query_rows(_ptr(q_rows), _ptr(dout_rows), _ptr(rb), _ptr(rh), _ptr(rt),
+                                    nrows, _ptr(k), _ptr(v), Hq, Hkv, S, d, float(scale),
+                                    int(bool(causal)), _ptr(dq), _ptr(lse), _ptr(Dv))
+        return dq, lse, Dv
+
+    def bwd_keys(self, q_rows, dout_rows, row_b, row_h, row_t, lse, Dv, key_b, key_g, key_t, k,
+                 v, Hq: int, scale: float, causal: bool):
+        """dk, dv of listed keys from the listed query rows (with their lse, D)."""
+        q_rows, dout_rows, k, v = _f32(q_rows), _f32(dout_rows), _f32(k), _f32(v)
+        rb, rh, rt, kb_, kg_, kt_ = (np.ascontiguousarray(x, np.int64)
+                                     for x in (row_b, row_h, row_t, key_b, key_g, key_t))
+        lse = np.ascontiguousarray(lse, np.float64)
+        Dv = np.ascontiguousarray(Dv, np.float64)
+        nrows, d = q_rows.shape
+        _, Hkv, S, _ = k.shape
+        dk = np.empty((len(kt_), d), np.float64)
+        dv = np.empty((len(kt_), d), np.float64)
+        self.lib.ora_bwd_keys(_ptr(q_rows), _ptr(dout_rows), _ptr(rb), _ptr(rh), _ptr(rt),
+                              _ptr(lse), _ptr(Dv), nrows, _ptr(kb_), _ptr(kg_), _ptr(kt_),
+                              len(kt_), _ptr(k), _ptr(v), Hq, Hkv, S, d, float(scale),
+                              int(bool(causal)), _ptr(dk), _ptr(dv))
+        return dk, dv
+
     def block_bwd(self, q, k, v, dout, lse, Dv, scale: float, causal: bool, qid, kid):
         """One (query shard, key block) pair's gradient contributions, given the
         global lse and D = <dO, O> per row: q, dout [B][Hq][nq][d]; k, v
@@ -282,6 +319,14 @@ def attention_bwd(*a, **kw):
 
 def block_bwd(*a, **kw):
     return default().block_bwd(*a, **kw)
+
+
+def bwd_query_rows(*a, **kw):
+    return default().bwd_query_rows(*a, **kw)
+
+
+def bwd_keys(*a, **kw):
+    return default().bwd_keys(*a, **kw)
 
 
 def block_partial(*a, **kw):

@@ -522,6 +522,114 @@ void ora_block_bwd(const float *q, const float *k, const float *v,
 }
 
 /*
+ * The backward of single outputs, for checks at sizes where the whole
+ * gradient is out of reach: the same definitions as ora_attention_bwd,
+ * evaluated one row or one key at a time.
+ *
+ * ora_bwd_query_rows: for each listed query row (b, h, t), over its allowed
+ * keys of the whole sequence (original order): lse, D = sum_j p_j <dO, v_j>
+ * and dq = scale sum_j p_j (<dO, v_j> - D) k_j.
+ *   dout_rows [nrows][d] the row's upstream gradient; outputs dq [nrows][d],
+ *   lse [nrows], Dv [nrows] (double).
+ */
+void ora_bwd_query_rows(const float *q_rows, const float *dout_rows,
+                        const int64_t *row_b, const int64_t *row_h,
+                        const int64_t *row_t, int64_t nrows, const float *k,
+                        const float *v, int64_t Hq, int64_t Hkv, int64_t S,
+                        int64_t d, double scale, int causal, double *dq,
+                        double *lse_out, double *D_out) {
+  int64_t group = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const float *qi = q_rows + r * d;
+    const float *gi = dout_rows + r * d;
+    int64_t b = row_b[r], g = row_h[r] / group, t = row_t[r];
+    const float *kb = k + (b * Hkv + g) * S * d;
+    const float *vb = v + (b * Hkv + g) * S * d;
+    int64_t last = causal ? t : S - 1;
+    double m = -INFINITY;
+    for (int64_t j = 0; j <= last; ++j) {
+      double acc = 0.0;
+      for (int64_t c = 0; c < d; ++c) acc += (double)qi[c] * (double)kb[j * d + c];
+      if (acc * scale > m) m = acc * scale;
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j <= last; ++j) {
+      double acc = 0.0;
+      for (int64_t c = 0; c < d; ++c) acc += (double)qi[c] * (double)kb[j * d + c];
+      l += exp(acc * scale - m);
+    }
+    double lse = m + log(l), D = 0.0;
+    for (int64_t j = 0; j <= last; ++j) {
+      double sj = 0.0, dpj = 0.0;
+      for (int64_t c = 0; c < d; ++c) {
+        sj += (double)qi[c] * (double)kb[j * d + c];
+        dpj += (double)gi[c] * (double)vb[j * d + c];
+      }
+      D += exp(sj * scale - lse) * dpj;
+    }
+    double *dqi = dq + r * d;
+    for (int64_t c = 0; c < d; ++c) dqi[c] = 0.0;
+    for (int64_t j = 0; j <= last; ++j) {
+      double sj = 0.0, dpj = 0.0;
+      for (int64_t c = 0; c < d; ++c) {
+        sj += (double)qi[c] * (double)kb[j * d + c];
+        dpj += (double)gi[c] * (double)vb[j * d + c];
+      }
+      double ds = exp(sj * scale - lse) * (dpj - D);
+      for (int64_t c = 0; c < d; ++c) dqi[c] += scale * ds * (double)kb[j * d + c];
+    }
+    lse_out[r] = lse;
+    D_out[r] = D;
+  }
+}
+
+/*
+ * ora_bwd_keys: dk, dv of listed keys (b, g, t) from listed query rows (b, h,
+ * t_q) with their lse and D (from ora_bwd_query_rows): every listed row of
+ * the same batch whose head reads K/V head g and that may see the key
+ * (t <= t_q when causal) contributes p = exp(s - lse):
+ *   dv += p dO,  dk += scale p (<dO, v> - D) q.
+ * q_rows, dout_rows [nrows][d]; outputs dk, dv [nkeys][d] (double).
+ */
+void ora_bwd_keys(const float *q_rows, const float *dout_rows, const int64_t *row_b,
+                  const int64_t *row_h, const int64_t *row_t, const double *lse,
+                  const double *Dv, int64_t nrows, const int64_t *key_b,
+                  const int64_t *key_g, const int64_t *key_t, int64_t nkeys,
+                  const float *k, const float *v, int64_t Hq, int64_t Hkv,
+                  int64_t S, int64_t d, double scale, int causal, double *dk,
+                  double *dv) {
+  int64_t group = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t e = 0; e < nkeys; ++e) {
+    int64_t b = key_b[e], g = key_g[e], t = key_t[e];
+    const float *kj = k + ((b * Hkv + g) * S + t) * d;
+    const float *vj = v + ((b * Hkv + g) * S + t) * d;
+    double *dke = dk + e * d, *dve = dv + e * d;
+    for (int64_t c = 0; c < d; ++c) {
+      dke[c] = 0.0;
+      dve[c] = 0.0;
+    }
+    for (int64_t r = 0; r < nrows; ++r) {
+      if (row_b[r] != b || row_h[r] / group != g) continue;
+      if (causal && t > row_t[r]) continue;
+      const float *qi = q_rows + r * d;
+      const float *gi = dout_rows + r * d;
+      double sj = 0.0, dpj = 0.0;
+      for (int64_t c = 0; c < d; ++c) {
+        sj += (double)qi[c] * (double)kj[c];
+        dpj += (double)gi[c] * (double)vj[c];
+      }
+      double p = exp(sj * scale - lse[r]);
+      for (int64_t c = 0; c < d; ++c) {
+        dve[c] += p * (double)gi[c];
+        dke[c] += scale * p * (dpj - Dv[r]) * (double)qi[c];
+      }
+    }
+  }
+}
+
+/*
  * Causal work per rank by brute force: W[r] = number of (query of rank r,
  * key) pairs with key token <= query token, over the whole sequence.
  * O(S^2): for the small sequences of the tests ([ZZ]: the interleaved

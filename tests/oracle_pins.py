@@ -519,10 +519,39 @@ def check_bwd_constant_values(orc):
     _close(dv.sum(axis=2), g.astype(np.float64).sum(axis=2), 1e-12, 1e-12, "dv sums")
 
 
+def check_bwd_sampled_outputs(orc):
+    """The one-output-at-a-time backward (query rows, then keys from listed rows)
+    equals the whole gradient (pinned by finite differences above), both masks,
+    grouped heads."""
+    rng = _rng(34)
+    B, Hq, Hkv, S, d = 2, 4, 2, 17, 5
+    q = rng.standard_normal((B, Hq, S, d)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, S, d)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, S, d)).astype(np.float32)
+    g = rng.standard_normal((B, Hq, S, d)).astype(np.float32)
+    for causal in (True, False):
+        dq, dk, dv = orc.attention_bwd(q, k, v, g, 0.6, causal)
+        o, lse_full = orc.attention_full(q, k, v, 0.6, causal)
+        bb, hh, tt = (x.ravel() for x in np.meshgrid(np.arange(B), np.arange(Hq), np.arange(S),
+                                                      indexing="ij"))
+        rq, rl, rD = orc.bwd_query_rows(q[bb, hh, tt], g[bb, hh, tt], bb, hh, tt, k, v, Hq, 0.6,
+                                        causal)
+        _close(rq.reshape(B, Hq, S, d), dq, 1e-12, 1e-13, "rows dq")
+        _close(rl.reshape(B, Hq, S), lse_full, 1e-12, 1e-13, "rows lse")
+        _close(rD.reshape(B, Hq, S), (g.astype(np.float64) * o).sum(-1), 1e-12, 1e-13, "rows D")
+        kb, kg, kt = (x.ravel() for x in np.meshgrid(np.arange(B), np.arange(Hkv), np.arange(S),
+                                                      indexing="ij"))
+        rk, rv = orc.bwd_keys(q[bb, hh, tt], g[bb, hh, tt], bb, hh, tt, rl, rD, kb, kg, kt, k, v,
+                              Hq, 0.6, causal)
+        _close(rk.reshape(B, Hkv, S, d), dk, 1e-12, 1e-13, "keys dk")
+        _close(rv.reshape(B, Hkv, S, d), dv, 1e-12, 1e-13, "keys dv")
+
+
 ALL_CHECKS = [
     check_layout_golden, check_layout_bijection, check_zigzag_layout, check_brute_force, check_block_partial_brute,
     check_identical_keys, check_dominant_logit, check_constant_values, check_key_shift,
     check_library_sdpa, check_ring_equals_full, check_layout_independence, check_merge_algebra,
     check_pair_counts, check_coverage, check_gqa_equals_repeated_mha,
     check_bwd_finite_differences, check_bwd_block_partition, check_bwd_constant_values,
+    check_bwd_sampled_outputs,
 ]
