@@ -282,7 +282,8 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
  *               the call ADDS this pair's contributions (dk, dv summed over
  *               the query heads of a K/V head)
  * 16-bit dtypes, d in {64, 128}.  The workspace (ra_block_bwd_workspace_size
- * bytes, 256-byte aligned) holds transposed copies of q, dout, k and D.
+ * bytes, 256-byte aligned) holds transposed copies of q, dout, k, and D and
+ * -lse log2(e) per query row.
  * Deterministic (no atomics).  Asynchronous on `stream`.
  * Errors: RA_ERR_INVALID_ARG, RA_ERR_SHAPE, RA_ERR_DTYPE, RA_ERR_ALIGNMENT,
  * RA_ERR_WORKSPACE, RA_ERR_UNSUPPORTED, RA_ERR_HIP.
@@ -318,7 +319,7 @@ ra_status ra_block_bwd(const ra_block_bwd_args *a, void *workspace, size_t works
  *   dk_sh, dv_sh   device [R][B][Hkv][n][d] in dtype (written): gradients of
  *                  every source block from the computed query ranks
  * Workspace: ra_ring_bwd_workspace_size bytes, 256-byte aligned (transposed
- * copies of Q, dO, K, D and fp32 accumulators).  Asynchronous on `stream`.
+ * copies of Q, dO, K; D and -lse log2(e) per query row; fp32 accumulators).  Asynchronous on `stream`.
  * Errors: as ra_ring_fwd, plus RA_ERR_UNSUPPORTED for fp32.
  */
 typedef struct {

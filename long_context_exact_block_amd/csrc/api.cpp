@@ -173,7 +173,7 @@ ra_status check_block_bwd(const ra_block_bwd_args *a) {
 }
 
 struct BwdWs {
-  size_t qT, doT, kT, dv, total;
+  size_t qT, doT, kT, dv, nl, total;
 };
 BwdWs block_bwd_ws(const ra_block_bwd_args *a) {
   BwdWs w{};
@@ -188,6 +188,7 @@ BwdWs block_bwd_ws(const ra_block_bwd_args *a) {
   w.doT = take(qbytes);
   w.kT = take((size_t)a->B * a->Hkv * a->d * packed_n(a->n_k) * 2);
   w.dv = take((size_t)a->B * a->Hq * a->n_q * 4);
+  w.nl = take((size_t)a->B * a->Hq * a->n_q * 4);
   w.total = off;
   return w;
 }
@@ -226,7 +227,7 @@ ra_status check_ring_bwd(const ra_ring_bwd_args *a) {
 }
 
 struct RingBwdWs {
-  size_t qT, doT, kT, D, dq, dk, dv, total;
+  size_t qT, doT, kT, D, nl, dq, dk, dv, total;
 };
 RingBwdWs ring_bwd_ws(const ra_ring_bwd_args *a) {
   RingBwdWs w{};
@@ -243,6 +244,7 @@ RingBwdWs ring_bwd_ws(const ra_ring_bwd_args *a) {
   w.doT = take(qrows * a->d * np * 2);
   w.kT = take(kblocks * a->d * np * 2);
   w.D = take(qrows * a->n * 4);
+  w.nl = take(qrows * a->n * 4);
   w.dq = take(qrows * a->n * a->d * 4);
   w.dk = take(kblocks * a->n * a->d * 4);
   w.dv = take(kblocks * a->n * a->d * 4);
@@ -805,8 +807,8 @@ ra_status ra_block_bwd(const ra_block_bwd_args *a, void *workspace, size_t works
   const int64_t d = a->d;
   const int64_t qs[3] = {(int64_t)a->Hq * a->n_q * d, (int64_t)a->n_q * d, d};
   const int64_t ks[3] = {(int64_t)a->Hkv * a->n_k * d, (int64_t)a->n_k * d, d};
-  RA_HIP(launch_bwd_prep(a->o, a->dout, (float *)(ws + L.dv), a->dtype,
-                         (int64_t)a->B * a->Hq * a->n_q, a->d, s), "bwd prep");
+  RA_HIP(launch_bwd_prep(a->o, a->dout, a->lse, (float *)(ws + L.dv), (float *)(ws + L.nl),
+                         a->dtype, (int64_t)a->B * a->Hq * a->n_q, a->d, s), "bwd prep");
   RA_HIP(launch_pack_v(a->q, ws + L.qT, 2, (int64_t)a->B * a->Hq, a->Hq, a->n_q, d, qs[0], qs[1],
                        qs[2], s), "pack q");
   RA_HIP(launch_pack_v(a->dout, ws + L.doT, 2, (int64_t)a->B * a->Hq, a->Hq, a->n_q, d, qs[0],
@@ -845,7 +847,7 @@ ra_status ra_block_bwd(const ra_block_bwd_args *a, void *workspace, size_t works
   P.qT = ws + L.qT;
   P.doT = ws + L.doT;
   P.kT = ws + L.kT;
-  P.lse = a->lse;
+  P.nl = (const float *)(ws + L.nl);
   P.Dv = (const float *)(ws + L.dv);
   P.dq = a->dq;
   P.dk = a->dk;
@@ -881,8 +883,8 @@ ra_status ra_ring_bwd(const ra_ring_bwd_args *a, void *workspace, size_t workspa
   RA_HIP(launch_zero(dq, nr * qz, s), "zero dq");
   RA_HIP(launch_zero(dk, R * kz, s), "zero dk");
   RA_HIP(launch_zero(dv, R * kz, s), "zero dv");
-  RA_HIP(launch_bwd_prep(a->o_sh, a->dout_sh, (float *)(ws + L.D), a->dtype,
-                         (int64_t)nr * a->B * a->Hq * n, a->d, s), "bwd prep");
+  RA_HIP(launch_bwd_prep(a->o_sh, a->dout_sh, a->lse, (float *)(ws + L.D), (float *)(ws + L.nl),
+                         a->dtype, (int64_t)nr * a->B * a->Hq * n, a->d, s), "bwd prep");
   RA_HIP(launch_pack_v(a->q_sh, ws + L.qT, 2, (int64_t)nr * a->B * a->Hq, a->Hq, n, d,
                        (int64_t)a->Hq * n * d, (int64_t)n * d, d, s), "pack q");
   RA_HIP(launch_pack_v(a->dout_sh, ws + L.doT, 2, (int64_t)nr * a->B * a->Hq, a->Hq, n, d,
@@ -932,7 +934,7 @@ ra_status ra_ring_bwd(const ra_ring_bwd_args *a, void *workspace, size_t workspa
   P.kT = ws + L.kT;
   P.qT_zstride = (int64_t)a->B * a->Hq * d * n_pad;
   P.kT_zstride = (int64_t)a->B * a->Hkv * d * n_pad;
-  P.lse = a->lse;
+  P.nl = (const float *)(ws + L.nl);
   P.Dv = (const float *)(ws + L.D);
   P.dq = dq;
   P.dk = dk;

@@ -26,6 +26,7 @@
 // read-add-write: no atomics, deterministic.
 #include <cfloat>
 #include <cmath>
+#include <type_traits>
 
 #include "attn_common.h"
 
@@ -120,7 +121,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
   constexpr int TT = D * TB;         // bytes of a packed tile
   constexpr size_t ST = dkdv_stage_bytes<D>();
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  // stage layout: sQ | sdO | sQT | sdOT | lse[64] | D[64]
+  // stage layout: sQ | sdO | sQT | sdOT | nl[64] | D[64]
 
   // workgroup -> (key tile, problem, batch, K/V head); key tile slowest so the
   // heaviest causal tiles (most queries after them) start first
@@ -149,9 +150,15 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
   const int jw = j0w + c32;
   const bool kvalid = jw < p.nk;
   const bool wave_keys = j0w < p.nk;
-  const int64_t kj = kvalid ? kid(jw) : INT64_MAX;
   const int64_t kfirst = wave_keys ? kid(j0w) : INT64_MAX;
   const int64_t klast = wave_keys ? kid(min(j0w + 31, p.nk - 1)) : INT64_MAX;
+  // First local query row that may see this lane's key (ids increase with the
+  // row), and the same for the wave's first and last key: rows before imin_w0
+  // see no key of the wave, rows from imax_w on see all of them.  A lane past
+  // the block end keeps 0: its column is never stored.
+  const int imin = (p.causal && kvalid) ? first_query(qid, p.nq, kid(jw)) : 0;
+  const int imin_w0 = (p.causal && wave_keys) ? first_query(qid, p.nq, kfirst) : 0;
+  const int imax_w = (p.causal && wave_keys) ? first_query(qid, p.nq, klast) : 0;
 
   // B operands of S = Q K^T and dP = dO V^T: K^T, V^T columns = this lane's key row
   s16x8 kB[KS], vB[KS];
@@ -201,7 +208,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
     if (wave == 0) {
       const int64_t moff = p.ml_zstride * z + ((int64_t)b * p.Hq + h) * p.nq;
       const int64_t mbytes = (int64_t)p.nq * 4;
-      dma4b(rsrc(P.lse + moff, mbytes), (lds_void *)(st + 2 * TQ + 2 * TT), lane * 4,
+      dma4b(rsrc(P.nl + moff, mbytes), (lds_void *)(st + 2 * TQ + 2 * TT), lane * 4,
             qt * kBT * 4);
       dma4b(rsrc(P.Dv + moff, mbytes), (lds_void *)(st + 2 * TQ + 2 * TT + kBT * 4), lane * 4,
             qt * kBT * 4);
@@ -217,103 +224,104 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
     if (f + 1 < nf) issue(f + 1, (f + 1) & 1);
     const char *st = lds + (f & 1) * ST;
     const char *sQ = st, *sdO = st + TQ, *sQT = st + 2 * TQ, *sdOT = st + 2 * TQ + TT;
-    const float *sLse = (const float *)(st + 2 * TQ + 2 * TT);
-    const float *sDv = sLse + kBT;
+    const float *sNl = (const float *)(st + 2 * TQ + 2 * TT);
+    const float *sDv = sNl + kBT;
     const int i0 = (qt0 + f % per) * kBT;
     const int ilast = min(i0 + kBT, p.nq) - 1;
-    if (!wave_keys || (p.causal && kfirst > qid(ilast))) continue;  // nothing allowed
+    if (!wave_keys || imin_w0 > ilast) continue;  // nothing allowed
     // no mask when every query of the tile is valid and sees every key of the wave
-    const bool full = !p.causal ? (i0 + kBT <= p.nq) : (i0 + kBT <= p.nq && klast <= qid(i0));
+    const bool full = i0 + kBT <= p.nq && imax_w <= i0;
 
-    // S = Q K^T and dP = dO V^T: four independent accumulators, the A
-    // operands of k-step ks + 1 read from LDS while k-step ks is multiplied
-    f32x16 S[2], dP[2];
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        S[ib][e] = 0.f;
-        dP[ib][e] = 0.f;
-      }
-    s16x8 aq[KS][2], ao[KS][2];
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      aq[0][ib] = rd<RB>(sQ, 32 * ib + c32, hl);
-      ao[0][ib] = rd<RB>(sdO, 32 * ib + c32, hl);
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 1 < KS) {
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-          aq[ks + 1][ib] = rd<RB>(sQ, 32 * ib + c32, 2 * (ks + 1) + hl);
-          ao[ks + 1][ib] = rd<RB>(sdO, 32 * ib + c32, 2 * (ks + 1) + hl);
-        }
-      }
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
-        S[ib] = M::mma(aq[ks][ib], kB[ks], S[ib]);
-        dP[ib] = M::mma(ao[ks][ib], vB[ks], dP[ib]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // Group kq (16 queries: half kq/2, registers 8(kq%2) .. +7) of the tile:
-    // P and dS packed as B operands.  Element e of S[ib] is query
-    // 32ib + 8(e/4) + 4hl + e%4 of the tile, key column jw.
+    // The tile in two halves of 32 queries (ib): S = Q K^T and dP = dO V^T for
+    // the half (A operands of k-step ks + 1 read from LDS while k-step ks is
+    // multiplied), then its two groups of 16 queries (kq = 2 ib + g) into
+    // dV^T += dO^T P and dK^T += Q^T dS.  Element e of S is query
+    // 32 ib + 8(e/4) + 4 hl + e%4 of the tile, key column jw.
+    // Rows with no key at all have nl = -inf, so p = 0.  Full tiles need no
+    // mask; otherwise row r is allowed for this lane's key iff imin <= r < nq.
     struct PdS {
       s16x8 p, ds;
     };
-    auto elem = [&](int kq) {
-      const int ib = kq >> 1, e0 = 8 * (kq & 1);
-      f32x16 pv, dv;
+    auto half = [&](const int ib, auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
+      f32x16 S, dP;
 #pragma unroll
-      for (int rg = 0; rg < 2; ++rg) {
-        const int il = 32 * ib + 8 * ((e0 >> 2) + rg) + 4 * hl;
-        const float4 l4 = *(const float4 *)(sLse + il);
-        const float4 d4 = *(const float4 *)(sDv + il);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int e = e0 + 4 * rg + u;
-          bool ok = kvalid && lv[u] > -INFINITY;  // a row with no key at all has no gradient
-          if (!full) ok = ok && (i0 + il + u < p.nq) && (!p.causal || kj <= qid(i0 + il + u));
-          const float pe = ok ? __builtin_amdgcn_exp2f(fmaf(S[ib][e], c, -lv[u] * kLog2e)) : 0.f;
-          pv[4 * rg + u] = pe;
-          dv[4 * rg + u] = pe * (dP[ib][e] - dd[u]);
-        }
+      for (int e = 0; e < 16; ++e) {
+        S[e] = 0.f;
+        dP[e] = 0.f;
       }
-      PdS r;
-      r.p = M::pack(pv, 0);
-      r.ds = M::pack(dv, 0);
-      return r;
-    };
-    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 64 queries: the
-    // operands of group kq + 1 are read and its P, dS computed while the
-    // MFMAs of group kq run
-    s16x8 ct[4][DT][2];
+      s16x8 aq[KS], ao[KS];
+      aq[0] = rd<RB>(sQ, 32 * ib + c32, hl);
+      ao[0] = rd<RB>(sdO, 32 * ib + c32, hl);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      ct[0][dt][0] = rd<TB>(sdOT, 32 * dt + c32, hl);
-      ct[0][dt][1] = rd<TB>(sQT, 32 * dt + c32, hl);
-    }
-    PdS cur = elem(0);
-#pragma unroll
-    for (int kq = 0; kq < 4; ++kq) {
-      if (kq + 1 < 4) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          ct[kq + 1][dt][0] = rd<TB>(sdOT, 32 * dt + c32, 2 * (kq + 1) + hl);
-          ct[kq + 1][dt][1] = rd<TB>(sQT, 32 * dt + c32, 2 * (kq + 1) + hl);
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) {
+          aq[ks + 1] = rd<RB>(sQ, 32 * ib + c32, 2 * (ks + 1) + hl);
+          ao[ks + 1] = rd<RB>(sdO, 32 * ib + c32, 2 * (ks + 1) + hl);
         }
+        S = M::mma(aq[ks], kB[ks], S);
+        dP = M::mma(ao[ks], vB[ks], dP);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      auto elem = [&](const int g) {  // group g: registers 8g .. 8g+7
+        f32x16 pv, dv;
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg) {
+          const int il = 32 * ib + 8 * (2 * g + rg) + 4 * hl;
+          const float4 l4 = *(const float4 *)(sNl + il);
+          const float4 d4 = *(const float4 *)(sDv + il);
+          const float nl[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int e = 8 * g + 4 * rg + u;
+            float pe = __builtin_amdgcn_exp2f(fmaf(S[e], c, nl[u]));
+            if (!FULL) {
+              const int r = i0 + il + u;
+              pe = (uint32_t)(r - imin) < (uint32_t)(p.nq - imin) ? pe : 0.f;
+            }
+            pv[4 * rg + u] = pe;
+            dv[4 * rg + u] = pe * (dP[e] - dd[u]);
+          }
+        }
+        PdS r;
+        r.p = M::pack(pv, 0);
+        r.ds = M::pack(dv, 0);
+        return r;
+      };
+      // group 1's operands are read and its P, dS computed while the MFMAs of
+      // group 0 run
+      s16x8 ct[2][DT][2];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        dVt[dt] = M::mma(ct[kq][dt][0], cur.p, dVt[dt]);
-        dKt[dt] = M::mma(ct[kq][dt][1], cur.ds, dKt[dt]);
+        ct[0][dt][0] = rd<TB>(sdOT, 32 * dt + c32, 4 * ib + hl);
+        ct[0][dt][1] = rd<TB>(sQT, 32 * dt + c32, 4 * ib + hl);
       }
-      if (kq + 1 < 4) cur = elem(kq + 1);
-      __builtin_amdgcn_sched_barrier(0);
+      PdS cur = elem(0);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        if (g == 0) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            ct[1][dt][0] = rd<TB>(sdOT, 32 * dt + c32, 4 * ib + 2 + hl);
+            ct[1][dt][1] = rd<TB>(sQT, 32 * dt + c32, 4 * ib + 2 + hl);
+          }
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          dVt[dt] = M::mma(ct[g][dt][0], cur.p, dVt[dt]);
+          dKt[dt] = M::mma(ct[g][dt][1], cur.ds, dKt[dt]);
+        }
+        if (g == 0) cur = elem(1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if (full) {
+      half(0, std::true_type());
+      half(1, std::true_type());
+    } else {
+      half(0, std::false_type());
+      half(1, std::false_type());
     }
   }
   if (!kvalid) return;
@@ -394,10 +402,9 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
     dB[ks] = y;
   }
   const int64_t moff = p.ml_zstride * z + ((int64_t)b * p.Hq + h) * p.nq;
-  float l2 = INFINITY, dd = 0.f;
+  float nl = -INFINITY, dd = 0.f;
   if (valid) {
-    const float lse = P.lse[moff + iw];
-    if (lse > -INFINITY) l2 = lse * kLog2e;
+    nl = P.nl[moff + iw];
     dd = P.Dv[moff + iw];
   }
   const int jlim = valid ? key_prefix(p, kid, qid(iw)) : 0;
@@ -476,7 +483,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
         const int e = e0 + u;
         const int j = j0 + 32 * kb + (e >> 2) * 8 + 4 * hl + (e & 3);
         const bool ok = !diag || j < jlim;
-        const float pe = ok ? __builtin_amdgcn_exp2f(fmaf(S[kb][e], c, -l2)) : 0.f;
+        const float pe = ok ? __builtin_amdgcn_exp2f(fmaf(S[kb][e], c, nl)) : 0.f;
         dv[u] = pe * (dP[kb][e] - dd);
       }
       return M::pack(dv, 0);
@@ -515,11 +522,15 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
     }
 }
 
-// D = <dO, O> per row (16-bit inputs), one wave per row
+// Per query row (16-bit inputs, one wave per row): D = <dO, O>, and the
+// exponent offset nl = -lse log2(e) of p = exp2(s c + nl), -inf for a row
+// with no key (lse = -inf), so that its probabilities come out as 0.
 template <typename T>
 __global__ void __launch_bounds__(256) bwd_prep_kernel(const T *__restrict__ o,
                                                        const T *__restrict__ dout,
-                                                       float *__restrict__ Dv, int64_t rows,
+                                                       const float *__restrict__ lse,
+                                                       float *__restrict__ Dv,
+                                                       float *__restrict__ nl, int64_t rows,
                                                        int d) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -529,7 +540,11 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const T *__restrict__ o,
     acc += (float)o[row * d + c] * (float)dout[row * d + c];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) Dv[row] = acc;
+  if (lane == 0) {
+    Dv[row] = acc;
+    const float x = lse[row];
+    nl[row] = x > -INFINITY ? -x * kLog2e : -INFINITY;
+  }
 }
 
 __global__ void __launch_bounds__(256) zero_kernel(float4 *__restrict__ x, int64_t n4) {
@@ -578,16 +593,16 @@ hipError_t launch_bwd_d(const BwdParams &P, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_bwd_prep(const void *o, const void *dout, float *Dv, int dtype, int64_t rows,
-                           int32_t d, hipStream_t s) {
+hipError_t launch_bwd_prep(const void *o, const void *dout, const float *lse, float *Dv,
+                           float *nl, int dtype, int64_t rows, int32_t d, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((rows + 3) / 4);
   if (dtype == RA_DT_BF16)
     hipLaunchKernelGGL(bwd_prep_kernel<__bf16>, dim3(blocks), dim3(256), 0, s,
-                       (const __bf16 *)o, (const __bf16 *)dout, Dv, rows, d);
+                       (const __bf16 *)o, (const __bf16 *)dout, lse, Dv, nl, rows, d);
   else
     hipLaunchKernelGGL(bwd_prep_kernel<_Float16>, dim3(blocks), dim3(256), 0, s,
-                       (const _Float16 *)o, (const _Float16 *)dout, Dv, rows, d);
+                       (const _Float16 *)o, (const _Float16 *)dout, lse, Dv, nl, rows, d);
   return hipGetLastError();
 }
 
