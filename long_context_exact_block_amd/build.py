@@ -18,6 +18,10 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=" + ARCH,
     # packed fp32 VALU forms are kept out of the generated code on purpose
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the default heuristics put them in AGPRs
+    # and then copy them to and from VGPRs around every loop iteration of the
+    # backward kernels (and spill into AGPRs elsewhere)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

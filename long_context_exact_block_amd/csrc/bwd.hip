@@ -228,8 +228,12 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
     const float *sDv = sNl + kBT;
     const int i0 = (qt0 + f % per) * kBT;
     const int ilast = min(i0 + kBT, p.nq) - 1;
-    if (!wave_keys || imin_w0 > ilast) continue;  // nothing allowed
-    // no mask when every query of the tile is valid and sees every key of the wave
+    // no mask when every query of the tile is valid and sees every key of the
+    // wave.  A tile where the wave sees nothing is not skipped: it runs fully
+    // masked (only the first tiles of a workgroup), which keeps the
+    // accumulators on a single path through the loop.
+    (void)ilast;
+    (void)imin_w0;
     const bool full = i0 + kBT <= p.nq && imax_w <= i0;
 
     // The tile in two halves of 32 queries (ib): S = Q K^T and dP = dO V^T for
@@ -237,18 +241,26 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
     // multiplied), then its two groups of 16 queries (kq = 2 ib + g) into
     // dV^T += dO^T P and dK^T += Q^T dS.  Element e of S is query
     // 32 ib + 8(e/4) + 4 hl + e%4 of the tile, key column jw.
-    // Rows with no key at all have nl = -inf, so p = 0.  Full tiles need no
-    // mask; otherwise row r is allowed for this lane's key iff imin <= r < nq.
+    // The mask is the initial value of S: 0 where row r may see this lane's
+    // key (imin <= r < nq), -inf elsewhere, so that p = exp2(S c + nl) = 0
+    // there; full tiles start from 0.  Rows with no key at all have
+    // nl = -inf, so p = 0 as well.
     struct PdS {
       s16x8 p, ds;
     };
-    auto half = [&](const int ib, auto full_c) {
-      constexpr bool FULL = decltype(full_c)::value;
+    auto half = [&](const int ib) {
       f32x16 S, dP;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        S[e] = 0.f;
-        dP[e] = 0.f;
+      for (int e = 0; e < 16; ++e) dP[e] = 0.f;
+      if (full) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) S[e] = 0.f;
+      } else {
+        const int rl = i0 + 32 * ib + 4 * hl - imin;  // row - imin of element 0
+        const uint32_t span = (uint32_t)(p.nq - imin);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          S[e] = (uint32_t)(rl + 8 * (e >> 2) + (e & 3)) < span ? 0.f : -INFINITY;
       }
       s16x8 aq[KS], ao[KS];
       aq[0] = rd<RB>(sQ, 32 * ib + c32, hl);
@@ -275,11 +287,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int e = 8 * g + 4 * rg + u;
-            float pe = __builtin_amdgcn_exp2f(fmaf(S[e], c, nl[u]));
-            if (!FULL) {
-              const int r = i0 + il + u;
-              pe = (uint32_t)(r - imin) < (uint32_t)(p.nq - imin) ? pe : 0.f;
-            }
+            const float pe = __builtin_amdgcn_exp2f(fmaf(S[e], c, nl[u]));
             pv[4 * rg + u] = pe;
             dv[4 * rg + u] = pe * (dP[e] - dd[u]);
           }
@@ -316,13 +324,8 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    if (full) {
-      half(0, std::true_type());
-      half(1, std::true_type());
-    } else {
-      half(0, std::false_type());
-      half(1, std::false_type());
-    }
+    half(0);
+    half(1);
   }
   if (!kvalid) return;
   // element e of dKt[dt]: d = 32dt + 8(e/4) + 4hl + e%4 of key jw
