@@ -173,7 +173,7 @@ ra_status check_block_bwd(const ra_block_bwd_args *a) {
 }
 
 struct BwdWs {
-  size_t qT, doT, kT, dv, nl, total;
+  size_t qT, doT, kT, nd, nl, total;
 };
 BwdWs block_bwd_ws(const ra_block_bwd_args *a) {
   BwdWs w{};
@@ -187,7 +187,7 @@ BwdWs block_bwd_ws(const ra_block_bwd_args *a) {
   w.qT = take(qbytes);
   w.doT = take(qbytes);
   w.kT = take((size_t)a->B * a->Hkv * a->d * packed_n(a->n_k) * 2);
-  w.dv = take((size_t)a->B * a->Hq * a->n_q * 4);
+  w.nd = take((size_t)a->B * a->Hq * a->n_q * 4);
   w.nl = take((size_t)a->B * a->Hq * a->n_q * 4);
   w.total = off;
   return w;
@@ -807,7 +807,7 @@ ra_status ra_block_bwd(const ra_block_bwd_args *a, void *workspace, size_t works
   const int64_t d = a->d;
   const int64_t qs[3] = {(int64_t)a->Hq * a->n_q * d, (int64_t)a->n_q * d, d};
   const int64_t ks[3] = {(int64_t)a->Hkv * a->n_k * d, (int64_t)a->n_k * d, d};
-  RA_HIP(launch_bwd_prep(a->o, a->dout, a->lse, (float *)(ws + L.dv), (float *)(ws + L.nl),
+  RA_HIP(launch_bwd_prep(a->o, a->dout, a->lse, (float *)(ws + L.nd), (float *)(ws + L.nl),
                          a->dtype, (int64_t)a->B * a->Hq * a->n_q, a->d, s), "bwd prep");
   RA_HIP(launch_pack_v(a->q, ws + L.qT, 2, (int64_t)a->B * a->Hq, a->Hq, a->n_q, d, qs[0], qs[1],
                        qs[2], s), "pack q");
@@ -848,7 +848,7 @@ ra_status ra_block_bwd(const ra_block_bwd_args *a, void *workspace, size_t works
   P.doT = ws + L.doT;
   P.kT = ws + L.kT;
   P.nl = (const float *)(ws + L.nl);
-  P.Dv = (const float *)(ws + L.dv);
+  P.nD = (const float *)(ws + L.nd);
   P.dq = a->dq;
   P.dk = a->dk;
   P.dv = a->dv;
@@ -935,7 +935,7 @@ ra_status ra_ring_bwd(const ra_ring_bwd_args *a, void *workspace, size_t workspa
   P.qT_zstride = (int64_t)a->B * a->Hq * d * n_pad;
   P.kT_zstride = (int64_t)a->B * a->Hkv * d * n_pad;
   P.nl = (const float *)(ws + L.nl);
-  P.Dv = (const float *)(ws + L.D);
+  P.nD = (const float *)(ws + L.D);
   P.dq = dq;
   P.dk = dk;
   P.dv = dv;

@@ -121,7 +121,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
   constexpr int TT = D * TB;         // bytes of a packed tile
   constexpr size_t ST = dkdv_stage_bytes<D>();
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  // stage layout: sQ | sdO | sQT | sdOT | nl[64] | D[64]
+  // stage layout: sQ | sdO | sQT | sdOT | nl[64] | -D[64]
 
   // workgroup -> (key tile, problem, batch, K/V head); key tile slowest so the
   // heaviest causal tiles (most queries after them) start first
@@ -150,14 +150,12 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
   const int jw = j0w + c32;
   const bool kvalid = jw < p.nk;
   const bool wave_keys = j0w < p.nk;
-  const int64_t kfirst = wave_keys ? kid(j0w) : INT64_MAX;
   const int64_t klast = wave_keys ? kid(min(j0w + 31, p.nk - 1)) : INT64_MAX;
   // First local query row that may see this lane's key (ids increase with the
-  // row), and the same for the wave's first and last key: rows before imin_w0
-  // see no key of the wave, rows from imax_w on see all of them.  A lane past
-  // the block end keeps 0: its column is never stored.
+  // row), and the same for the wave's last key: rows from imax_w on see every
+  // key of the wave.  A lane past the block end keeps 0: its column is never
+  // stored.
   const int imin = (p.causal && kvalid) ? first_query(qid, p.nq, kid(jw)) : 0;
-  const int imin_w0 = (p.causal && wave_keys) ? first_query(qid, p.nq, kfirst) : 0;
   const int imax_w = (p.causal && wave_keys) ? first_query(qid, p.nq, klast) : 0;
 
   // B operands of S = Q K^T and dP = dO V^T: K^T, V^T columns = this lane's key row
@@ -210,57 +208,55 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
       const int64_t mbytes = (int64_t)p.nq * 4;
       dma4b(rsrc(P.nl + moff, mbytes), (lds_void *)(st + 2 * TQ + 2 * TT), lane * 4,
             qt * kBT * 4);
-      dma4b(rsrc(P.Dv + moff, mbytes), (lds_void *)(st + 2 * TQ + 2 * TT + kBT * 4), lane * 4,
+      dma4b(rsrc(P.nD + moff, mbytes), (lds_void *)(st + 2 * TQ + 2 * TT + kBT * 4), lane * 4,
             qt * kBT * 4);
     }
   };
 
-  if (nf > 0) issue(0, 0);
-  for (int f = 0; f < nf; ++f) {
-    // tile f has landed (this wave's loads, then everyone's); stage (f+1)&1 was
-    // last read in iteration f-1
+  // Iteration f: tile f has landed (this wave's loads, then everyone's) and
+  // stage (f+1)&1, last read in iteration f-1, takes tile f+1.  FULL: every
+  // query of the tile sees every key of the wave.
+  auto step = [&](const int f, auto full_c) {
+    constexpr bool FULL = decltype(full_c)::value;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     if (f + 1 < nf) issue(f + 1, (f + 1) & 1);
     const char *st = lds + (f & 1) * ST;
     const char *sQ = st, *sdO = st + TQ, *sQT = st + 2 * TQ, *sdOT = st + 2 * TQ + TT;
     const float *sNl = (const float *)(st + 2 * TQ + 2 * TT);
-    const float *sDv = sNl + kBT;
+    const float *sND = sNl + kBT;
     const int i0 = (qt0 + f % per) * kBT;
-    const int ilast = min(i0 + kBT, p.nq) - 1;
-    // no mask when every query of the tile is valid and sees every key of the
-    // wave.  A tile where the wave sees nothing is not skipped: it runs fully
-    // masked (only the first tiles of a workgroup), which keeps the
-    // accumulators on a single path through the loop.
-    (void)ilast;
-    (void)imin_w0;
-    const bool full = i0 + kBT <= p.nq && imax_w <= i0;
 
-    // The tile in two halves of 32 queries (ib): S = Q K^T and dP = dO V^T for
-    // the half (A operands of k-step ks + 1 read from LDS while k-step ks is
-    // multiplied), then its two groups of 16 queries (kq = 2 ib + g) into
+    // The tile in two halves of 32 queries (ib): S = Q K^T and dP - D = dO V^T - D
+    // for the half (A operands of k-step ks + 1 read from LDS while k-step ks
+    // is multiplied), then its two groups of 16 queries (kq = 2 ib + g) into
     // dV^T += dO^T P and dK^T += Q^T dS.  Element e of S is query
     // 32 ib + 8(e/4) + 4 hl + e%4 of the tile, key column jw.
-    // The mask is the initial value of S: 0 where row r may see this lane's
-    // key (imin <= r < nq), -inf elsewhere, so that p = exp2(S c + nl) = 0
-    // there; full tiles start from 0.  Rows with no key at all have
-    // nl = -inf, so p = 0 as well.
+    // The causal mask is the initial value of S: -inf where the row comes
+    // before imin (p = exp2(S c + nl) = 0 there), else 0.  Rows past the end of
+    // the shard need none: their Q and dO rows and packed columns are zero, so
+    // they add nothing.  Rows with no key at all have nl = -inf, so p = 0.
     struct PdS {
       s16x8 p, ds;
     };
     auto half = [&](const int ib) {
+      // dP starts at -D of its row, so the product leaves dP - D
       f32x16 S, dP;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) dP[e] = 0.f;
-      if (full) {
+      for (int rg = 0; rg < 4; ++rg) {
+        const float4 d4 = *(const float4 *)(sND + 32 * ib + 8 * rg + 4 * hl);
+        dP[4 * rg + 0] = d4.x;
+        dP[4 * rg + 1] = d4.y;
+        dP[4 * rg + 2] = d4.z;
+        dP[4 * rg + 3] = d4.w;
+      }
+      if (FULL) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) S[e] = 0.f;
       } else {
-        const int rl = i0 + 32 * ib + 4 * hl - imin;  // row - imin of element 0
-        const uint32_t span = (uint32_t)(p.nq - imin);
+        const int lo = imin - (i0 + 32 * ib + 4 * hl);  // first allowed element row
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          S[e] = (uint32_t)(rl + 8 * (e >> 2) + (e & 3)) < span ? 0.f : -INFINITY;
+        for (int e = 0; e < 16; ++e) S[e] = 8 * (e >> 2) + (e & 3) >= lo ? 0.f : -INFINITY;
       }
       s16x8 aq[KS], ao[KS];
       aq[0] = rd<RB>(sQ, 32 * ib + c32, hl);
@@ -281,15 +277,13 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
         for (int rg = 0; rg < 2; ++rg) {
           const int il = 32 * ib + 8 * (2 * g + rg) + 4 * hl;
           const float4 l4 = *(const float4 *)(sNl + il);
-          const float4 d4 = *(const float4 *)(sDv + il);
           const float nl[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int e = 8 * g + 4 * rg + u;
             const float pe = __builtin_amdgcn_exp2f(fmaf(S[e], c, nl[u]));
             pv[4 * rg + u] = pe;
-            dv[4 * rg + u] = pe * (dP[e] - dd[u]);
+            dv[4 * rg + u] = pe * dP[e];
           }
         }
         PdS r;
@@ -326,6 +320,18 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
     };
     half(0);
     half(1);
+  };
+
+  // Per wave the tiles of each query head come as a run of partial tiles (the
+  // causal diagonal; a tile where the wave sees nothing runs fully masked, so
+  // the accumulators stay on one path) and then a run of full ones: two loops
+  // with one body each keep the mask code out of the full tiles.
+  auto tile_full = [&](const int f) { return (qt0 + f % per) * kBT >= imax_w; };
+  if (nf > 0) issue(0, 0);
+  int f = 0;
+  while (f < nf) {
+    for (; f < nf && !tile_full(f); ++f) step(f, std::false_type());
+    for (; f < nf && tile_full(f); ++f) step(f, std::true_type());
   }
   if (!kvalid) return;
   // element e of dKt[dt]: d = 32dt + 8(e/4) + 4hl + e%4 of key jw
@@ -405,10 +411,10 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
     dB[ks] = y;
   }
   const int64_t moff = p.ml_zstride * z + ((int64_t)b * p.Hq + h) * p.nq;
-  float nl = -INFINITY, dd = 0.f;
+  float nl = -INFINITY, nd = 0.f;
   if (valid) {
     nl = P.nl[moff + iw];
-    dd = P.Dv[moff + iw];
+    nd = P.nD[moff + iw];
   }
   const int jlim = valid ? key_prefix(p, kid, qid(iw)) : 0;
   const int iw_last = min(iw0 + 31, p.nq - 1), i_wg_last = min(qt * 128 + 127, p.nq - 1);
@@ -435,23 +441,32 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) dQt[dt][e] = 0.f;
 
-  if (ntiles > 0) issue(0, 0);
-  for (int t = 0; t < ntiles; ++t) {
+  // Iteration t: tile t has landed, stage (t+1)&1 takes tile t+1.  MODE 2: a
+  // full tile (every key allowed for every query of the wave), 1: a diagonal
+  // or ragged one, whose mask is the initial value of S^T (-inf for keys at or
+  // past jlim, which includes keys past the block end), 0: nothing for this
+  // wave, loads only.
+  auto step = [&](const int t, auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
-    if (t >= ntiles_w) continue;
+    if (MODE == 0) return;
     const char *st = lds + (t & 1) * ST;
     const char *sK = st, *sV = st + TQ, *sKT = st + 2 * TQ;
     const int j0 = t * kBT;
-    // S^T = K Q^T and dP^T = V dO^T, A operands one k-step ahead
+    // S^T = K Q^T and dP^T = V dO^T, A operands one k-step ahead; dP^T starts
+    // at -D of this lane's row, so the product leaves dP - D.  Element e of
+    // S^T[kb] is key j0 + 32kb + 8(e/4) + 4hl + e%4 of this lane's query.
     f32x16 S[2], dP[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        S[kb][e] = 0.f;
-        dP[kb][e] = 0.f;
+        S[kb][e] = MODE == 2 || j0 + 32 * kb + 8 * (e >> 2) + 4 * hl + (e & 3) < jlim
+                       ? 0.f
+                       : -INFINITY;
+        dP[kb][e] = nd;
       }
     s16x8 ak[KS][2], av[KS][2];
 #pragma unroll
@@ -475,19 +490,15 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    const bool diag = t >= nfull_w || !valid;
-    // group kq (16 keys: half kq/2, registers 8(kq%2) .. +7): dS^T packed.
-    // Element e of S^T[kb] is key j0 + 32kb + 8(e/4) + 4hl + e%4 of this lane's query.
+    // group kq (16 keys: half kq/2, registers 8(kq%2) .. +7): dS^T packed
     auto elem = [&](int kq) {
       const int kb = kq >> 1, e0 = 8 * (kq & 1);
       f32x16 dv;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int e = e0 + u;
-        const int j = j0 + 32 * kb + (e >> 2) * 8 + 4 * hl + (e & 3);
-        const bool ok = !diag || j < jlim;
-        const float pe = ok ? __builtin_amdgcn_exp2f(fmaf(S[kb][e], c, nl)) : 0.f;
-        dv[u] = pe * (dP[kb][e] - dd);
+        const float pe = __builtin_amdgcn_exp2f(fmaf(S[kb][e], c, nl));
+        dv[u] = pe * dP[kb][e];
       }
       return M::pack(dv, 0);
     };
@@ -508,7 +519,16 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
       if (kq + 1 < 4) cur = elem(kq + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
+  // the wave's tiles come as full ones, then diagonal / ragged ones, then
+  // ones it has nothing in: one loop per kind keeps the mask code out of the
+  // full tiles
+  if (ntiles > 0) issue(0, 0);
+  const int nfull = min(nfull_w, ntiles_w);
+  int t = 0;
+  for (; t < nfull; ++t) step(t, std::integral_constant<int, 2>());
+  for (; t < ntiles_w; ++t) step(t, std::integral_constant<int, 1>());
+  for (; t < ntiles; ++t) step(t, std::integral_constant<int, 0>());
   if (!valid) return;
   float *dq = P.dq + P.dq_zstride * z + (((int64_t)b * p.Hq + h) * p.nq + iw) * D;
 #pragma unroll
@@ -525,14 +545,15 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
     }
 }
 
-// Per query row (16-bit inputs, one wave per row): D = <dO, O>, and the
+// Per query row (16-bit inputs, one wave per row): nD = -<dO, O> (the
+// starting value of the dP accumulators, which then hold dP - D), and the
 // exponent offset nl = -lse log2(e) of p = exp2(s c + nl), -inf for a row
 // with no key (lse = -inf), so that its probabilities come out as 0.
 template <typename T>
 __global__ void __launch_bounds__(256) bwd_prep_kernel(const T *__restrict__ o,
                                                        const T *__restrict__ dout,
                                                        const float *__restrict__ lse,
-                                                       float *__restrict__ Dv,
+                                                       float *__restrict__ nD,
                                                        float *__restrict__ nl, int64_t rows,
                                                        int d) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -544,7 +565,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const T *__restrict__ o,
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
   if (lane == 0) {
-    Dv[row] = acc;
+    nD[row] = -acc;
     const float x = lse[row];
     nl[row] = x > -INFINITY ? -x * kLog2e : -INFINITY;
   }
@@ -596,16 +617,16 @@ hipError_t launch_bwd_d(const BwdParams &P, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_bwd_prep(const void *o, const void *dout, const float *lse, float *Dv,
+hipError_t launch_bwd_prep(const void *o, const void *dout, const float *lse, float *nD,
                            float *nl, int dtype, int64_t rows, int32_t d, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((rows + 3) / 4);
   if (dtype == RA_DT_BF16)
     hipLaunchKernelGGL(bwd_prep_kernel<__bf16>, dim3(blocks), dim3(256), 0, s,
-                       (const __bf16 *)o, (const __bf16 *)dout, lse, Dv, nl, rows, d);
+                       (const __bf16 *)o, (const __bf16 *)dout, lse, nD, nl, rows, d);
   else
     hipLaunchKernelGGL(bwd_prep_kernel<_Float16>, dim3(blocks), dim3(256), 0, s,
-                       (const _Float16 *)o, (const _Float16 *)dout, lse, Dv, nl, rows, d);
+                       (const _Float16 *)o, (const _Float16 *)dout, lse, nD, nl, rows, d);
   return hipGetLastError();
 }
 

@@ -112,8 +112,8 @@ hipError_t launch_layout_move(bool gather, const void *src, void *dst, const int
 //   dout        like q (same strides)
 //   qT, doT     packed (ra_pack_v layout) per query problem z: q_zstride_p
 //   kT          packed per K/V block (block index as for k): kT_zstride
-//   nl, Dv      fp32 per query row: + z*ml_zstride, [b][h][i]; nl = -lse log2(e)
-//               (-inf for a row with no key), D = <dO, O>, both from launch_bwd_prep
+//   nl, nD      fp32 per query row: + z*ml_zstride, [b][h][i]; nl = -lse log2(e)
+//               (-inf for a row with no key), nD = -<dO, O>, both from launch_bwd_prep
 //   dq          fp32 accumulator like q rows: + z*dq_zstride, [b][h][i][d]
 //   dk, dv      fp32 accumulators per K/V block: + kv*dk_zstride, [b][kvh][j][d]
 // Each problem z adds its contributions; within a launch no two problems
@@ -123,11 +123,11 @@ struct BwdParams {
   const void *dout;
   const void *qT, *doT, *kT;
   int64_t qT_zstride, kT_zstride;
-  const float *nl, *Dv;
+  const float *nl, *nD;
   float *dq, *dk, *dv;
   int64_t dq_zstride, dk_zstride;
 };
-hipError_t launch_bwd_prep(const void *o, const void *dout, const float *lse, float *Dv,
+hipError_t launch_bwd_prep(const void *o, const void *dout, const float *lse, float *nD,
                            float *nl, int dtype, int64_t rows, int32_t d, hipStream_t s);
 hipError_t launch_bwd(const BwdParams &p, int dtype, hipStream_t s);
 hipError_t launch_zero(float *x, int64_t n, hipStream_t s);  // n % 4 == 0
