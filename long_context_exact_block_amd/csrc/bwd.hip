@@ -69,23 +69,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t
   return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, (int)(uint32_t)lim, kBufWord3B);
 }
 
-// One 64-row tile of rows x ROW_BYTES into a swizzled LDS tile by the 4
+// A tile of ROWS rows x ROW_BYTES goes into a swizzled LDS tile by the 4
 // waves: wave-load u covers rows (wave + 4u) * RPI .. + RPI - 1; lane l lands
 // at LDS chunk l % CPR of its row and fetches the chunk that belongs there
-// (the swizzle is an involution).  soff: byte offset of the tile's first row.
+// (the swizzle is an involution).  The swizzle of a row depends on its
+// position in a 16-row (or 32-row) period only, which wave-load u shifts by a
+// multiple of it, so every wave-load uses the per-lane offset of u = 0
+// (tile_voff, computed once) plus u * 4 * RPI rows in the scalar offset.
+// row_bytes: source row pitch (bytes); soff: offset of the tile's first row.
+template <int ROW_BYTES>
+__device__ __forceinline__ uint32_t tile_voff(uint32_t row_bytes, int wave, int lane) {
+  constexpr int CPR = ROW_BYTES / 16, RPI = 1024 / ROW_BYTES;
+  const int row = wave * RPI + lane / CPR;
+  const int ch = (lane % CPR) ^ swz16<ROW_BYTES>(row);
+  return (uint32_t)row * row_bytes + (uint32_t)ch * 16;
+}
 template <int ROW_BYTES, int ROWS>
 __device__ __forceinline__ void load_tile(char *dst, __amdgpu_buffer_rsrc_t r, uint32_t row_bytes,
-                                          uint32_t soff, int wave, int lane) {
-  constexpr int CPR = ROW_BYTES / 16, RPI = 1024 / ROW_BYTES;
+                                          uint32_t voff, uint32_t soff, int wave) {
+  constexpr int RPI = 1024 / ROW_BYTES;
   constexpr int NU = ROWS * ROW_BYTES / 1024 / kBW;
   static_assert(NU * kBW * 1024 == ROWS * ROW_BYTES, "tile must split over the waves");
+  static_assert(kBW * RPI % 16 == 0, "wave-loads must shift rows by whole swizzle periods");
 #pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int idx = wave + kBW * u;
-    const int row = idx * RPI + lane / CPR;
-    const int ch = (lane % CPR) ^ swz16<ROW_BYTES>(row);
-    dma16b(r, (lds_void *)(dst + idx * 1024), row * row_bytes + ch * 16, soff);
-  }
+  for (int u = 0; u < NU; ++u)
+    dma16b(r, (lds_void *)(dst + (wave + kBW * u) * 1024), voff,
+           soff + (uint32_t)(kBW * RPI * u) * row_bytes);
 }
 
 // first local query index i with qid(i) >= kg (nq if none); ids increase with i
@@ -180,52 +189,73 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
     }
 
   // query tiles that can see any key of this workgroup, for every query head
-  // of the K/V head: iteration f = hq * per + (qt - qt0)
+  // of the K/V head: iteration f = hq * per + (qt - qt0), heads outermost
   const int64_t kwg = kid(min(kt * 128, p.nk - 1));
   const int qt0 = (p.causal ? first_query(qid, p.nq, kwg) : 0) / kBT;
   const int per = (p.nq + kBT - 1) / kBT - qt0;
   const int nf = per > 0 ? G * per : 0;
-  const int nq_pad = (p.nq + 63) / 64 * 64;
+  const int nqt = (p.nq + kBT - 1) / kBT;
+  const int nq_pad = nqt * kBT;
   const uint32_t rowb = (uint32_t)p.qs_t * 2;
-  auto issue = [&](int f, int stage) {
-    const int hq = f / per, qt = qt0 + f % per;
+  const uint32_t vo_r = tile_voff<RB>(rowb, wave, lane), vo_t = tile_voff<TB>(TB, wave, lane);
+  // Loads walk the tiles (head hq, query tile qt) in iteration order; the
+  // buffer descriptors of a head are built when the walk reaches it.
+  int iss_hq = 0, iss_qt = qt0;
+  __amdgpu_buffer_rsrc_t r_q, r_do, r_qT, r_doT, r_nl, r_nD;
+  auto set_head = [&](const int hq) {
     const int h = kvh * G + hq;
     const int64_t qoff = p.q_zstride * z + b * p.qs_b + h * p.qs_h;
     const int64_t rows_bytes = (int64_t)p.nq * rowb;
-    char *st = lds + stage * ST;
-    load_tile<RB, kBT>(st, rsrc((const short *)p.q + qoff, rows_bytes), rowb, qt * kBT * rowb,
-                       wave, lane);
-    load_tile<RB, kBT>(st + TQ, rsrc((const short *)P.dout + qoff, rows_bytes), rowb,
-                       qt * kBT * rowb, wave, lane);
+    r_q = rsrc((const short *)p.q + qoff, rows_bytes);
+    r_do = rsrc((const short *)P.dout + qoff, rows_bytes);
     const int64_t toff = P.qT_zstride * z + ((int64_t)b * p.Hq + h) * D * nq_pad;
     const int64_t tbytes = (int64_t)D * nq_pad * 2;
-    load_tile<TB, D>(st + 2 * TQ, rsrc((const short *)P.qT + toff, tbytes), TB, qt * TT, wave,
-                     lane);
-    load_tile<TB, D>(st + 2 * TQ + TT, rsrc((const short *)P.doT + toff, tbytes), TB, qt * TT,
-                     wave, lane);
-    if (wave == 0) {
-      const int64_t moff = p.ml_zstride * z + ((int64_t)b * p.Hq + h) * p.nq;
-      const int64_t mbytes = (int64_t)p.nq * 4;
-      dma4b(rsrc(P.nl + moff, mbytes), (lds_void *)(st + 2 * TQ + 2 * TT), lane * 4,
-            qt * kBT * 4);
-      dma4b(rsrc(P.nD + moff, mbytes), (lds_void *)(st + 2 * TQ + 2 * TT + kBT * 4), lane * 4,
-            qt * kBT * 4);
+    r_qT = rsrc((const short *)P.qT + toff, tbytes);
+    r_doT = rsrc((const short *)P.doT + toff, tbytes);
+    const int64_t moff = p.ml_zstride * z + ((int64_t)b * p.Hq + h) * p.nq;
+    r_nl = rsrc(P.nl + moff, (int64_t)p.nq * 4);
+    r_nD = rsrc(P.nD + moff, (int64_t)p.nq * 4);
+  };
+  set_head(0);
+  // The next tile of the walk into `stage`, in three parts issued at three
+  // points of an iteration: a burst of all of a tile's loads from the four
+  // waves fills the load queue and stalls their instruction issue.
+  auto issue = [&](const int stage, const int part) {
+    char *st = lds + stage * ST;
+    const uint32_t so = (uint32_t)iss_qt * kBT * rowb, sot = (uint32_t)iss_qt * TT;
+    if (part == 0) {
+      load_tile<RB, kBT>(st, r_q, rowb, vo_r, so, wave);
+      load_tile<RB, kBT>(st + TQ, r_do, rowb, vo_r, so, wave);
+    } else if (part == 1) {
+      load_tile<TB, D>(st + 2 * TQ, r_qT, TB, vo_t, sot, wave);
+    } else {
+      load_tile<TB, D>(st + 2 * TQ + TT, r_doT, TB, vo_t, sot, wave);
+      if (wave == 0) {
+        dma4b(r_nl, (lds_void *)(st + 2 * TQ + 2 * TT), lane * 4, (uint32_t)iss_qt * kBT * 4);
+        dma4b(r_nD, (lds_void *)(st + 2 * TQ + 2 * TT + kBT * 4), lane * 4,
+              (uint32_t)iss_qt * kBT * 4);
+      }
+      if (++iss_qt == nqt) {
+        iss_qt = qt0;
+        if (++iss_hq < G) set_head(iss_hq);
+      }
     }
   };
 
   // Iteration f: tile f has landed (this wave's loads, then everyone's) and
   // stage (f+1)&1, last read in iteration f-1, takes tile f+1.  FULL: every
   // query of the tile sees every key of the wave.
-  auto step = [&](const int f, auto full_c) {
+  auto step = [&](const int f, const int qt, auto full_c) {
     constexpr bool FULL = decltype(full_c)::value;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (f + 1 < nf) issue(f + 1, (f + 1) & 1);
+    const bool more = f + 1 < nf;
+    if (more) issue((f + 1) & 1, 0);
     const char *st = lds + (f & 1) * ST;
     const char *sQ = st, *sdO = st + TQ, *sQT = st + 2 * TQ, *sdOT = st + 2 * TQ + TT;
     const float *sNl = (const float *)(st + 2 * TQ + 2 * TT);
     const float *sND = sNl + kBT;
-    const int i0 = (qt0 + f % per) * kBT;
+    const int i0 = qt * kBT;
 
     // The tile in two halves of 32 queries (ib): S = Q K^T and dP - D = dO V^T - D
     // for the half (A operands of k-step ks + 1 read from LDS while k-step ks
@@ -239,16 +269,38 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
     struct PdS {
       s16x8 p, ds;
     };
+    // One wave per SIMD: nothing else hides the LDS latency, so every LDS
+    // operand is read well ahead of its MFMA.  A operands of S / dP run KA
+    // k-steps ahead; the first KA of half 1, its -D and its nl are read during
+    // the dV/dK products of half 0; a half's first dO^T / Q^T group during its
+    // own last k-steps.
+    constexpr int KA = 3;
+    s16x8 aq[2][KS], ao[2][KS];
+    float4 nd4[2][4], l4[2][4];
+    auto read_a = [&](const int ib, const int ks) {
+      aq[ib][ks] = rd<RB>(sQ, 32 * ib + c32, 2 * ks + hl);
+      ao[ib][ks] = rd<RB>(sdO, 32 * ib + c32, 2 * ks + hl);
+    };
+    auto read_nd = [&](const int ib) {  // -D and nl of the half's rows
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        nd4[ib][rg] = *(const float4 *)(sND + 32 * ib + 8 * rg + 4 * hl);
+        l4[ib][rg] = *(const float4 *)(sNl + 32 * ib + 8 * rg + 4 * hl);
+      }
+    };
+    read_nd(0);
+#pragma unroll
+    for (int ks = 0; ks < KA; ++ks) read_a(0, ks);
+
     auto half = [&](const int ib) {
       // dP starts at -D of its row, so the product leaves dP - D
       f32x16 S, dP;
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const float4 d4 = *(const float4 *)(sND + 32 * ib + 8 * rg + 4 * hl);
-        dP[4 * rg + 0] = d4.x;
-        dP[4 * rg + 1] = d4.y;
-        dP[4 * rg + 2] = d4.z;
-        dP[4 * rg + 3] = d4.w;
+        dP[4 * rg + 0] = nd4[ib][rg].x;
+        dP[4 * rg + 1] = nd4[ib][rg].y;
+        dP[4 * rg + 2] = nd4[ib][rg].z;
+        dP[4 * rg + 3] = nd4[ib][rg].w;
       }
       if (FULL) {
 #pragma unroll
@@ -258,26 +310,29 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) S[e] = 8 * (e >> 2) + (e & 3) >= lo ? 0.f : -INFINITY;
       }
-      s16x8 aq[KS], ao[KS];
-      aq[0] = rd<RB>(sQ, 32 * ib + c32, hl);
-      ao[0] = rd<RB>(sdO, 32 * ib + c32, hl);
+      s16x8 ct[2][DT][2];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) {
-          aq[ks + 1] = rd<RB>(sQ, 32 * ib + c32, 2 * (ks + 1) + hl);
-          ao[ks + 1] = rd<RB>(sdO, 32 * ib + c32, 2 * (ks + 1) + hl);
+        if (ks + KA < KS) {
+          read_a(ib, ks + KA);
+        } else if (ks + KA == KS) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) ct[0][dt][0] = rd<TB>(sdOT, 32 * dt + c32, 4 * ib + hl);
+        } else if (ks + KA == KS + 1) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) ct[0][dt][1] = rd<TB>(sQT, 32 * dt + c32, 4 * ib + hl);
         }
-        S = M::mma(aq[ks], kB[ks], S);
-        dP = M::mma(ao[ks], vB[ks], dP);
+        S = M::mma(aq[ib][ks], kB[ks], S);
+        dP = M::mma(ao[ib][ks], vB[ks], dP);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (ib == 0 && more) issue((f + 1) & 1, 1);
       auto elem = [&](const int g) {  // group g: registers 8g .. 8g+7
         f32x16 pv, dv;
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg) {
-          const int il = 32 * ib + 8 * (2 * g + rg) + 4 * hl;
-          const float4 l4 = *(const float4 *)(sNl + il);
-          const float nl[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float4 x = l4[ib][2 * g + rg];
+          const float nl[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int e = 8 * g + 4 * rg + u;
@@ -292,13 +347,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
         return r;
       };
       // group 1's operands are read and its P, dS computed while the MFMAs of
-      // group 0 run
-      s16x8 ct[2][DT][2];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        ct[0][dt][0] = rd<TB>(sdOT, 32 * dt + c32, 4 * ib + hl);
-        ct[0][dt][1] = rd<TB>(sQT, 32 * dt + c32, 4 * ib + hl);
-      }
+      // group 0 run; during group 1's, the first operands of half 1
       PdS cur = elem(0);
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
@@ -308,6 +357,10 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
             ct[1][dt][0] = rd<TB>(sdOT, 32 * dt + c32, 4 * ib + 2 + hl);
             ct[1][dt][1] = rd<TB>(sQT, 32 * dt + c32, 4 * ib + 2 + hl);
           }
+        } else if (ib == 0) {
+          read_nd(1);
+#pragma unroll
+          for (int ks = 0; ks < KA; ++ks) read_a(1, ks);
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -319,6 +372,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
       }
     };
     half(0);
+    if (more) issue((f + 1) & 1, 2);
     half(1);
   };
 
@@ -326,12 +380,19 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
   // causal diagonal; a tile where the wave sees nothing runs fully masked, so
   // the accumulators stay on one path) and then a run of full ones: two loops
   // with one body each keep the mask code out of the full tiles.
-  auto tile_full = [&](const int f) { return (qt0 + f % per) * kBT >= imax_w; };
-  if (nf > 0) issue(0, 0);
-  int f = 0;
+  if (nf > 0) {
+    issue(0, 0);
+    issue(0, 1);
+    issue(0, 2);
+  }
+  int f = 0, qt = qt0;  // qt: query tile of iteration f
+  auto next = [&]() {
+    ++f;
+    if (++qt == nqt) qt = qt0;
+  };
   while (f < nf) {
-    for (; f < nf && !tile_full(f); ++f) step(f, std::false_type());
-    for (; f < nf && tile_full(f); ++f) step(f, std::true_type());
+    for (; f < nf && qt * kBT < imax_w; next()) step(f, qt, std::false_type());
+    for (; f < nf && qt * kBT >= imax_w; next()) step(f, qt, std::true_type());
   }
   if (!kvalid) return;
   // element e of dKt[dt]: d = 32dt + 8(e/4) + 4hl + e%4 of key jw
@@ -423,16 +484,22 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
   const int ntiles_w = wave_rows ? (key_prefix(p, kid, qid(iw_last)) + kBT - 1) / kBT : 0;
   const int nfull_w = wave_rows ? key_prefix(p, kid, qid(iw0)) / kBT : 0;
 
-  const uint32_t rowb = (uint32_t)p.ks_t * 2;
+  const uint32_t rowb = (uint32_t)p.ks_t * 2, vrowb = (uint32_t)p.vs_t * 2;
   const int64_t kbytes = (int64_t)p.nk * rowb;
-  const auto kr = rsrc(kp, kbytes), vr = rsrc(vp, (int64_t)p.nk * p.vs_t * 2),
+  const auto kr = rsrc(kp, kbytes), vr = rsrc(vp, (int64_t)p.nk * vrowb),
              tr = rsrc(kT, (int64_t)D * nk_pad * 2);
-  auto issue = [&](int t, int stage) {
+  const uint32_t vo_k = tile_voff<RB>(rowb, wave, lane), vo_v = tile_voff<RB>(vrowb, wave, lane),
+                 vo_t = tile_voff<TB>(TB, wave, lane);
+  // tile t into `stage`, in three parts issued at three points of an
+  // iteration (a burst of a whole tile's loads stalls instruction issue)
+  auto issue = [&](int t, int stage, int part) {
     char *st = lds + stage * ST;
-    load_tile<RB, kBT>(st, kr, rowb, t * kBT * rowb, wave, lane);
-    load_tile<RB, kBT>(st + TQ, vr, (uint32_t)p.vs_t * 2, t * kBT * (uint32_t)p.vs_t * 2, wave,
-                       lane);
-    load_tile<TB, D>(st + 2 * TQ, tr, TB, t * TT, wave, lane);
+    if (part == 0)
+      load_tile<RB, kBT>(st, kr, rowb, vo_k, (uint32_t)t * kBT * rowb, wave);
+    else if (part == 1)
+      load_tile<RB, kBT>(st + TQ, vr, vrowb, vo_v, (uint32_t)t * kBT * vrowb, wave);
+    else
+      load_tile<TB, D>(st + 2 * TQ, tr, TB, vo_t, (uint32_t)t * TT, wave);
   };
 
   f32x16 dQt[DT];
@@ -450,8 +517,15 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
     constexpr int MODE = decltype(mode_c)::value;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
-    if (MODE == 0) return;
+    const bool more = t + 1 < ntiles;
+    if (more) issue(t + 1, (t + 1) & 1, 0);
+    if (MODE == 0) {
+      if (more) {
+        issue(t + 1, (t + 1) & 1, 1);
+        issue(t + 1, (t + 1) & 1, 2);
+      }
+      return;
+    }
     const char *st = lds + (t & 1) * ST;
     const char *sK = st, *sV = st + TQ, *sKT = st + 2 * TQ;
     const int j0 = t * kBT;
@@ -490,6 +564,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (more) issue(t + 1, (t + 1) & 1, 1);
     // group kq (16 keys: half kq/2, registers 8(kq%2) .. +7): dS^T packed
     auto elem = [&](int kq) {
       const int kb = kq >> 1, e0 = 8 * (kq & 1);
@@ -517,13 +592,18 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) dQt[dt] = M::mma(ct[kq][dt], cur, dQt[dt]);
       if (kq + 1 < 4) cur = elem(kq + 1);
+      if (kq == 1 && more) issue(t + 1, (t + 1) & 1, 2);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   // the wave's tiles come as full ones, then diagonal / ragged ones, then
   // ones it has nothing in: one loop per kind keeps the mask code out of the
   // full tiles
-  if (ntiles > 0) issue(0, 0);
+  if (ntiles > 0) {
+    issue(0, 0, 0);
+    issue(0, 0, 1);
+    issue(0, 0, 2);
+  }
   const int nfull = min(nfull_w, ntiles_w);
   int t = 0;
   for (; t < nfull; ++t) step(t, std::integral_constant<int, 2>());
