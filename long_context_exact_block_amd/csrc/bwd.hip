@@ -19,9 +19,13 @@
 //    lane owns a key column; dV^T += dO^T P and dK^T += Q^T dS then read
 //    dO^T and Q^T from the packed transposed layout (the one V uses in the
 //    forward), whose key order matches how P and dS sit in the registers.
-//  * bwd_dq_kernel (a workgroup owns 128 queries, a wave 32; loops over
-//    64-key tiles): S^T = K Q^T and dP^T = V dO^T as in the forward (a lane
-//    owns a query), dQ^T += K^T dS^T with K^T packed.
+//  * bwd_dq_kernel (a workgroup owns 256 queries, a wave 32, two waves per
+//    SIMD; loops over 64-key tiles): S^T = K Q^T and dP^T = V dO^T as in the
+//    forward (a lane owns a query), dQ^T += K^T dS^T with K^T packed.
+// Loaded bytes per MFMA are what these kernels pay for most (the loads
+// stream into LDS next to the operand reads), so a workgroup covers as many
+// rows as its registers allow: dK/dV's per-wave state (K, V rows and two
+// accumulators) needs one wave per SIMD; dQ's fits two.
 // Each workgroup owns its output tile, so the fp32 accumulation is plain
 // read-add-write: no atomics, deterministic.
 #include <cfloat>
@@ -35,7 +39,8 @@ namespace {
 
 using namespace attn;
 
-constexpr int kBW = 4;       // waves per workgroup (one per SIMD: up to 512 registers)
+constexpr int kBW = 4;       // dK/dV waves per workgroup (one per SIMD: up to 512 registers)
+constexpr int kQW = 8;       // dQ waves per workgroup (two per SIMD, 256 registers each)
 constexpr int kBT = 64;      // rows of a staged tile (queries in dkdv, keys in dq)
 
 template <int ROW_BYTES>
@@ -84,17 +89,17 @@ __device__ __forceinline__ uint32_t tile_voff(uint32_t row_bytes, int wave, int 
   const int ch = (lane % CPR) ^ swz16<ROW_BYTES>(row);
   return (uint32_t)row * row_bytes + (uint32_t)ch * 16;
 }
-template <int ROW_BYTES, int ROWS>
+template <int ROW_BYTES, int ROWS, int NW>
 __device__ __forceinline__ void load_tile(char *dst, __amdgpu_buffer_rsrc_t r, uint32_t row_bytes,
                                           uint32_t voff, uint32_t soff, int wave) {
   constexpr int RPI = 1024 / ROW_BYTES;
-  constexpr int NU = ROWS * ROW_BYTES / 1024 / kBW;
-  static_assert(NU * kBW * 1024 == ROWS * ROW_BYTES, "tile must split over the waves");
-  static_assert(kBW * RPI % 16 == 0, "wave-loads must shift rows by whole swizzle periods");
+  constexpr int NU = ROWS * ROW_BYTES / 1024 / NW;
+  static_assert(NU * NW * 1024 == ROWS * ROW_BYTES, "tile must split over the waves");
+  static_assert(NW * RPI % 16 == 0, "wave-loads must shift rows by whole swizzle periods");
 #pragma unroll
   for (int u = 0; u < NU; ++u)
-    dma16b(r, (lds_void *)(dst + (wave + kBW * u) * 1024), voff,
-           soff + (uint32_t)(kBW * RPI * u) * row_bytes);
+    dma16b(r, (lds_void *)(dst + (wave + NW * u) * 1024), voff,
+           soff + (uint32_t)(NW * RPI * u) * row_bytes);
 }
 
 // first local query index i with qid(i) >= kg (nq if none); ids increase with i
@@ -224,12 +229,12 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
     char *st = lds + stage * ST;
     const uint32_t so = (uint32_t)iss_qt * kBT * rowb, sot = (uint32_t)iss_qt * TT;
     if (part == 0) {
-      load_tile<RB, kBT>(st, r_q, rowb, vo_r, so, wave);
-      load_tile<RB, kBT>(st + TQ, r_do, rowb, vo_r, so, wave);
+      load_tile<RB, kBT, kBW>(st, r_q, rowb, vo_r, so, wave);
+      load_tile<RB, kBT, kBW>(st + TQ, r_do, rowb, vo_r, so, wave);
     } else if (part == 1) {
-      load_tile<TB, D>(st + 2 * TQ, r_qT, TB, vo_t, sot, wave);
+      load_tile<TB, D, kBW>(st + 2 * TQ, r_qT, TB, vo_t, sot, wave);
     } else {
-      load_tile<TB, D>(st + 2 * TQ + TT, r_doT, TB, vo_t, sot, wave);
+      load_tile<TB, D, kBW>(st + 2 * TQ + TT, r_doT, TB, vo_t, sot, wave);
       if (wave == 0) {
         dma4b(r_nl, (lds_void *)(st + 2 * TQ + 2 * TT), lane * 4, (uint32_t)iss_qt * kBT * 4);
         dma4b(r_nD, (lds_void *)(st + 2 * TQ + 2 * TT + kBT * 4), lane * 4,
@@ -419,7 +424,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
 }
 
 template <int D, bool BF16>
-__global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
+__global__ void __launch_bounds__(kQW * 64) bwd_dq_kernel(BwdParams P) {
   using M = Mfma16<BF16>;
   const BatchParams &p = P.a;
   constexpr int KS = D / 16, DT = D / 32;
@@ -433,7 +438,8 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
 
   // workgroup -> (query tile, problem, batch, query head); query tile slowest,
   // last tiles (most keys before them) first
-  const int nqt = (p.nq + 127) / 128;
+  constexpr int QWG = kQW * 32;  // queries per workgroup
+  const int nqt = (p.nq + QWG - 1) / QWG;
   const int per_qt = p.nz * p.B * p.Hq;
   int idx = blockIdx.x;
   const int qtr = idx / per_qt;
@@ -456,7 +462,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
   const float c = p.scale * kLog2e;
 
   // this wave's 32 queries and this lane's query
-  const int iw0 = qt * 128 + wave * 32;
+  const int iw0 = qt * QWG + wave * 32;
   const int iw = iw0 + c32;
   const bool valid = iw < p.nq;
   const int64_t qoff = p.q_zstride * z + b * p.qs_b + h * p.qs_h;
@@ -478,7 +484,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
     nd = P.nD[moff + iw];
   }
   const int jlim = valid ? key_prefix(p, kid, qid(iw)) : 0;
-  const int iw_last = min(iw0 + 31, p.nq - 1), i_wg_last = min(qt * 128 + 127, p.nq - 1);
+  const int iw_last = min(iw0 + 31, p.nq - 1), i_wg_last = min(qt * QWG + QWG - 1, p.nq - 1);
   const bool wave_rows = iw0 < p.nq;
   const int ntiles = (key_prefix(p, kid, qid(i_wg_last)) + kBT - 1) / kBT;
   const int ntiles_w = wave_rows ? (key_prefix(p, kid, qid(iw_last)) + kBT - 1) / kBT : 0;
@@ -495,11 +501,11 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dq_kernel(BwdParams P) {
   auto issue = [&](int t, int stage, int part) {
     char *st = lds + stage * ST;
     if (part == 0)
-      load_tile<RB, kBT>(st, kr, rowb, vo_k, (uint32_t)t * kBT * rowb, wave);
+      load_tile<RB, kBT, kQW>(st, kr, rowb, vo_k, (uint32_t)t * kBT * rowb, wave);
     else if (part == 1)
-      load_tile<RB, kBT>(st + TQ, vr, vrowb, vo_v, (uint32_t)t * kBT * vrowb, wave);
+      load_tile<RB, kBT, kQW>(st + TQ, vr, vrowb, vo_v, (uint32_t)t * kBT * vrowb, wave);
     else
-      load_tile<TB, D>(st + 2 * TQ, tr, TB, vo_t, (uint32_t)t * TT, wave);
+      load_tile<TB, D, kQW>(st + 2 * TQ, tr, TB, vo_t, (uint32_t)t * TT, wave);
   };
 
   f32x16 dQt[DT];
@@ -690,8 +696,8 @@ hipError_t launch_bwd_d(const BwdParams &P, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t n2 = groups * p.Hq * ((p.nq + 127) / 128);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, BF16>), dim3((unsigned)n2), dim3(kBW * 64), l2, s, P);
+  const int64_t n2 = groups * p.Hq * ((p.nq + kQW * 32 - 1) / (kQW * 32));
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BF16>), dim3((unsigned)n2), dim3(kQW * 64), l2, s, P);
   return hipGetLastError();
 }
 
