@@ -39,8 +39,9 @@ namespace {
 
 using namespace attn;
 
-constexpr int kBW = 4;       // dK/dV waves per workgroup (one per SIMD: up to 512 registers)
+constexpr int kKW = 8;       // dV / dK waves per workgroup (two per SIMD, 256 registers each)
 constexpr int kQW = 8;       // dQ waves per workgroup (two per SIMD, 256 registers each)
+constexpr int kRoleV = 0, kRoleK = 1;
 constexpr int kBT = 64;      // rows of a staged tile (queries in dkdv, keys in dq)
 
 template <int ROW_BYTES>
@@ -115,31 +116,49 @@ __device__ __forceinline__ int first_query(const IdMap &q, int nq, int64_t kg) {
   return lo;
 }
 
-template <int D>
-constexpr size_t dkdv_stage_bytes() {
-  return (size_t)4 * kBT * D * 2 + 2 * kBT * 4;  // Q, dO rows, Q^T, dO^T tiles, lse, D
+// Stage of the dV / dK kernels: Q rows | (dK: dO rows) | packed dO^T (dV) or
+// Q^T (dK) | nl[64] | (dK: -D[64])
+template <int D, int ROLE>
+constexpr size_t kv_stage_bytes() {
+  return ROLE == kRoleV ? (size_t)2 * kBT * D * 2 + kBT * 4
+                        : (size_t)3 * kBT * D * 2 + 2 * kBT * 4;
 }
 template <int D>
 constexpr size_t dq_stage_bytes() {
   return (size_t)3 * kBT * D * 2;  // K, V rows, K^T tile
 }
 
-template <int D, bool BF16>
-__global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
+// dV (ROLE kRoleV) or dK (kRoleK) of a batch of problems: a workgroup owns
+// 256 keys (a wave 32, two waves per SIMD) and loops over the query heads of
+// its K/V head and the 64-query tiles that may see its keys.  S = Q K^T with
+// Q rows from LDS and this lane's K row in registers (a lane owns a key
+// column), then
+//   dV: P = exp2(S c + nl), dV^T += dO^T P;
+//   dK: dP - D = dO V^T - D as well, dS = P (dP - D), dK^T += Q^T dS,
+// with dO^T / Q^T from the packed transposed layout, whose query order inside
+// each 16 matches how P and dS sit in the registers.  The two gradients run
+// as two kernels so that each wave's state fits 256 registers (dV and dK
+// together need more, which allowed one wave per SIMD and half the keys per
+// workgroup, i.e. twice the loaded bytes per MFMA): computing S twice costs
+// less than those loads.
+template <int D, bool BF16, int ROLE>
+__global__ void __launch_bounds__(kKW * 64) bwd_kv_kernel(BwdParams P) {
   using M = Mfma16<BF16>;
+  constexpr bool DK = ROLE == kRoleK;
   const BatchParams &p = P.a;
   constexpr int KS = D / 16, DT = D / 32;
   constexpr int RB = D * 2;          // bytes of a Q / dO row
   constexpr int TB = kBT * 2;        // bytes of a packed Q^T / dO^T row (64 queries)
   constexpr int TQ = kBT * RB;       // bytes of a row tile
   constexpr int TT = D * TB;         // bytes of a packed tile
-  constexpr size_t ST = dkdv_stage_bytes<D>();
+  constexpr int KWG = kKW * 32;      // keys per workgroup
+  constexpr int OFF_T = DK ? 2 * TQ : TQ;     // packed tile
+  constexpr int OFF_NL = OFF_T + TT;          // nl[64], then (dK) -D[64]
+  constexpr size_t ST = kv_stage_bytes<D, ROLE>();
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  // stage layout: sQ | sdO | sQT | sdOT | nl[64] | -D[64]
 
   // workgroup -> (key tile, problem, batch, K/V head); key tile slowest so the
   // heaviest causal tiles (most queries after them) start first
-  const int nkt = (p.nk + 127) / 128;
   const int per_kt = p.nz * p.B * p.Hkv;
   int idx = blockIdx.x;
   const int kt = idx / per_kt;
@@ -148,7 +167,6 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
   idx /= p.Hkv;
   const int b = idx % p.B;
   const int z = idx / p.B;
-  (void)nkt;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int hl = lane >> 5, c32 = lane & 31;
@@ -160,7 +178,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
   const float c = p.scale * kLog2e;
 
   // this wave's 32 keys and this lane's key column
-  const int j0w = kt * 128 + wave * 32;
+  const int j0w = kt * KWG + wave * 32;
   const int jw = j0w + c32;
   const bool kvalid = jw < p.nk;
   const bool wave_keys = j0w < p.nk;
@@ -172,73 +190,67 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
   const int imin = (p.causal && kvalid) ? first_query(qid, p.nq, kid(jw)) : 0;
   const int imax_w = (p.causal && wave_keys) ? first_query(qid, p.nq, klast) : 0;
 
-  // B operands of S = Q K^T and dP = dO V^T: K^T, V^T columns = this lane's key row
-  s16x8 kB[KS], vB[KS];
+  // B operands of S = Q K^T (and dP = dO V^T): this lane's K (V) row
+  s16x8 kB[KS], vB[DK ? KS : 1];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    s16x8 x = (s16x8){0, 0, 0, 0, 0, 0, 0, 0}, y = x;
-    if (kvalid) {
-      x = *(const s16x8 *)(kp + (int64_t)jw * p.ks_t + 16 * ks + 8 * hl);
-      y = *(const s16x8 *)(vp + (int64_t)jw * p.vs_t + 16 * ks + 8 * hl);
-    }
+    s16x8 x = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    if (kvalid) x = *(const s16x8 *)(kp + (int64_t)jw * p.ks_t + 16 * ks + 8 * hl);
     kB[ks] = x;
-    vB[ks] = y;
+    if (DK) {
+      s16x8 y = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
+      if (kvalid) y = *(const s16x8 *)(vp + (int64_t)jw * p.vs_t + 16 * ks + 8 * hl);
+      vB[DK ? ks : 0] = y;
+    }
   }
-  f32x16 dKt[DT], dVt[DT];
+  f32x16 acc[DT];  // dV^T or dK^T of this lane's key
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      dKt[dt][e] = 0.f;
-      dVt[dt][e] = 0.f;
-    }
+    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
 
   // query tiles that can see any key of this workgroup, for every query head
   // of the K/V head: iteration f = hq * per + (qt - qt0), heads outermost
-  const int64_t kwg = kid(min(kt * 128, p.nk - 1));
+  const int64_t kwg = kid(min(kt * KWG, p.nk - 1));
   const int qt0 = (p.causal ? first_query(qid, p.nq, kwg) : 0) / kBT;
-  const int per = (p.nq + kBT - 1) / kBT - qt0;
-  const int nf = per > 0 ? G * per : 0;
   const int nqt = (p.nq + kBT - 1) / kBT;
+  const int per = nqt - qt0;
+  const int nf = per > 0 ? G * per : 0;
   const int nq_pad = nqt * kBT;
   const uint32_t rowb = (uint32_t)p.qs_t * 2;
   const uint32_t vo_r = tile_voff<RB>(rowb, wave, lane), vo_t = tile_voff<TB>(TB, wave, lane);
   // Loads walk the tiles (head hq, query tile qt) in iteration order; the
   // buffer descriptors of a head are built when the walk reaches it.
   int iss_hq = 0, iss_qt = qt0;
-  __amdgpu_buffer_rsrc_t r_q, r_do, r_qT, r_doT, r_nl, r_nD;
+  __amdgpu_buffer_rsrc_t r_q, r_do, r_t, r_nl, r_nD;
   auto set_head = [&](const int hq) {
     const int h = kvh * G + hq;
     const int64_t qoff = p.q_zstride * z + b * p.qs_b + h * p.qs_h;
     const int64_t rows_bytes = (int64_t)p.nq * rowb;
     r_q = rsrc((const short *)p.q + qoff, rows_bytes);
-    r_do = rsrc((const short *)P.dout + qoff, rows_bytes);
+    if (DK) r_do = rsrc((const short *)P.dout + qoff, rows_bytes);
     const int64_t toff = P.qT_zstride * z + ((int64_t)b * p.Hq + h) * D * nq_pad;
-    const int64_t tbytes = (int64_t)D * nq_pad * 2;
-    r_qT = rsrc((const short *)P.qT + toff, tbytes);
-    r_doT = rsrc((const short *)P.doT + toff, tbytes);
+    r_t = rsrc((const short *)(DK ? P.qT : P.doT) + toff, (int64_t)D * nq_pad * 2);
     const int64_t moff = p.ml_zstride * z + ((int64_t)b * p.Hq + h) * p.nq;
     r_nl = rsrc(P.nl + moff, (int64_t)p.nq * 4);
-    r_nD = rsrc(P.nD + moff, (int64_t)p.nq * 4);
+    if (DK) r_nD = rsrc(P.nD + moff, (int64_t)p.nq * 4);
   };
   set_head(0);
   // The next tile of the walk into `stage`, in three parts issued at three
-  // points of an iteration: a burst of all of a tile's loads from the four
-  // waves fills the load queue and stalls their instruction issue.
+  // points of an iteration (a burst of a whole tile's loads stalls issue).
   auto issue = [&](const int stage, const int part) {
     char *st = lds + stage * ST;
-    const uint32_t so = (uint32_t)iss_qt * kBT * rowb, sot = (uint32_t)iss_qt * TT;
+    const uint32_t so = (uint32_t)iss_qt * kBT * rowb;
     if (part == 0) {
-      load_tile<RB, kBT, kBW>(st, r_q, rowb, vo_r, so, wave);
-      load_tile<RB, kBT, kBW>(st + TQ, r_do, rowb, vo_r, so, wave);
+      load_tile<RB, kBT, kKW>(st, r_q, rowb, vo_r, so, wave);
+      if (DK) load_tile<RB, kBT, kKW>(st + TQ, r_do, rowb, vo_r, so, wave);
     } else if (part == 1) {
-      load_tile<TB, D, kBW>(st + 2 * TQ, r_qT, TB, vo_t, sot, wave);
+      load_tile<TB, D, kKW>(st + OFF_T, r_t, TB, vo_t, (uint32_t)iss_qt * TT, wave);
     } else {
-      load_tile<TB, D, kBW>(st + 2 * TQ + TT, r_doT, TB, vo_t, sot, wave);
       if (wave == 0) {
-        dma4b(r_nl, (lds_void *)(st + 2 * TQ + 2 * TT), lane * 4, (uint32_t)iss_qt * kBT * 4);
-        dma4b(r_nD, (lds_void *)(st + 2 * TQ + 2 * TT + kBT * 4), lane * 4,
-              (uint32_t)iss_qt * kBT * 4);
+        dma4b(r_nl, (lds_void *)(st + OFF_NL), lane * 4, (uint32_t)iss_qt * kBT * 4);
+        if (DK)
+          dma4b(r_nD, (lds_void *)(st + OFF_NL + kBT * 4), lane * 4, (uint32_t)iss_qt * kBT * 4);
       }
       if (++iss_qt == nqt) {
         iss_qt = qt0;
@@ -257,55 +269,51 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
     const bool more = f + 1 < nf;
     if (more) issue((f + 1) & 1, 0);
     const char *st = lds + (f & 1) * ST;
-    const char *sQ = st, *sdO = st + TQ, *sQT = st + 2 * TQ, *sdOT = st + 2 * TQ + TT;
-    const float *sNl = (const float *)(st + 2 * TQ + 2 * TT);
+    const char *sQ = st, *sdO = st + TQ, *sT = st + OFF_T;
+    const float *sNl = (const float *)(st + OFF_NL);
     const float *sND = sNl + kBT;
     const int i0 = qt * kBT;
 
-    // The tile in two halves of 32 queries (ib): S = Q K^T and dP - D = dO V^T - D
-    // for the half (A operands of k-step ks + 1 read from LDS while k-step ks
-    // is multiplied), then its two groups of 16 queries (kq = 2 ib + g) into
-    // dV^T += dO^T P and dK^T += Q^T dS.  Element e of S is query
-    // 32 ib + 8(e/4) + 4 hl + e%4 of the tile, key column jw.
-    // The causal mask is the initial value of S: -inf where the row comes
-    // before imin (p = exp2(S c + nl) = 0 there), else 0.  Rows past the end of
-    // the shard need none: their Q and dO rows and packed columns are zero, so
-    // they add nothing.  Rows with no key at all have nl = -inf, so p = 0.
-    struct PdS {
-      s16x8 p, ds;
-    };
-    // One wave per SIMD: nothing else hides the LDS latency, so every LDS
-    // operand is read well ahead of its MFMA.  A operands of S / dP run KA
-    // k-steps ahead; the first KA of half 1, its -D and its nl are read during
-    // the dV/dK products of half 0; a half's first dO^T / Q^T group during its
-    // own last k-steps.
-    constexpr int KA = 3;
-    s16x8 aq[2][KS], ao[2][KS];
-    float4 nd4[2][4], l4[2][4];
+    // The tile in two halves of 32 queries (ib): S (and dP - D) for the
+    // half, then its two groups of 16 queries (kq = 2 ib + g) into the
+    // gradient.  Element e of S is query 32 ib + 8(e/4) + 4 hl + e%4 of the
+    // tile, key column jw.  The causal mask is the initial value of S: -inf
+    // where the row comes before imin (p = exp2(S c + nl) = 0 there), else 0.
+    // Rows past the end of the shard need none: their Q and dO rows and
+    // packed columns are zero, so they add nothing.  Rows with no key at all
+    // have nl = -inf, so p = 0.
+    // A operands of S / dP run KA k-steps ahead; the first KA of half 1 and
+    // its nl (and -D) are read during the gradient products of half 0; a
+    // half's first dO^T / Q^T group during its own last k-steps.
+    constexpr int KA = 2;
+    s16x8 aq[2][KS], ao[2][DK ? KS : 1];
+    float4 l4[2][4], nd4[2][DK ? 4 : 1];
     auto read_a = [&](const int ib, const int ks) {
       aq[ib][ks] = rd<RB>(sQ, 32 * ib + c32, 2 * ks + hl);
-      ao[ib][ks] = rd<RB>(sdO, 32 * ib + c32, 2 * ks + hl);
+      if (DK) ao[ib][DK ? ks : 0] = rd<RB>(sdO, 32 * ib + c32, 2 * ks + hl);
     };
-    auto read_nd = [&](const int ib) {  // -D and nl of the half's rows
+    auto read_rows = [&](const int ib) {  // nl (and -D) of the half's rows
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        nd4[ib][rg] = *(const float4 *)(sND + 32 * ib + 8 * rg + 4 * hl);
         l4[ib][rg] = *(const float4 *)(sNl + 32 * ib + 8 * rg + 4 * hl);
+        if (DK) nd4[ib][DK ? rg : 0] = *(const float4 *)(sND + 32 * ib + 8 * rg + 4 * hl);
       }
     };
-    read_nd(0);
+    read_rows(0);
 #pragma unroll
     for (int ks = 0; ks < KA; ++ks) read_a(0, ks);
 
     auto half = [&](const int ib) {
-      // dP starts at -D of its row, so the product leaves dP - D
       f32x16 S, dP;
+      if (DK) {  // dP starts at -D of its row, so the product leaves dP - D
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        dP[4 * rg + 0] = nd4[ib][rg].x;
-        dP[4 * rg + 1] = nd4[ib][rg].y;
-        dP[4 * rg + 2] = nd4[ib][rg].z;
-        dP[4 * rg + 3] = nd4[ib][rg].w;
+        for (int rg = 0; rg < 4; ++rg) {
+          const float4 x = nd4[ib][DK ? rg : 0];
+          dP[4 * rg + 0] = x.x;
+          dP[4 * rg + 1] = x.y;
+          dP[4 * rg + 2] = x.z;
+          dP[4 * rg + 3] = x.w;
+        }
       }
       if (FULL) {
 #pragma unroll
@@ -315,25 +323,22 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) S[e] = 8 * (e >> 2) + (e & 3) >= lo ? 0.f : -INFINITY;
       }
-      s16x8 ct[2][DT][2];
+      s16x8 ct[2][DT];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if (ks + KA < KS) {
           read_a(ib, ks + KA);
         } else if (ks + KA == KS) {
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) ct[0][dt][0] = rd<TB>(sdOT, 32 * dt + c32, 4 * ib + hl);
-        } else if (ks + KA == KS + 1) {
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) ct[0][dt][1] = rd<TB>(sQT, 32 * dt + c32, 4 * ib + hl);
+          for (int dt = 0; dt < DT; ++dt) ct[0][dt] = rd<TB>(sT, 32 * dt + c32, 4 * ib + hl);
         }
         S = M::mma(aq[ib][ks], kB[ks], S);
-        dP = M::mma(ao[ib][ks], vB[ks], dP);
+        if (DK) dP = M::mma(ao[ib][DK ? ks : 0], vB[DK ? ks : 0], dP);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (ib == 0 && more) issue((f + 1) & 1, 1);
-      auto elem = [&](const int g) {  // group g: registers 8g .. 8g+7
-        f32x16 pv, dv;
+      auto elem = [&](const int g) {  // group g: registers 8g .. 8g+7, packed B operand
+        f32x16 v;
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg) {
           const float4 x = l4[ib][2 * g + rg];
@@ -342,36 +347,26 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
           for (int u = 0; u < 4; ++u) {
             const int e = 8 * g + 4 * rg + u;
             const float pe = __builtin_amdgcn_exp2f(fmaf(S[e], c, nl[u]));
-            pv[4 * rg + u] = pe;
-            dv[4 * rg + u] = pe * dP[e];
+            v[4 * rg + u] = DK ? pe * dP[e] : pe;
           }
         }
-        PdS r;
-        r.p = M::pack(pv, 0);
-        r.ds = M::pack(dv, 0);
-        return r;
+        return M::pack(v, 0);
       };
-      // group 1's operands are read and its P, dS computed while the MFMAs of
-      // group 0 run; during group 1's, the first operands of half 1
-      PdS cur = elem(0);
+      // group 1's operands are read and its P (dS) computed while the MFMAs
+      // of group 0 run; during group 1's, the first operands of half 1
+      s16x8 cur = elem(0);
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         if (g == 0) {
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            ct[1][dt][0] = rd<TB>(sdOT, 32 * dt + c32, 4 * ib + 2 + hl);
-            ct[1][dt][1] = rd<TB>(sQT, 32 * dt + c32, 4 * ib + 2 + hl);
-          }
+          for (int dt = 0; dt < DT; ++dt) ct[1][dt] = rd<TB>(sT, 32 * dt + c32, 4 * ib + 2 + hl);
         } else if (ib == 0) {
-          read_nd(1);
+          read_rows(1);
 #pragma unroll
           for (int ks = 0; ks < KA; ++ks) read_a(1, ks);
         }
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          dVt[dt] = M::mma(ct[g][dt][0], cur.p, dVt[dt]);
-          dKt[dt] = M::mma(ct[g][dt][1], cur.ds, dKt[dt]);
-        }
+        for (int dt = 0; dt < DT; ++dt) acc[dt] = M::mma(ct[g][dt], cur, acc[dt]);
         if (g == 0) cur = elem(1);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -383,7 +378,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
 
   // Per wave the tiles of each query head come as a run of partial tiles (the
   // causal diagonal; a tile where the wave sees nothing runs fully masked, so
-  // the accumulators stay on one path) and then a run of full ones: two loops
+  // the accumulator stays on one path) and then a run of full ones: two loops
   // with one body each keep the mask code out of the full tiles.
   if (nf > 0) {
     issue(0, 0);
@@ -400,26 +395,21 @@ __global__ void __launch_bounds__(kBW * 64) bwd_dkdv_kernel(BwdParams P) {
     for (; f < nf && qt * kBT >= imax_w; next()) step(f, qt, std::true_type());
   }
   if (!kvalid) return;
-  // element e of dKt[dt]: d = 32dt + 8(e/4) + 4hl + e%4 of key jw
+  // element e of acc[dt]: d = 32dt + 8(e/4) + 4hl + e%4 of key jw
   const int64_t ko = P.dk_zstride * kvi + ((int64_t)(b * p.Hkv + kvh) * p.nk + jw) * D;
-  float *dk = P.dk + ko;
-  float *dv = P.dv + ko;
+  float *out = (DK ? P.dk : P.dv) + ko;
+  const float sc = DK ? p.scale : 1.f;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const int dd = 32 * dt + 8 * rg + 4 * hl;
-      float4 a = *(float4 *)(dk + dd), v = *(float4 *)(dv + dd);
-      a.x += p.scale * dKt[dt][4 * rg + 0];
-      a.y += p.scale * dKt[dt][4 * rg + 1];
-      a.z += p.scale * dKt[dt][4 * rg + 2];
-      a.w += p.scale * dKt[dt][4 * rg + 3];
-      v.x += dVt[dt][4 * rg + 0];
-      v.y += dVt[dt][4 * rg + 1];
-      v.z += dVt[dt][4 * rg + 2];
-      v.w += dVt[dt][4 * rg + 3];
-      *(float4 *)(dk + dd) = a;
-      *(float4 *)(dv + dd) = v;
+      float4 a = *(float4 *)(out + dd);
+      a.x += sc * acc[dt][4 * rg + 0];
+      a.y += sc * acc[dt][4 * rg + 1];
+      a.z += sc * acc[dt][4 * rg + 2];
+      a.w += sc * acc[dt][4 * rg + 3];
+      *(float4 *)(out + dd) = a;
     }
 }
 
@@ -679,11 +669,15 @@ template <int D, bool BF16>
 hipError_t launch_bwd_d(const BwdParams &P, hipStream_t s) {
   const BatchParams &p = P.a;
   const int64_t groups = (int64_t)p.nz * p.B;
-  constexpr size_t l1 = 2 * dkdv_stage_bytes<D>(), l2 = 2 * dq_stage_bytes<D>();
+  constexpr size_t lv = 2 * kv_stage_bytes<D, kRoleV>(), lk = 2 * kv_stage_bytes<D, kRoleK>(),
+                   l2 = 2 * dq_stage_bytes<D>();
   static bool attr_set = false;  // more than 64 KB of LDS per workgroup must be opted into
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)bwd_dkdv_kernel<D, BF16>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)l1);
+    hipError_t e = hipFuncSetAttribute((const void *)bwd_kv_kernel<D, BF16, kRoleV>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lv);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void *)bwd_kv_kernel<D, BF16, kRoleK>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lk);
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void *)bwd_dq_kernel<D, BF16>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)l2);
@@ -691,9 +685,14 @@ hipError_t launch_bwd_d(const BwdParams &P, hipStream_t s) {
     attr_set = true;
   }
   if (p.nk > 0) {
-    const int64_t n1 = groups * p.Hkv * ((p.nk + 127) / 128);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16>), dim3((unsigned)n1), dim3(kBW * 64), l1, s, P);
+    const int64_t n1 = groups * p.Hkv * ((p.nk + kKW * 32 - 1) / (kKW * 32));
+    hipLaunchKernelGGL((bwd_kv_kernel<D, BF16, kRoleV>), dim3((unsigned)n1), dim3(kKW * 64), lv,
+                       s, P);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_kv_kernel<D, BF16, kRoleK>), dim3((unsigned)n1), dim3(kKW * 64), lk,
+                       s, P);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int64_t n2 = groups * p.Hq * ((p.nq + kQW * 32 - 1) / (kQW * 32));
