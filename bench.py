@@ -160,8 +160,8 @@ def merge_bench(torch, rb, rows=4 * 16 * 512 * 64, d=64, iters=20):
 def overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse, t_copy_ms,
                   steps=3):
     """How much of the K/V hand-off the compute hides: the same step with the
-    blocks read in place (SWAP, no transfer), and the hop copies alone (one
-    device-to-device copy of the hand-off bytes per hop, on one stream)."""
+    blocks read in place (SWAP, no transfer), and the hop copies alone (the
+    library's hand-off copy of the hand-off bytes, once per hop, on one stream)."""
     ra = RingAttention(w.B, w.Hq, w.Hkv, w.S, w.d, w.R, layout, tdt, w.causal, w.scale,
                        rank0=w.rank0, n_ranks=w.ranks, handoff=rb.HANDOFF_SWAP)
     ra.run(q, k, v, o, lse)
@@ -181,12 +181,12 @@ def overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse, t_c
     per_hop = k_bytes + v_bytes
     src = torch.empty(per_hop, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
-    dst.copy_(src)
+    rb.ra_handoff_copy(dst, src)
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     c0.record()
     for _ in range(w.R - 1):
-        dst.copy_(src)
+        rb.ra_handoff_copy(dst, src)
     c1.record()
     torch.cuda.synchronize()
     t_copies = c0.elapsed_time(c1)

@@ -201,6 +201,20 @@ ra_status ra_merge(float *o_acc, float *m_acc, float *l_acc, const float *o_blk,
                    ra_stream stream);
 
 /*
+ * ra_handoff_copy -- the K/V hand-off between hops (highthink.cn article,
+ * section on Zig Zag Ring Attention: each rank passes the K/V it holds to its
+ * ring successor while attending to the current block): a device-to-device
+ * copy of `bytes` bytes on `stream`, as ra_ring_fwd issues it on its copy
+ * stream.  It runs on a small grid with non-temporal loads and stores, so next
+ * to a block kernel it takes few compute units and does not evict the K/V
+ * tiles that kernel reuses from L2.  dst, src: device pointers, not
+ * overlapping; 16-byte aligned pointers and a multiple of 16 bytes take the
+ * kernel, anything else falls back to hipMemcpyAsync.  Asynchronous.
+ * Errors: RA_ERR_INVALID_ARG (null pointer with bytes > 0), RA_ERR_HIP.
+ */
+ra_status ra_handoff_copy(void *dst, const void *src, size_t bytes, ra_stream stream);
+
+/*
  * ra_finalize -- running state to outputs: out = O rounded to nearest even
  * in `dtype`, lse = m + ln(l) (fp32, natural log; -inf for an empty row).
  * o_acc device fp32 [rows][d]; out device [rows][d] of dtype; m, l, lse

@@ -28,7 +28,7 @@ EXPORTED = ("ra_version", "ra_status_string", "ra_last_error", "ra_layout_permut
             "ra_pack_v", "ra_merge", "ra_finalize", "ra_ring_fwd_workspace_size", "ra_ring_fwd",
             "ra_causal_work", "ra_decode_fwd_workspace_size", "ra_decode_fwd",
             "ra_block_bwd_workspace_size", "ra_block_bwd", "ra_ring_bwd_workspace_size",
-            "ra_ring_bwd")
+            "ra_ring_bwd", "ra_handoff_copy")
 
 
 class RAError(RuntimeError):
@@ -112,6 +112,7 @@ def lib():
     L.ra_packed_v_bytes.argtypes = [I32, I32, I32, I32, I32]
     L.ra_packed_v_bytes.restype = ctypes.c_size_t
     L.ra_pack_v.argtypes = [P, P, I32, I32, I32, I32, I32, ctypes.POINTER(I64), P]
+    L.ra_handoff_copy.argtypes = [P, P, ctypes.c_size_t, P]
     L.ra_merge.argtypes = [P, P, P, P, P, P, I64, I32, P]
     L.ra_finalize.argtypes = [P, P, P, P, P, I32, I64, I32, P]
     L.ra_ring_fwd_workspace_size.argtypes = [ctypes.POINTER(RingArgs)]
@@ -222,6 +223,12 @@ def ra_pack_v(v, vp, stream=None):
     B, H, n, d = v.shape
     st = (I64 * 3)(v.stride(0), v.stride(1), v.stride(2))
     _check(lib().ra_pack_v(_ptr(v), _ptr(vp), dtype_code(v), B, H, n, d, st, _stream(stream)))
+
+
+def ra_handoff_copy(dst, src, nbytes=None, stream=None):
+    """Device copy of nbytes (default: all of src) from src to dst, as the ring's hand-off."""
+    nb = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    _check(lib().ra_handoff_copy(_ptr(dst), _ptr(src), nb, _stream(stream)))
 
 
 def ra_merge(o_acc, m_acc, l_acc, o_blk, m_blk, l_blk, stream=None):

@@ -564,6 +564,14 @@ ra_status ra_pack_v(const void *v, void *vp, int32_t dtype, int32_t B, int32_t H
   return RA_OK;
 }
 
+ra_status ra_handoff_copy(void *dst, const void *src, size_t bytes, ra_stream stream) {
+  clear_error();
+  if (bytes == 0) return RA_OK;
+  if (!dst || !src) return fail(RA_ERR_INVALID_ARG, "null pointer");
+  RA_HIP(launch_copy(dst, src, bytes, (hipStream_t)stream), "hand-off copy");
+  return RA_OK;
+}
+
 ra_status ra_merge(float *o_acc, float *m_acc, float *l_acc, const float *o_blk,
                    const float *m_blk, const float *l_blk, int64_t rows, int32_t d,
                    ra_stream stream) {
@@ -765,16 +773,12 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
           run_len += bb;
           continue;
         }
-        if (run_len)
-          RA_HIP(hipMemcpyAsync(run_dst, run_src, run_len, hipMemcpyDeviceToDevice, xs),
-                 "hand-off copy");
+        if (run_len) RA_HIP(launch_copy(run_dst, run_src, run_len, xs), "hand-off copy");
         run_src = src;
         run_dst = dst;
         run_len = bb;
       }
-      if (run_len)
-        RA_HIP(hipMemcpyAsync(run_dst, run_src, run_len, hipMemcpyDeviceToDevice, xs),
-               "hand-off copy");
+      if (run_len) RA_HIP(launch_copy(run_dst, run_src, run_len, xs), "hand-off copy");
     }
     RA_HIP(hipEventRecord(ev_copy(h), xs), "hipEventRecord");
   }

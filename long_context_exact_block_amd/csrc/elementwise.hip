@@ -142,6 +142,27 @@ inline unsigned blocks_for(int64_t total) { return (unsigned)((total + 255) / 25
 
 }  // namespace
 
+// The K/V hand-off between hops: a plain copy, run on the side stream next to
+// the block kernel.  A small grid (the copy has a whole hop to finish) and
+// non-temporal 16-byte loads and stores that stream past the caches, so the
+// copy neither takes many compute units nor evicts the K/V tiles the block
+// kernel's workgroups share in L2.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCopyGrid = 64, kCopyUnroll = 4;
+__global__ void __launch_bounds__(256) copy16_kernel(const u32x4 *__restrict__ src,
+                                                     u32x4 *__restrict__ dst, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + (kCopyUnroll - 1) * stride < n16; i += kCopyUnroll * stride) {
+    u32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) __builtin_nontemporal_store(v[u], dst + i + u * stride);
+  }
+  for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
 hipError_t launch_merge(float *o_acc, float *m_acc, float *l_acc, const float *o_blk,
                         const float *m_blk, const float *l_blk, int64_t rows, int32_t d,
                         hipStream_t s) {
@@ -205,6 +226,18 @@ hipError_t launch_layout_move(bool gather, const void *src, void *dst, const int
     hipLaunchKernelGGL(move_kernel<uint8_t>, dim3(blocks_for(total)), dim3(256), 0, s, gather,
                        (const uint8_t *)src, (uint8_t *)dst, fwd, B * H, S, n, d, rank0, total);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  if (((uintptr_t)dst | (uintptr_t)src | bytes) & 15)
+    return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+  const int64_t n16 = (int64_t)(bytes / 16);
+  const int64_t need = (n16 + 255) / 256;
+  const unsigned grid = (unsigned)(need < kCopyGrid ? need : kCopyGrid);
+  hipLaunchKernelGGL(copy16_kernel, dim3(grid), dim3(256), 0, s, (const u32x4 *)src, (u32x4 *)dst,
+                     n16);
   return hipGetLastError();
 }
 

@@ -102,6 +102,9 @@ hipError_t launch_finalize(const float *o_acc, const float *m, const float *l, v
                            float *lse, int dtype, int64_t rows, int32_t d, hipStream_t s);
 hipError_t launch_layout_permute(int layout, int64_t S, int32_t R, int32_t *fwd, int32_t *inv,
                                  hipStream_t s);
+// device-to-device copy on stream s (small grid, non-temporal; falls back to
+// hipMemcpyAsync for pointers or sizes that are not 16-byte multiples)
+hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
 hipError_t launch_layout_move(bool gather, const void *src, void *dst, const int32_t *fwd,
                               int32_t elem_bytes, int64_t B, int64_t H, int64_t S, int64_t d,
                               int32_t R, int32_t rank0, int32_t n_ranks, hipStream_t s);

@@ -162,6 +162,12 @@ def test_layout_rejects(lib):
     assert lib.ra_layout_gather(4096, 8192, 4096, 2, 1, 1, 8, 4, 4, 2, 3, None) == 2
 
 
+def test_handoff_copy_rejects(lib):
+    assert lib.ra_handoff_copy(None, 4096, 16, None) == 1
+    assert lib.ra_handoff_copy(4096, None, 16, None) == 1
+    assert lib.ra_handoff_copy(None, None, 0, None) == 0  # nothing to copy: no GPU call
+
+
 def test_merge_finalize_reject(lib):
     assert lib.ra_merge(4096, 4096, 4096, 4096, 4096, 4096, 10, 6, None) == 2
     assert lib.ra_merge(4100, 4096, 4096, 4096, 4096, 4096, 10, 8, None) == 4
