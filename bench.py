@@ -227,7 +227,7 @@ def backward_bench(torch, ra, w, layout_code, q, k, v, iters=2):
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                          "algorithmic_flops": flops,
-                         "kernels": "bwd_dkdv_kernel + bwd_dq_kernel (+ packing, D, casts)"}}
+                         "kernels": "bwd_kv_kernel<dV>, bwd_kv_kernel<dK>, bwd_dq_kernel (+ packing, D, casts)"}}
 
 
 def rb_ring_bwd(ra):
