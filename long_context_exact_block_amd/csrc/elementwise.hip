@@ -21,7 +21,10 @@ namespace ra {
 namespace {
 
 // One thread per 4 consecutive floats of a row; d/4 threads share a row.
-// Reads O_a, O_b (8d bytes), writes O (4d), plus the row's (m, l) pairs.
+// Reads O_a, O_b (8d bytes), writes O (4d), plus the row's (m, l) pairs.  The
+// O rows are touched once: non-temporal loads and stores stream them past the
+// caches (plain streaming reads top out ~10 % lower on MI355X).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 __global__ void __launch_bounds__(256) merge_kernel(float *__restrict__ o_acc,
                                                     float *__restrict__ m_acc,
                                                     float *__restrict__ l_acc,
@@ -47,14 +50,15 @@ __global__ void __launch_bounds__(256) merge_kernel(float *__restrict__ o_acc,
     l = wa + wb;
     const float inv = 1.f / l;
     const float ca = wa * inv, cb = wb * inv;
-    const float4 a = ((const float4 *)o_acc)[tid];
-    const float4 b = ((const float4 *)o_blk)[tid];
+    const f32x4 a = __builtin_nontemporal_load((const f32x4 *)o_acc + tid);
+    const f32x4 b = __builtin_nontemporal_load((const f32x4 *)o_blk + tid);
     r.x = ca * a.x + cb * b.x;
     r.y = ca * a.y + cb * b.y;
     r.z = ca * a.z + cb * b.z;
     r.w = ca * a.w + cb * b.w;
   }
-  ((float4 *)o_acc)[tid] = r;
+  const f32x4 rv = {r.x, r.y, r.z, r.w};
+  __builtin_nontemporal_store(rv, (f32x4 *)o_acc + tid);
   if (q == 0) {
     m_acc[row] = m;
     l_acc[row] = l;
