@@ -235,6 +235,43 @@ def rb_ring_bwd(ra):
     rb.ra_ring_bwd(ra.bargs, ra.bworkspace)
 
 
+def rank_share_bench(torch, rb, RingAttention, w, iters=3):
+    """Each rank's share of a ring run alone (w: causal MHA 32k, R = 8), for the
+    contiguous and striped layouts: the measured counterpart of the per-rank
+    causal work counts.  Times ra_ring_fwd for one computed rank (R hops, SWAP
+    hand-off, fused fold) after its shards are gathered; device-side random
+    inputs of the workload's shape."""
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed + 11)
+    q = torch.randn(w.B, w.Hq, w.S, w.d, device="cuda", generator=g).to(tdt)
+    k = torch.randn(w.B, w.Hkv, w.S, w.d, device="cuda", generator=g).to(tdt)
+    v = torch.randn(w.B, w.Hkv, w.S, w.d, device="cuda", generator=g).to(tdt)
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.Hq, w.S, device="cuda")
+    out = {}
+    for layout in ("contiguous", "striped"):
+        ms = []
+        for r in range(w.R):
+            ra = RingAttention(w.B, w.Hq, w.Hkv, w.S, w.d, w.R, layout, tdt, w.causal, w.scale,
+                               rank0=r, n_ranks=1, handoff=rb.HANDOFF_SWAP)
+            ra.run(q, k, v, o, lse)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+            torch.cuda.synchronize()
+            e[0].record()
+            for i in range(iters):
+                ra.ring()
+                e[i + 1].record()
+            torch.cuda.synchronize()
+            ms.append(float(np.median([e[i].elapsed_time(e[i + 1]) for i in range(iters)])))
+            del ra
+        a = np.array(ms)
+        out[layout] = {"rank_ms": [round(x, 3) for x in ms],
+                       "max_over_mean": round(float(a.max() / a.mean()), 4)}
+    del q, k, v, o, lse
+    return out
+
+
 def decode_bench(torch, rb, w, iters=20):
     """ra_decode_fwd on the long-context decode step (w: DecodeWorkload): nq new
     tokens against the whole KV cache, split contiguously over R ranks.  HBM
@@ -338,6 +375,8 @@ def main():
                     help="skip the long-context decode measurement (ra_decode_fwd)")
     ap.add_argument("--no-overlap-bench", action="store_true",
                     help="skip the hand-off overlap measurement (SWAP steps + copies alone)")
+    ap.add_argument("--no-rank-bench", action="store_true",
+                    help="skip timing each rank's share of the causal 32k MHA ring alone")
     ap.add_argument("--block-only", action="store_true",
                     help="time only the block kernel on one hop of the workload (query shard x "
                          "one K/V block, packed V), on seeded device-side random inputs")
@@ -432,6 +471,10 @@ def main():
         log("backward")
         backward = backward_bench(torch, ra, w, lcode, q, k, v)
     decode = None if args.no_decode_bench else decode_bench(torch, rb, configs.DECODE_1M)
+    rank_share = None
+    if not args.no_rank_bench:
+        log("rank shares of %s alone" % configs.MHA_32K.name)
+        rank_share = rank_share_bench(torch, rb, RingAttention, configs.MHA_32K)
     imbalance = {}
     for name, code in (("contiguous", 0), ("striped", 1), ("zigzag", 2)):
         if code == 2 and w.S % (2 * w.R):
@@ -492,6 +535,8 @@ def main():
         "backward": backward,
         "decode": decode,
         "causal_imbalance_max_over_mean": imbalance,
+        "rank_share_alone": (None if rank_share is None else
+                             {"workload": configs.MHA_32K.name, **rank_share}),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
