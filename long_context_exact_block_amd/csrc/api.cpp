@@ -297,12 +297,13 @@ DecodeParams decode_plan(const ra_decode_args *a) {
   p.col_blocks = ((a->Hq / a->Hkv) * a->nq + 31) / 32;
   const int64_t groups = (int64_t)a->R * a->B * a->Hkv * p.col_blocks;
   const int64_t W = kDecodeWaves;
-  const int64_t max_splits = std::max<int64_t>(1, (a->n + W * 32 - 1) / (W * 32));
+  // each wave streams whole 64-key tiles (one packed V^T tile each)
+  const int64_t max_splits = std::max<int64_t>(1, (a->n + W * 64 - 1) / (W * 64));
   const int64_t want = 1024;  // workgroups: four per CU keep the GPU busy to the end
   int64_t splits = std::min<int64_t>(max_splits, std::max<int64_t>(1, (want + groups - 1) / groups));
   splits = std::min<int64_t>(splits, std::max<int64_t>(1, 4096 / (int64_t)a->R));
   int64_t wk = (a->n + splits * W - 1) / (splits * W);
-  wk = std::max<int64_t>(32, (wk + 31) / 32 * 32);
+  wk = std::max<int64_t>(64, (wk + 63) / 64 * 64);
   splits = std::max<int64_t>(1, (a->n + W * wk - 1) / (W * wk));
   p.splits = (int32_t)splits;
   p.wave_keys = (int32_t)wk;

@@ -13,11 +13,16 @@
 // rows that share a K/V head (head-in-group x new token, up to 32 per column
 // block) fit one 32-wide MFMA operand, so every key is read once per column
 // block and no two waves need the same key: each wave streams its own key
-// range straight from HBM into MFMA operand registers (K rows and packed V^T
-// rows are 16-byte loads per lane, the next 32-key tile in flight while the
-// current one is computed).  At the end the waves of a workgroup fold their
-// partials in LDS into one (O normalised, m, l); decode_reduce folds the
-// partials of all workgroups of a row.
+// range through a private two-stage LDS ring, 64 keys per stage (the K rows
+// and the packed V^T tile of 64 keys are each one contiguous block).  The
+// stages are filled by non-temporal buffer loads that write LDS directly:
+// every 1 KB load covers whole cache lines and streams past the caches, which
+// on MI355X reads ~7.0 TB/s against ~5.9-6.2 TB/s for cached loads.  A wave
+// waits only on its own loads (vmcnt), so the loop has no barrier.  The MFMA
+// operands are 16-byte LDS reads with the forward kernel's swizzles.  At the
+// end the waves of a workgroup fold their partials in LDS into one (O
+// normalised, m, l); decode_reduce folds the partials of all workgroups of a
+// row.
 #include <cfloat>
 #include <cmath>
 
@@ -35,17 +40,39 @@ constexpr int kMaxP = 4096;   // partials per row the reduction holds in LDS
 // writes of the 32 columns on distinct bank groups
 template <int D>
 constexpr int sorow() { return D + 4; }
+constexpr int kDT = 64;  // keys per tile (one packed V^T tile)
+template <int D>
+constexpr int dec_stage_bytes() { return 2 * kDT * D * 2; }  // K rows + V^T tile
 template <int D>
 constexpr size_t decode_lds_bytes() {
-  return (size_t)kDW * 32 * sorow<D>() * 4 + 2 * kDW * 32 * 4;
+  const size_t fold = (size_t)kDW * 32 * sorow<D>() * 4 + 2 * kDW * 32 * 4;
+  const size_t ring = (size_t)kDW * 2 * dec_stage_bytes<D>();
+  return fold > ring ? fold : ring;
 }
+// LDS has 64 four-byte banks on gfx950: 16-byte chunks of a row are
+// XOR-swizzled by row so the 16-byte operand reads of a 16-lane group hit 16
+// distinct bank groups (256-byte rows: by row & 15; 128-byte rows, which
+// alternate between the two halves of the banks: by (row >> 1) & 7).
+template <int ROW_BYTES>
+__device__ __forceinline__ int dswz(int row) {
+  return ROW_BYTES == 256 ? (row & 15) : ((row >> 1) & 7);
+}
+typedef __attribute__((address_space(3))) void lds_void;
+// 16 bytes per lane, non-temporal, from a raw buffer straight into LDS (lane
+// l lands at dst + 16 l; dst goes to M0).  Cache policy 2 = nt.
+__device__ __forceinline__ void dma16nt(__amdgpu_buffer_rsrc_t rsrc, lds_void *dst, uint32_t voff,
+                                        uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, soff, 0, 2);
+}
+// s_waitcnt immediate waiting for vmcnt <= n only (n < 64; lgkmcnt, expcnt at max)
+constexpr int dwait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 template <int D, bool BF16>
 __global__ void __launch_bounds__(kDW * 64) decode_kernel(DecodeParams p) {
   using M = Mfma16<BF16>;
   constexpr int KS = D / 16;  // k-steps of S^T = K Q^T
   constexpr int DT = D / 32;  // 32-row d tiles of O^T
-  extern __shared__ __attribute__((aligned(16))) float smem[];
+  extern __shared__ __attribute__((aligned(1024))) float smem[];
   float *sO = smem;                                // [kDW][32][sorow]
   float *sM = smem + kDW * 32 * sorow<D>();        // [kDW][32] running max (log2 units)
   float *sL = sM + kDW * 32;                       // [kDW][32] sum
@@ -115,44 +142,66 @@ __global__ void __launch_bounds__(kDW * 64) decode_kernel(DecodeParams p) {
     const int64_t bh = ((int64_t)r * p.B + b) * p.Hkv + kvh;
     const short *kp = (const short *)p.k + bh * p.n * D;
     const short *vp = (const short *)p.v + bh * D * p.n_pad;
-
-    // operands of one 32-key tile, loaded one tile ahead (returned by value:
-    // an array captured by a lambda would be demoted to scratch memory)
-    struct Tile {
-      s16x8 k[KS];     // A of S^T: key jt + c32, d = 16ks + 8hl .. +7
-      s16x8 v[DT][2];  // A of O^T: packed V^T row 32dt + c32, keys jt + 16cc + 8hl ..
+    // byte counts fit 32 bits: n <= 2^23 keys (checked on the host)
+    const auto krsrc = __builtin_amdgcn_make_buffer_rsrc((void *)kp, 0, (int)((uint32_t)p.n * D * 2),
+                                                         0x00020000);
+    const auto vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)vp, 0, (int)((uint32_t)D * (uint32_t)p.n_pad * 2), 0x00020000);
+    constexpr int KROW = D * 2, KTB = kDT * KROW;   // K row / tile bytes
+    constexpr int VROW = kDT * 2, VTB = D * VROW;   // packed V^T row / tile bytes
+    constexpr int NK = KTB / 1024, NV = VTB / 1024;  // 1 KB loads per tile
+    constexpr int SB = dec_stage_bytes<D>();
+    char *ring = (char *)smem + wave * 2 * SB;      // this wave's two stages
+    // load tile jt (a multiple of 64) into stage st: 1 KB u of the K tile is
+    // rows u*RPI.., lane l its chunk l % CPR, fetched from the swizzled source
+    auto issue = [&](int jt, int st) {
+      char *dst = ring + st * SB;
+#pragma unroll
+      for (int u = 0; u < NK; ++u) {
+        constexpr int CPR = KROW / 16, RPI = 1024 / KROW;
+        const int row = u * RPI + lane / CPR;
+        const int ch = (lane % CPR) ^ dswz<KROW>(row);
+        dma16nt(krsrc, (lds_void *)(dst + u * 1024), row * KROW + ch * 16, (uint32_t)jt * KROW);
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        constexpr int CPR = VROW / 16, RPI = 1024 / VROW;
+        const int row = u * RPI + lane / CPR;
+        const int ch = (lane % CPR) ^ dswz<VROW>(row);
+        dma16nt(vrsrc, (lds_void *)(dst + KTB + u * 1024), row * VROW + ch * 16,
+                (uint32_t)(jt / kDT) * VTB);
+      }
     };
-    auto load = [&](int jt) {
-      Tile t;
-      // rows past the run are clamped in bounds (and masked); packed V is
-      // zero past n and n_pad >= jt + 32
-      const int krow = min(jt + c32, p.n - 1);
+    // per-lane operand offsets: K row kb*32 + c32 and V^T row 32dt + c32
+    // share the swizzle of row c32
+    int koff[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) koff[ks] = c32 * KROW + (((2 * ks + hl) ^ dswz<KROW>(c32)) << 4);
+    int voff[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) voff[q4] = KTB + c32 * VROW + (((2 * q4 + hl) ^ dswz<VROW>(c32)) << 4);
+
+    auto compute = [&](const char *stg, int jt) {
+      f32x16 S[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) S[kb][e] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        t.k[ks] = *(const s16x8 *)(kp + (int64_t)krow * D + 16 * ks + 8 * hl);
-      // packed V^T tile jt/64 is a [D][64] block; this 32-key half at jt % 64
-      const short *vt = vp + (int64_t)(jt >> 6) * D * 64 + (jt & 63);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-          t.v[dt][cc] = *(const s16x8 *)(vt + (32 * dt + c32) * 64 + 16 * cc + 8 * hl);
-      return t;
-    };
-    auto compute = [&](const Tile &t, int jt) {
-      f32x16 S;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) S[e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) S = M::mma(t.k[ks], qf[ks], S);
-      // element e of S^T is key jt + 8(e/4) + 4hl + e%4 of this lane's column
+        for (int kb = 0; kb < 2; ++kb)
+          S[kb] = M::mma(*(const s16x8 *)(stg + koff[ks] + kb * 32 * KROW), qf[ks], S[kb]);
+      // element e of S^T[kb] is key jt + 32kb + 8(e/4) + 4hl + e%4 of this lane's column
       float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = jt + (e >> 2) * 8 + 4 * hl + (e & 3);
-        if (j >= jlim) S[e] = -INFINITY;
-        mx = fmaxf(mx, S[e]);
-      }
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int j = jt + 32 * kb + (e >> 2) * 8 + 4 * hl + (e & 3);
+          if (j >= jlim) S[kb][e] = -INFINITY;
+          mx = fmaxf(mx, S[kb][e]);
+        }
       mx = half_max(mx);
       const float mt = mx * c;
       if (wave_any(mt > m_run + kTau)) {
@@ -166,31 +215,39 @@ __global__ void __launch_bounds__(kDW * 64) decode_kernel(DecodeParams p) {
         m_run = mn;
       }
       const float nm = -m_run;
-      f32x16 pb;
+      // P^T (B operand), 16 keys per MFMA in the packed order: group q4 is
+      // registers 8(q4 % 2) .. +7 of S^T[q4 / 2]
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        pb[e] = __builtin_amdgcn_exp2f(fmaf(S[e], c, nm));
-        lsum += pb[e];
-      }
-      // P^T (B operand), 16 keys per MFMA in the packed order
-      const s16x8 P0 = M::pack(pb, 0), P1 = M::pack(pb, 8);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x16 pb;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        O[dt] = M::mma(t.v[dt][0], P0, O[dt]);
-        O[dt] = M::mma(t.v[dt][1], P1, O[dt]);
+        for (int e = 0; e < 8; ++e) {
+          pb[e] = __builtin_amdgcn_exp2f(fmaf(S[q4 >> 1][8 * (q4 & 1) + e], c, nm));
+          lsum += pb[e];
+        }
+        const s16x8 P = M::pack(pb, 0);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          O[dt] = M::mma(*(const s16x8 *)(stg + voff[q4] + dt * 32 * VROW), P, O[dt]);
       }
     };
-    // two tiles per iteration so the buffers swap roles instead of being copied
-    Tile ta = load(j0), tb;
-    for (int jt = j0; jt < jend; jt += 64) {
-      if (jt + 32 < jend) tb = load(jt + 32);
-      compute(ta, jt);
-      if (jt + 32 >= jend) break;
-      if (jt + 64 < jend) ta = load(jt + 64);
-      compute(tb, jt + 32);
+    // tile t + 1 streams into the other stage (last read by tile t - 1, whose
+    // operands were consumed before its MFMAs) while tile t is computed
+    const int ntile = (jend - j0 + kDT - 1) / kDT;
+    issue(j0, 0);
+    for (int t = 0; t < ntile; ++t) {
+      if (t + 1 < ntile) {
+        issue(j0 + (t + 1) * kDT, (t + 1) & 1);
+        __builtin_amdgcn_s_waitcnt(dwait_vm(NK + NV));  // tile t has landed
+      } else {
+        __builtin_amdgcn_s_waitcnt(dwait_vm(0));
+      }
+      compute(ring + (t & 1) * SB, j0 + t * kDT);
     }
   }
 
+  // the staging ring and the partials below share the LDS
+  __syncthreads();
   // Fold the waves' partials in LDS: m = max m_w, weights 2^(m_w - m),
   // O = sum w O_w / sum w l_w.  Then one partial per workgroup.
   const float lt = half_sum(lsum);

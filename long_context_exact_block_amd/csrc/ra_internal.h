@@ -77,7 +77,7 @@ hipError_t launch_block_fwd(const BatchParams &p, int dtype, hipStream_t s);
 // columns (column c = head-in-group * nq + query); the waves of a workgroup
 // fold their results into one partial (O normalised, m, l), and
 // decode_reduce folds the P partials of every row.
-constexpr int kDecodeWaves = 4;  // waves per decode workgroup (each streams its own keys)
+constexpr int kDecodeWaves = 2;  // waves per decode workgroup (each streams its own keys)
 struct DecodeParams {
   const void *q;  // [B][Hq][nq][d]
   const void *k;  // [R][B][Hkv][n][d]
