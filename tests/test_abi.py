@@ -225,6 +225,6 @@ def test_decode_workspace(lib):
     a = _decode()
     need = lib.ra_decode_fwd_workspace_size(ctypes.byref(a))
     rows = 1 * 32 * 4
-    assert need >= 8 * 8 * rows * (128 + 2) * 4  # at least one partial per wave of each rank
+    assert need >= 8 * rows * (128 + 2) * 4  # at least one partial (O, m, l) per rank and row
     assert lib.ra_decode_fwd(ctypes.byref(a), ctypes.c_void_p(4096), need - 1, None) == 5
     assert lib.ra_decode_fwd(ctypes.byref(a), ctypes.c_void_p(4096 + 16), need, None) == 5
