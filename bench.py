@@ -531,7 +531,8 @@ def main():
         "step_ms_min": round(float(step_ms.min()), 3),
         "hop_ms": [round(float(x), 3) for x in hop_ms.mean(axis=0)],
         "handoff": handoff,
-        "merge": merge,
+        "merge": (None if merge is None else dict(merge, traffic=traffic_from_profile(
+            ["long_context_exact_block_amd/csrc/elementwise.hip"], "profiles/merge_traffic.json"))),
         "backward": backward,
         "decode": decode,
         "causal_imbalance_max_over_mean": imbalance,
