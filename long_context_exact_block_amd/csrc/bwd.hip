@@ -12,20 +12,21 @@
 //
 // gfx950 design.  The two MFMA operands of a 32x32x16 product both want
 // their reduction dimension contiguous per lane, so each product picks the
-// orientation whose operands are plain 16-byte reads:
-//  * bwd_dkdv_kernel (a workgroup owns 128 keys, a wave 32; loops over the
-//    query heads of its K/V head and 64-query tiles): S = Q K^T and
-//    dP = dO V^T with Q, dO rows from LDS and K, V rows in registers, so a
-//    lane owns a key column; dV^T += dO^T P and dK^T += Q^T dS then read
-//    dO^T and Q^T from the packed transposed layout (the one V uses in the
-//    forward), whose key order matches how P and dS sit in the registers.
-//  * bwd_dq_kernel (a workgroup owns 256 queries, a wave 32, two waves per
-//    SIMD; loops over 64-key tiles): S^T = K Q^T and dP^T = V dO^T as in the
-//    forward (a lane owns a query), dQ^T += K^T dS^T with K^T packed.
+// orientation whose operands are plain 16-byte reads.  Three kernels per hop:
+//  * bwd_kv_kernel<dV> and bwd_kv_kernel<dK> (a workgroup owns 256 keys, a
+//    wave 32; loop over the query heads of the K/V head and 64-query tiles):
+//    S = Q K^T (and dP = dO V^T) with Q, dO rows from LDS and this lane's K,
+//    V rows in registers, so a lane owns a key column; dV^T += dO^T P or
+//    dK^T += Q^T dS then read dO^T / Q^T from the packed transposed layout
+//    (the one V uses in the forward), whose query order matches how P and dS
+//    sit in the registers.  dV and dK are separate kernels so that a wave's
+//    state fits 256 registers; S is computed by both.
+//  * bwd_dq_kernel (a workgroup owns 256 queries, a wave 32; loops over
+//    64-key tiles): S^T = K Q^T and dP^T = V dO^T as in the forward (a lane
+//    owns a query), dQ^T += K^T dS^T with K^T packed.
 // Loaded bytes per MFMA are what these kernels pay for most (the loads
-// stream into LDS next to the operand reads), so a workgroup covers as many
-// rows as its registers allow: dK/dV's per-wave state (K, V rows and two
-// accumulators) needs one wave per SIMD; dQ's fits two.
+// stream into LDS next to the operand reads), so every kernel runs two waves
+// per SIMD over 256 rows per workgroup: one loaded tile serves 256 rows.
 // Each workgroup owns its output tile, so the fp32 accumulation is plain
 // read-add-write: no atomics, deterministic.
 #include <cfloat>
@@ -42,7 +43,7 @@ using namespace attn;
 constexpr int kKW = 8;       // dV / dK waves per workgroup (two per SIMD, 256 registers each)
 constexpr int kQW = 8;       // dQ waves per workgroup (two per SIMD, 256 registers each)
 constexpr int kRoleV = 0, kRoleK = 1;
-constexpr int kBT = 64;      // rows of a staged tile (queries in dkdv, keys in dq)
+constexpr int kBT = 64;      // rows of a staged tile (queries in dV / dK, keys in dQ)
 
 template <int ROW_BYTES>
 __device__ __forceinline__ int swz16(int row) {  // 16-byte chunk swizzle, 64 LDS banks
