@@ -25,6 +25,8 @@ def _cases():
     for w in configs.ALL:
         for layout in w.layouts:
             yield pytest.param(w, layout, id="%s-%s" % (w.name, layout))
+    # the 2R-chunk zig-zag layout on the 1M-token share (rank 3 holds chunks 3 and 12)
+    yield pytest.param(configs.SHARE_1M, "zigzag", id="%s-zigzag" % configs.SHARE_1M.name)
 
 
 @pytest.mark.timeout(900)
