@@ -372,9 +372,85 @@ __global__ void __launch_bounds__(kKW * 64) bwd_kv_kernel(BwdParams P) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    half(0);
+    if (DK) {
+      half(0);
+      if (more) issue((f + 1) & 1, 2);
+      half(1);
+      return;
+    }
+    // dV: the two halves software-pipelined so that MFMA and VALU work
+    // overlap inside the wave: S of half 1 runs under the exponentials of
+    // group (0, 0); each group's dV^T MFMAs run under the next group's
+    // exponentials.
+    //   phase 0: S(0) | phase 1: S(1) + P(0,0) | phase 2: dV(0,0) + P(0,1) |
+    //   phase 3: dV(0,1) + P(1,0) | phase 4: dV(1,0) + P(1,1) | phase 5: dV(1,1)
+    f32x16 Sv[2];
+    auto init_s = [&](const int ib) {
+      if (FULL) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) Sv[ib][e] = 0.f;
+      } else {
+        const int lo = imin - (i0 + 32 * ib + 4 * hl);  // first allowed element row
+#pragma unroll
+        for (int e = 0; e < 16; ++e) Sv[ib][e] = 8 * (e >> 2) + (e & 3) >= lo ? 0.f : -INFINITY;
+      }
+    };
+    // A operands of S: one stream over both halves' 2 KS k-steps, KA ahead
+    auto read_next = [&](const int kk) {  // k-step kk of the 2 KS stream
+      if (kk < 2 * KS) read_a(kk / KS, kk % KS);
+    };
+    auto pe_of = [&](const int ib, const int g, const int u8) {  // element u8 of group (ib, g)
+      const int rg = u8 >> 2, u = u8 & 3;
+      const float4 x = l4[ib][2 * g + rg];
+      const float nl = u == 0 ? x.x : (u == 1 ? x.y : (u == 2 ? x.z : x.w));
+      return __builtin_amdgcn_exp2f(fmaf(Sv[ib][8 * g + u8], c, nl));
+    };
+    s16x8 cv[2][DT];  // dO^T fragments of two groups
+    auto read_ct = [&](const int gi) {  // group gi = 2 ib + g into buffer gi & 1
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) cv[gi & 1][dt] = rd<TB>(sT, 32 * dt + c32, 2 * gi + hl);
+    };
+    init_s(0);
+    // phase 0
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      read_next(ks + KA);
+      if (ks == 0) read_rows(1);
+      Sv[0] = M::mma(aq[0][ks], kB[ks], Sv[0]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) issue((f + 1) & 1, 1);
+    init_s(1);
+    // phase 1
+    f32x16 pv;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      read_next(KS + ks + KA);
+      if (ks == 1) read_ct(0);
+      if (ks == KS - 2) read_ct(1);
+      Sv[1] = M::mma(aq[1][ks], kB[ks], Sv[1]);
+#pragma unroll
+      for (int u8 = (8 * ks) / KS; u8 < (8 * (ks + 1)) / KS; ++u8) pv[u8] = pe_of(0, 0, u8);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (more) issue((f + 1) & 1, 2);
-    half(1);
+    s16x8 cur = M::pack(pv, 0);
+    // phases 2..5: group gi's MFMAs, two elements of group gi + 1 per MFMA
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      if (gi >= 1 && gi + 1 < 4) read_ct(gi + 1);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        acc[dt] = M::mma(cv[gi & 1][dt], cur, acc[dt]);
+        if (gi + 1 < 4) {
+#pragma unroll
+          for (int u8 = (8 * dt) / DT; u8 < (8 * (dt + 1)) / DT; ++u8)
+            pv[u8] = pe_of((gi + 1) >> 1, (gi + 1) & 1, u8);
+        }
+      }
+      if (gi + 1 < 4) cur = M::pack(pv, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // Per wave the tiles of each query head come as a run of partial tiles (the
