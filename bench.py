@@ -157,6 +157,51 @@ def merge_bench(torch, rb, rows=4 * 16 * 512 * 64, d=64, iters=20):
             PEAK_HBM_GBS}
 
 
+def step_parts_bench(torch, rb, ra, w, q, k, v, o, lse, iters=10):
+    """The HBM-bound parts of a step, each timed alone with HIP events around `iters` calls
+    (inputs resident): the index maps (8 B per token), the shard gather of Q, K, V and the
+    scatter of O and LSE (each row read and written once; the 4-byte map entry per row is not
+    counted), and ra_finalize of the running state (4d + 8 B read, elt*d + 4 B written per row;
+    the step runs it inside ra_ring_fwd) on synthetic fp32 state of the same rows."""
+    elt = q.element_size()
+    d = w.d
+    q_rows = ra.n_ranks * w.B * w.Hq * ra.n
+    kv_rows = w.R * w.B * w.Hkv * ra.n
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    parts = {}
+
+    def put(name, ms, nbytes):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        parts[name] = {"ms": round(ms, 4), "bytes": int(nbytes), "GB/s": round(gbs, 1),
+                       "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+    put("layout_maps", timed(ra.maps), 8 * w.S)
+    put("gather_qkv", timed(lambda: ra.gather(q, k, v)), 2 * elt * d * (q_rows + 2 * kv_rows))
+    put("scatter_o_lse", timed(lambda: ra.scatter(o, lse)), 2 * (elt * d + 4) * q_rows)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed + 77)
+    o_acc = torch.randn((q_rows, d), device="cuda", generator=g)
+    m = torch.randn(q_rows, device="cuda", generator=g)
+    l = torch.rand(q_rows, device="cuda", generator=g) + 0.5
+    out = torch.empty((q_rows, d), dtype=q.dtype, device="cuda")
+    lse_out = torch.empty(q_rows, device="cuda")
+    put("finalize", timed(lambda: rb.ra_finalize(o_acc, m, l, out, lse_out)),
+        (4 * d + 8 + elt * d + 4) * q_rows)
+    del o_acc, m, l, out, lse_out
+    return parts
+
+
 def overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse, t_copy_ms,
                   steps=3):
     """How much of the K/V hand-off the compute hides: the same step with the
@@ -375,6 +420,8 @@ def main():
                     help="skip the long-context decode measurement (ra_decode_fwd)")
     ap.add_argument("--no-overlap-bench", action="store_true",
                     help="skip the hand-off overlap measurement (SWAP steps + copies alone)")
+    ap.add_argument("--no-parts-bench", action="store_true",
+                    help="skip timing the maps, gather, scatter and finalize alone")
     ap.add_argument("--no-rank-bench", action="store_true",
                     help="skip timing each rank's share of the causal 32k MHA ring alone")
     ap.add_argument("--block-only", action="store_true",
@@ -466,6 +513,10 @@ def main():
         handoff = overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse,
                                 float(np.median(step_ms)))
     merge = None if args.no_merge_bench else merge_bench(torch, rb)
+    parts = None
+    if not args.no_parts_bench:
+        log("maps, gather, scatter, finalize alone")
+        parts = step_parts_bench(torch, rb, ra, w, q, k, v, o, lse)
     backward = None
     if not args.no_bwd_bench and w.dtype != "fp32":
         log("backward")
@@ -533,6 +584,7 @@ def main():
         "handoff": handoff,
         "merge": (None if merge is None else dict(merge, traffic=traffic_from_profile(
             ["long_context_exact_block_amd/csrc/elementwise.hip"], "profiles/merge_traffic.json"))),
+        "step_parts": parts,
         "backward": backward,
         "decode": decode,
         "causal_imbalance_max_over_mean": imbalance,

@@ -103,6 +103,42 @@ __global__ void __launch_bounds__(256) finalize_kernel(const float *__restrict__
   }
 }
 
+// The same for d % 8 == 0 and a 16-byte aligned output: one thread per 8
+// floats of a row, read with two non-temporal 16-byte loads and written as
+// one 16-byte store of 16-bit values (two for fp32 output), all streaming.
+template <typename T>
+__global__ void __launch_bounds__(256) finalize8_kernel(const float *__restrict__ o_acc,
+                                                        const float *__restrict__ m,
+                                                        const float *__restrict__ l,
+                                                        T *__restrict__ out,
+                                                        float *__restrict__ lse, int d8,
+                                                        int64_t total) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= total) return;
+  const int64_t row = tid / d8;
+  const int q = (int)(tid - row * d8);
+  const f32x4 a = __builtin_nontemporal_load((const f32x4 *)o_acc + 2 * tid);
+  const f32x4 b = __builtin_nontemporal_load((const f32x4 *)o_acc + 2 * tid + 1);
+  if constexpr (sizeof(T) == 4) {
+    __builtin_nontemporal_store(a, (f32x4 *)out + 2 * tid);
+    __builtin_nontemporal_store(b, (f32x4 *)out + 2 * tid + 1);
+  } else {
+    typedef T t8 __attribute__((ext_vector_type(8)));
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    t8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] = cast_out<T>(a[e]);
+      r[4 + e] = cast_out<T>(b[e]);
+    }
+    __builtin_nontemporal_store(__builtin_bit_cast(u4, r), (u4 *)out + tid);
+  }
+  if (q == 0) {
+    const float lv = l[row];
+    lse[row] = lv > 0.f ? m[row] + __logf(lv) : -INFINITY;
+  }
+}
+
 __global__ void layout_kernel(int layout, int64_t S, int32_t R, int64_t n, int32_t *fwd,
                               int32_t *inv) {
   const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -140,6 +176,30 @@ __global__ void move_kernel(bool gather, const U *__restrict__ src, U *__restric
     dst[tid] = src[orig];
   else
     dst[orig] = src[tid];
+}
+
+// The 16-byte path of the same move on a 2-D grid: blockIdx.y is the shard
+// slab kbh = k * BH + bh (uniform, so its split is scalar work), x runs over
+// the n * ru 16-byte units of the slab.  Every unit is read and written once:
+// non-temporal loads and stores.
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__global__ void __launch_bounds__(256) move16_kernel(bool gather, const u32x4v *__restrict__ src,
+                                                     u32x4v *__restrict__ dst,
+                                                     const int32_t *__restrict__ fwd, int64_t BH,
+                                                     int64_t S, int64_t n, uint32_t ru,
+                                                     int32_t rank0) {
+  const uint32_t x = blockIdx.x * 256u + threadIdx.x;  // unit within the slab (< n * ru < 2^32)
+  if ((int64_t)x >= n * ru) return;
+  const int64_t kbh = blockIdx.y;
+  const int64_t k = kbh / BH, bh = kbh - k * BH;
+  const uint32_t j = x / ru, u = x - j * ru;
+  const int64_t tok = fwd[(rank0 + k) * n + j];
+  const int64_t sh = kbh * n * ru + x;
+  const int64_t orig = (bh * S + tok) * ru + u;
+  if (gather)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(src + orig), dst + sh);
+  else
+    __builtin_nontemporal_store(__builtin_nontemporal_load(src + sh), dst + orig);
 }
 
 inline unsigned blocks_for(int64_t total) { return (unsigned)((total + 255) / 256); }
@@ -181,6 +241,19 @@ hipError_t launch_finalize(const float *o_acc, const float *m, const float *l, v
                            float *lse, int dtype, int64_t rows, int32_t d, hipStream_t s) {
   const int64_t total = rows * (d / 4);
   if (total == 0) return hipSuccess;
+  if (d % 8 == 0 && (uintptr_t)out % 16 == 0) {
+    const int64_t t8 = rows * (d / 8);
+    if (dtype == RA_DT_BF16)
+      hipLaunchKernelGGL(finalize8_kernel<__bf16>, dim3(blocks_for(t8)), dim3(256), 0, s, o_acc,
+                         m, l, (__bf16 *)out, lse, d / 8, t8);
+    else if (dtype == RA_DT_FP16)
+      hipLaunchKernelGGL(finalize8_kernel<_Float16>, dim3(blocks_for(t8)), dim3(256), 0, s, o_acc,
+                         m, l, (_Float16 *)out, lse, d / 8, t8);
+    else
+      hipLaunchKernelGGL(finalize8_kernel<float>, dim3(blocks_for(t8)), dim3(256), 0, s, o_acc, m,
+                         l, (float *)out, lse, d / 8, t8);
+    return hipGetLastError();
+  }
   if (dtype == RA_DT_BF16)
     hipLaunchKernelGGL(finalize_kernel<__bf16>, dim3(blocks_for(total)), dim3(256), 0, s, o_acc, m,
                        l, (__bf16 *)out, lse, d / 4, total);
@@ -209,7 +282,12 @@ hipError_t launch_layout_move(bool gather, const void *src, void *dst, const int
   const int64_t rows = (int64_t)n_ranks * B * H * n;
   if (rows == 0 || row_bytes == 0) return hipSuccess;
   const bool vec = (row_bytes % 16 == 0) && ((uintptr_t)src % 16 == 0) && ((uintptr_t)dst % 16 == 0);
-  if (vec) {
+  const int64_t ru16 = row_bytes / 16, slabs = (int64_t)n_ranks * B * H;
+  if (vec && slabs <= 65535 && n * ru16 < (int64_t)1 << 31) {
+    const dim3 grid((unsigned)((n * ru16 + 255) / 256), (unsigned)slabs);
+    hipLaunchKernelGGL(move16_kernel, grid, dim3(256), 0, s, gather, (const u32x4v *)src,
+                       (u32x4v *)dst, fwd, B * H, S, n, (uint32_t)ru16, rank0);
+  } else if (vec) {
     const int64_t ru = row_bytes / 16, total = rows * ru;
     hipLaunchKernelGGL(move_kernel<uint4>, dim3(blocks_for(total)), dim3(256), 0, s, gather,
                        (const uint4 *)src, (uint4 *)dst, fwd, B * H, S, n, ru, rank0, total);

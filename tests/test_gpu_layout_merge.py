@@ -56,6 +56,26 @@ def test_gather_scatter_bit_exact(dtype, d, rank0, n_ranks):
         assert (b[:, :, ~mask] == 7).all()
 
 
+def test_gather_scatter_many_slabs():
+    """More (rank, batch, head) slabs than a 2-D grid's y extent: the 1-D kernel."""
+    import torch
+    B, H, S, R, d = 1, 70000, 4, 4, 8  # 16-byte rows, 4 * 70000 shard slabs
+    n = S // R
+    x = torch.arange(B * H * S * d, dtype=torch.int32).remainder(30011).to(torch.int16)
+    x = x.view(B, H, S, d)
+    of, _ = oracle.layout_maps(rb.LAYOUT_STRIPED, S, R)
+    fwd = torch.from_numpy(of).cuda()
+    xd = x.cuda()
+    xs = torch.zeros((R, B, H, n, d), dtype=torch.int16, device="cuda")
+    rb.ra_layout_gather(xd, xs, fwd, R, 0, R)
+    xn = x.numpy()
+    expect = np.stack([xn[:, :, of[k * n:(k + 1) * n]] for k in range(R)])
+    assert np.array_equal(xs.cpu().numpy(), expect)
+    back = torch.zeros_like(xd)
+    rb.ra_layout_scatter(xs, back, fwd, R, 0, R)
+    assert torch.equal(back.cpu(), x)
+
+
 def _partials(rows, d, seed, empty_frac=0.1):
     rng = np.random.default_rng(seed)
     o = rng.standard_normal((rows, d)).astype(np.float32)
@@ -90,12 +110,15 @@ def test_merge_matches_oracle(rows, d):
     assert (go[~fin] == 0).all() and (gl[~fin] == 0).all()
 
 
+# (rows, d, output offset in elements): d % 8 == 0 with a 16-byte aligned output
+# takes the 8-wide kernel, the others the 4-wide one
+@pytest.mark.parametrize("rows,d,off", [(513, 128, 0), (77, 64, 0), (300, 12, 0), (129, 128, 1)])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-def test_finalize(dtype):
+def test_finalize(dtype, rows, d, off):
     import torch
-    rows, d = 513, 128
     o, m, l = _partials(rows, d, 3)
-    out = torch.empty((rows, d), dtype=parity.torch_dtype(dtype), device="cuda")
+    buf = torch.empty(rows * d + off, dtype=parity.torch_dtype(dtype), device="cuda")
+    out = buf[off:].view(rows, d)
     lse = torch.empty(rows, dtype=torch.float32, device="cuda")
     rb.ra_finalize(torch.from_numpy(o).cuda(), torch.from_numpy(m).cuda(),
                    torch.from_numpy(l).cuda(), out, lse)
