@@ -242,28 +242,24 @@ __global__ void __launch_bounds__(kKW * 64) bwd_kv_kernel(BwdParams P) {
     if (DK) r_nD = rsrc(P.nD + moff, (int64_t)p.nq * 4);
   };
   set_head(0);
-  // The next tile of the walk into `stage`, in three parts issued at three
-  // points of an iteration (a burst of a whole tile's loads stalls issue).
-  auto issue = [&](const int stage, const int part) {
+  // The next tile of the walk into `stage` (rows, the packed tile, the row
+  // statistics), issued right after the barrier by the loading waves; then
+  // the walk advances (every wave keeps it, only the loaders use it).
+  auto issue = [&](const int stage) {
     char *st = lds + stage * ST;
     const uint32_t so = (uint32_t)iss_qt * kBT * rowb;
-    if (part == 0) {
-      if (wave < kLW) {
-        load_tile<RB, kBT, kLW>(st, r_q, rowb, vo_r, so, wave);
-        if (DK) load_tile<RB, kBT, kLW>(st + TQ, r_do, rowb, vo_r, so, wave);
-      }
-    } else if (part == 1) {
-      if (wave < kLW) load_tile<TB, D, kLW>(st + OFF_T, r_t, TB, vo_t, (uint32_t)iss_qt * TT, wave);
-    } else {
-      if (wave == 0) {
-        dma4b(r_nl, (lds_void *)(st + OFF_NL), lane * 4, (uint32_t)iss_qt * kBT * 4);
-        if (DK)
-          dma4b(r_nD, (lds_void *)(st + OFF_NL + kBT * 4), lane * 4, (uint32_t)iss_qt * kBT * 4);
-      }
-      if (++iss_qt == nqt) {
-        iss_qt = qt0;
-        if (++iss_hq < G) set_head(iss_hq);
-      }
+    if (wave < kLW) {
+      load_tile<RB, kBT, kLW>(st, r_q, rowb, vo_r, so, wave);
+      if (DK) load_tile<RB, kBT, kLW>(st + TQ, r_do, rowb, vo_r, so, wave);
+      load_tile<TB, D, kLW>(st + OFF_T, r_t, TB, vo_t, (uint32_t)iss_qt * TT, wave);
+    }
+    if (wave == 0) {
+      dma4b(r_nl, (lds_void *)(st + OFF_NL), lane * 4, (uint32_t)iss_qt * kBT * 4);
+      if (DK) dma4b(r_nD, (lds_void *)(st + OFF_NL + kBT * 4), lane * 4, (uint32_t)iss_qt * kBT * 4);
+    }
+    if (++iss_qt == nqt) {
+      iss_qt = qt0;
+      if (++iss_hq < G) set_head(iss_hq);
     }
   };
 
@@ -275,7 +271,7 @@ __global__ void __launch_bounds__(kKW * 64) bwd_kv_kernel(BwdParams P) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     const bool more = f + 1 < nf;
-    if (more) issue((f + 1) & 1, 0);
+    if (more) issue((f + 1) & 1);
     const char *st = lds + (f & 1) * ST;
     const char *sQ = st, *sdO = st + TQ, *sT = st + OFF_T;
     const float *sNl = (const float *)(st + OFF_NL);
@@ -344,7 +340,6 @@ __global__ void __launch_bounds__(kKW * 64) bwd_kv_kernel(BwdParams P) {
         if (DK) dP = M::mma(ao[ib][DK ? ks : 0], vB[DK ? ks : 0], dP);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (ib == 0 && more) issue((f + 1) & 1, 1);
       auto elem = [&](const int g) {  // group g: registers 8g .. 8g+7, packed B operand
         f32x16 v;
 #pragma unroll
@@ -381,7 +376,6 @@ __global__ void __launch_bounds__(kKW * 64) bwd_kv_kernel(BwdParams P) {
     };
     if (DK) {
       half(0);
-      if (more) issue((f + 1) & 1, 2);
       half(1);
       return;
     }
@@ -426,7 +420,6 @@ __global__ void __launch_bounds__(kKW * 64) bwd_kv_kernel(BwdParams P) {
       Sv[0] = M::mma(aq[0][ks], kB[ks], Sv[0]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) issue((f + 1) & 1, 1);
     init_s(1);
     // phase 1
     f32x16 pv;
@@ -440,7 +433,6 @@ __global__ void __launch_bounds__(kKW * 64) bwd_kv_kernel(BwdParams P) {
       for (int u8 = (8 * ks) / KS; u8 < (8 * (ks + 1)) / KS; ++u8) pv[u8] = pe_of(0, 0, u8);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) issue((f + 1) & 1, 2);
     s16x8 cur = M::pack(pv, 0);
     // phases 2..5: group gi's MFMAs, two elements of group gi + 1 per MFMA
 #pragma unroll
@@ -464,11 +456,7 @@ __global__ void __launch_bounds__(kKW * 64) bwd_kv_kernel(BwdParams P) {
   // causal diagonal; a tile where the wave sees nothing runs fully masked, so
   // the accumulator stays on one path) and then a run of full ones: two loops
   // with one body each keep the mask code out of the full tiles.
-  if (nf > 0) {
-    issue(0, 0);
-    issue(0, 1);
-    issue(0, 2);
-  }
+  if (nf > 0) issue(0);
   int f = 0, qt = qt0;  // qt: query tile of iteration f
   auto next = [&]() {
     ++f;
@@ -570,18 +558,14 @@ __global__ void __launch_bounds__(kQW * 64) bwd_dq_kernel(BwdParams P) {
              tr = rsrc(kT, (int64_t)D * nk_pad * 2);
   const uint32_t vo_k = tile_voff<RB>(rowb, wave, lane), vo_v = tile_voff<RB>(vrowb, wave, lane),
                  vo_t = tile_voff<TB>(TB, wave, lane);
-  // tile t into `stage`, in three parts issued at three points of an
-  // iteration (a burst of a whole tile's loads stalls instruction issue),
-  // by the loading waves only
-  auto issue = [&](int t, int stage, int part) {
+  // tile t into `stage` (K rows, V rows, packed K^T), issued right after the
+  // barrier by the loading waves only
+  auto issue = [&](int t, int stage) {
     if (wave >= kLW) return;
     char *st = lds + stage * ST;
-    if (part == 0)
-      load_tile<RB, kBT, kLW>(st, kr, rowb, vo_k, (uint32_t)t * kBT * rowb, wave);
-    else if (part == 1)
-      load_tile<RB, kBT, kLW>(st + TQ, vr, vrowb, vo_v, (uint32_t)t * kBT * vrowb, wave);
-    else
-      load_tile<TB, D, kLW>(st + 2 * TQ, tr, TB, vo_t, (uint32_t)t * TT, wave);
+    load_tile<RB, kBT, kLW>(st, kr, rowb, vo_k, (uint32_t)t * kBT * rowb, wave);
+    load_tile<RB, kBT, kLW>(st + TQ, vr, vrowb, vo_v, (uint32_t)t * kBT * vrowb, wave);
+    load_tile<TB, D, kLW>(st + 2 * TQ, tr, TB, vo_t, (uint32_t)t * TT, wave);
   };
 
   f32x16 dQt[DT];
@@ -600,14 +584,8 @@ __global__ void __launch_bounds__(kQW * 64) bwd_dq_kernel(BwdParams P) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     const bool more = t + 1 < ntiles;
-    if (more) issue(t + 1, (t + 1) & 1, 0);
-    if (MODE == 0) {
-      if (more) {
-        issue(t + 1, (t + 1) & 1, 1);
-        issue(t + 1, (t + 1) & 1, 2);
-      }
-      return;
-    }
+    if (more) issue(t + 1, (t + 1) & 1);
+    if (MODE == 0) return;
     const char *st = lds + (t & 1) * ST;
     const char *sK = st, *sV = st + TQ, *sKT = st + 2 * TQ;
     const int j0 = t * kBT;
@@ -646,7 +624,6 @@ __global__ void __launch_bounds__(kQW * 64) bwd_dq_kernel(BwdParams P) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) issue(t + 1, (t + 1) & 1, 1);
     // group kq (16 keys: half kq/2, registers 8(kq%2) .. +7): dS^T packed
     auto elem = [&](int kq) {
       const int kb = kq >> 1, e0 = 8 * (kq & 1);
@@ -674,18 +651,13 @@ __global__ void __launch_bounds__(kQW * 64) bwd_dq_kernel(BwdParams P) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) dQt[dt] = M::mma(ct[kq][dt], cur, dQt[dt]);
       if (kq + 1 < 4) cur = elem(kq + 1);
-      if (kq == 1 && more) issue(t + 1, (t + 1) & 1, 2);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   // the wave's tiles come as full ones, then diagonal / ragged ones, then
   // ones it has nothing in: one loop per kind keeps the mask code out of the
   // full tiles
-  if (ntiles > 0) {
-    issue(0, 0, 0);
-    issue(0, 0, 1);
-    issue(0, 0, 2);
-  }
+  if (ntiles > 0) issue(0, 0);
   const int nfull = min(nfull_w, ntiles_w);
   int t = 0;
   for (; t < nfull; ++t) step(t, std::integral_constant<int, 2>());
