@@ -368,6 +368,11 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
             ka[d][kh] = *(const s16x8 *)(stn + koff[d] + kh * 32 * KROW);
         float ls = 0.f;
         f32x16 pbuf;
+        // While a wave interleaves QK with the exponentials it takes issue
+        // priority over the other wave of its SIMD, whose PV phase is MFMAs
+        // only and fills the MFMA pipe around it (3 % faster than equal
+        // priorities; priority during PV instead is slower).
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int step = 0; step < NSTEP; ++step) {
           const int ks = step >> 1, kh = step & 1;
@@ -392,6 +397,7 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
         if (!EXACT) {
           // a probability above 2^kTau means a new maximum: rescale and redo
           if (wave_any(ls > kSumLimit)) {
