@@ -106,11 +106,15 @@ def cpu_baseline(w, data, layout_code, seconds_target, seed=4242):
     orc.set_threads(1)
     dt1, k1 = run(4)
     orc.set_threads(cores)
-    dt0, k0 = run(max(cores, 8))
+    dt0, k0 = run(max(2 * cores, 8))
     per_key = dt0 / max(k0, 1.0)
     avg_keys = (w.S / 2) if w.causal else w.S
-    rows = int(max(cores, min(4096, seconds_target / (per_key * avg_keys))))
+    cap = 8192
+    rows = int(max(cores, min(cap, seconds_target / (per_key * avg_keys))))
     dt, keys = run(rows)
+    if dt < 0.6 * seconds_target and rows < cap:  # the small calibration ran slow: resize once
+        rows = int(max(cores, min(cap, rows * seconds_target / max(dt, 1e-3))))
+        dt, keys = run(rows)
     flops = 4.0 * w.d * keys
     total_pairs = w.metric_flops() / (4.0 * w.d)
     model = ""
