@@ -228,3 +228,77 @@ def test_decode_workspace(lib):
     assert need >= 8 * rows * (128 + 2) * 4  # at least one partial (O, m, l) per rank and row
     assert lib.ra_decode_fwd(ctypes.byref(a), ctypes.c_void_p(4096), need - 1, None) == 5
     assert lib.ra_decode_fwd(ctypes.byref(a), ctypes.c_void_p(4096 + 16), need, None) == 5
+
+
+def _block_bwd(**kw):
+    a = rb.BlockBwdArgs()
+    for f in ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"):
+        setattr(a, f, 4096)
+    a.dtype, a.B, a.Hq, a.Hkv, a.n_q, a.n_k, a.d = rb.DT_BF16, 1, 4, 2, 300, 200, 128
+    a.scale, a.causal = 0.088, 1
+    a.q_gid0, a.q_gid_step, a.k_gid0, a.k_gid_step = 0, 1, 0, 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dtype", rb.DT_FP32, 6), ("dtype", 9, 3), ("d", 96, 2), ("Hkv", 3, 2), ("B", 0, 2),
+    ("n_q", -1, 2), ("n_k", (1 << 23) + 1, 6), ("q_gid_step", 0, 1), ("scale", 0.0, 1),
+    ("dout", 0, 1), ("lse", 0, 1), ("dk", 0, 1), ("dq", 4100, 4), ("v", 4104, 4),
+])
+def test_block_bwd_rejects(lib, field, value, status):
+    a = _block_bwd(**{field: value})
+    st = lib.ra_block_bwd(ctypes.byref(a), ctypes.c_void_p(4096), 1 << 40, None)
+    assert st == status, (st, rb.last_error())
+    assert lib.ra_block_bwd_workspace_size(ctypes.byref(a)) == 0
+
+
+def test_block_bwd_workspace_and_empty(lib):
+    a = _block_bwd()
+    need = lib.ra_block_bwd_workspace_size(ctypes.byref(a))
+    # packed Q^T and dO^T (300 rows padded to 320), packed K^T (200 -> 256), -D and nl per row
+    assert need >= 2 * 4 * 128 * 320 * 2 + 2 * 128 * 256 * 2 + 2 * 4 * 300 * 4
+    assert lib.ra_block_bwd(ctypes.byref(a), None, need, None) == 5
+    assert lib.ra_block_bwd(ctypes.byref(a), ctypes.c_void_p(4096), need - 1, None) == 5
+    assert lib.ra_block_bwd(ctypes.byref(a), ctypes.c_void_p(4096 + 16), need, None) == 5
+    # no query rows: nothing to do, no workspace or tensors needed
+    e = _block_bwd(n_q=0, q=0, o=0, dout=0, lse=0, dq=0)
+    assert lib.ra_block_bwd(ctypes.byref(e), None, 0, None) == 0
+
+
+def _ring_bwd(**kw):
+    a = rb.RingBwdArgs()
+    for f in ("q_sh", "k_sh", "v_sh", "o_sh", "dout_sh", "lse", "dq_sh", "dk_sh", "dv_sh"):
+        setattr(a, f, 4096)
+    a.dtype, a.R, a.rank0, a.n_ranks = rb.DT_BF16, 8, 0, 8
+    a.B, a.Hq, a.Hkv, a.n, a.d = 1, 4, 2, 256, 128
+    a.scale, a.causal, a.layout = 0.088, 1, rb.LAYOUT_STRIPED
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dtype", rb.DT_FP32, 6), ("dtype", 9, 3), ("layout", 5, 1), ("R", 0, 2), ("n_ranks", 9, 2),
+    ("rank0", 1, 2), ("d", 32, 2), ("Hkv", 3, 2), ("n", (1 << 23) + 2, 6),
+    ("scale", float("inf"), 1), ("dout_sh", 0, 1), ("lse", 0, 1), ("dv_sh", 4104, 4),
+])
+def test_ring_bwd_rejects(lib, field, value, status):
+    a = _ring_bwd(**{field: value})
+    st = lib.ra_ring_bwd(ctypes.byref(a), ctypes.c_void_p(4096), 1 << 40, None)
+    assert st == status, (st, rb.last_error())
+    assert lib.ra_ring_bwd_workspace_size(ctypes.byref(a)) == 0
+
+
+def test_ring_bwd_zigzag_needs_even_blocks_and_workspace(lib):
+    odd = _ring_bwd(layout=rb.LAYOUT_ZIGZAG, n=255)
+    assert lib.ra_ring_bwd(ctypes.byref(odd), ctypes.c_void_p(4096), 1 << 40, None) == 2
+    a = _ring_bwd()
+    need = lib.ra_ring_bwd_workspace_size(ctypes.byref(a))
+    rows = 8 * 1 * 4 * 256
+    # fp32 dq of the computed rows and dk, dv of every block, plus the per-row -D and nl
+    assert need >= rows * 128 * 4 + 2 * 8 * 1 * 2 * 256 * 128 * 4 + 2 * rows * 4
+    assert lib.ra_ring_bwd(ctypes.byref(a), None, need, None) == 5
+    assert lib.ra_ring_bwd(ctypes.byref(a), ctypes.c_void_p(4096), need - 1, None) == 5
+    assert lib.ra_ring_bwd(ctypes.byref(a), ctypes.c_void_p(4096 + 16), need, None) == 5
