@@ -286,8 +286,8 @@ def rb_ring_bwd(ra):
 
 def rank_share_bench(torch, rb, RingAttention, w, iters=3):
     """Each rank's share of a ring run alone (w: causal MHA 32k, R = 8), for the
-    contiguous and striped layouts: the measured counterpart of the per-rank
-    causal work counts.  Times ra_ring_fwd for one computed rank (R hops, SWAP
+    contiguous, striped and zig-zag layouts: the measured counterpart of the
+    per-rank causal work counts.  Times ra_ring_fwd for one computed rank (R hops, SWAP
     hand-off, fused fold) after its shards are gathered; device-side random
     inputs of the workload's shape."""
     tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
@@ -299,7 +299,9 @@ def rank_share_bench(torch, rb, RingAttention, w, iters=3):
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.Hq, w.S, device="cuda")
     out = {}
-    for layout in ("contiguous", "striped"):
+    for layout in ("contiguous", "striped", "zigzag"):
+        if layout == "zigzag" and w.S % (2 * w.R):
+            continue
         ms = []
         for r in range(w.R):
             ra = RingAttention(w.B, w.Hq, w.Hkv, w.S, w.d, w.R, layout, tdt, w.causal, w.scale,
