@@ -263,8 +263,9 @@ __global__ void __launch_bounds__(kKW * 64) bwd_kv_kernel(BwdParams P) {
     }
   };
 
-  // Iteration f: tile f has landed (this wave's loads, then everyone's) and
-  // stage (f+1)&1, last read in iteration f-1, takes tile f+1.  FULL: every
+  // Iteration f: tile f has landed (each loading wave waits for its own
+  // loads, then the barrier) and stage (f+1)&1, last read in iteration f-1,
+  // takes tile f+1.  FULL: every
   // query of the tile sees every key of the wave.
   auto step = [&](const int f, const int qt, auto full_c) {
     constexpr bool FULL = decltype(full_c)::value;
