@@ -23,6 +23,7 @@ CASES = [
     ("empty_block", 1, 2, 2, 100, 128, True, 0, 1, 1000, 1),
     ("noncausal_ragged", 2, 2, 2, 130, 520, False, 0, 1, 0, 1),
     ("gqa_4to1", 1, 8, 2, 384, 384, True, 0, 1, 0, 1),
+    ("two_tiles_ragged", 1, 2, 2, 100, 100, True, 0, 1, 0, 1),
     ("tiny", 1, 1, 1, 1, 1, True, 0, 1, 0, 1),
     ("no_keys", 1, 2, 2, 70, 0, True, 0, 1, 0, 1),
 ]
