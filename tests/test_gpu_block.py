@@ -22,6 +22,7 @@ CASES = [
     ("noncausal_ragged", 2, 2, 2, 130, 520, False, 0, 1, 0, 1),
     ("gqa_4to1", 1, 8, 2, 384, 384, True, 0, 1, 0, 1),
     ("two_tiles_ragged", 1, 2, 2, 100, 100, True, 0, 1, 0, 1),
+    ("gqa_8to1_ragged", 1, 8, 1, 130, 130, True, 0, 1, 0, 1),
     ("tiny", 1, 1, 1, 1, 1, True, 0, 1, 0, 1),
     ("no_keys", 1, 2, 2, 70, 0, True, 0, 1, 0, 1),
 ]
