@@ -250,7 +250,11 @@ def overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse, t_c
 def backward_bench(torch, ra, w, layout_code, q, k, v, iters=2):
     """ra_ring_bwd after the forward ring (same shards): MFMA roofline with the
     algorithmic count of the backward, 10*d FLOP per allowed pair per query head
-    (S = QK^T, dP = dO V^T, dV, dK, dQ; recomputing S and dP for dQ is not credited)."""
+    (S = QK^T, dP = dO V^T, dV, dK, dQ; recomputing S and dP for dQ is not credited).
+    Also how much of the backward hand-off (K, V, transposed K and the fp32 dK/dV
+    accumulators travelling with each block) the compute hides: the pass with
+    blocks read and accumulated in place (SWAP), and the hop copies alone."""
+    from long_context_exact_block_amd import binding as rb
     tdt = q.dtype
     g = torch.Generator(device="cuda")
     g.manual_seed(w.seed + 7)
@@ -259,20 +263,55 @@ def backward_bench(torch, ra, w, layout_code, q, k, v, iters=2):
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     ra.backward(dout, dq, dk, dv)  # warm-up, allocates the workspace
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
-    torch.cuda.synchronize()
-    ev[0].record()
-    for i in range(iters):
+
+    def timed(handoff):
+        ra.bargs.handoff = handoff
         rb_ring_bwd(ra)
-        ev[i + 1].record()
-    torch.cuda.synchronize()
-    ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(iters)])
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(iters):
+            rb_ring_bwd(ra)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(iters)])
+
+    handoff0 = ra.bargs.handoff
+    ms = timed(handoff0)
+    handoff = None
+    if handoff0 == rb.HANDOFF_COPY and w.R > 1:
+        ms_swap = timed(rb.HANDOFF_SWAP)
+        ra.bargs.handoff = handoff0
+        kz = w.B * w.Hkv * w.n * w.d
+        n_pad = (w.n + 63) // 64 * 64
+        per_hop = w.ranks * (2 * kz * 2 + 2 * w.B * w.Hkv * w.d * n_pad + 2 * kz * 4)
+        home = w.ranks * 2 * kz * 4
+        src = torch.empty(per_hop, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        rb.ra_handoff_copy(dst, src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        c0.record()
+        for _ in range(w.R - 1):
+            rb.ra_handoff_copy(dst, src)
+        rb.ra_handoff_copy(dst, src, home)
+        c1.record()
+        torch.cuda.synchronize()
+        t_copies = c0.elapsed_time(c1)
+        del src, dst
+        t_copy, t_swap = float(np.median(ms)), float(np.median(ms_swap))
+        moved = 2.0 * (per_hop * (w.R - 1) + home)
+        handoff = {"ms_copy": round(t_copy, 3), "ms_swap": round(t_swap, 3),
+                   "copies_alone_ms": round(t_copies, 3), "bytes_per_hop": per_hop,
+                   "copy_GB/s": round(moved / (t_copies * 1e-3) / 1e9, 1),
+                   "overlap": round(1.0 - (t_copy - t_swap) / t_copies, 3) if t_copies > 0 else None}
     pairs = sum(hop_pairs(w, layout_code))
     flops = 10.0 * w.d * w.B * w.Hq * pairs
     med = float(np.median(ms))
     tf = flops / (med * 1e-3) / 1e12
     del dout, dq, dk, dv
     return {"ms_median": round(med, 3), "ms_min": round(float(ms.min()), 3),
+            "handoff": handoff,
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                          "algorithmic_flops": flops,
@@ -281,7 +320,7 @@ def backward_bench(torch, ra, w, layout_code, q, k, v, iters=2):
 
 def rb_ring_bwd(ra):
     from long_context_exact_block_amd import binding as rb
-    rb.ra_ring_bwd(ra.bargs, ra.bworkspace)
+    rb.ra_ring_bwd(ra.bargs, ra.bworkspace, None, ra.copy_stream)
 
 
 def rank_share_bench(torch, rb, RingAttention, w, iters=3):

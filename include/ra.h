@@ -321,11 +321,18 @@ ra_status ra_block_bwd(const ra_block_bwd_args *a, void *workspace, size_t works
  * ra_ring_bwd -- the backward pass over the whole ring on one GPU: every
  * computed query rank r meets the block of source rank s = (r - h) mod R at
  * hop h (as in ra_ring_fwd) and adds that pair's gradient contributions; dQ
- * stays with its rank, dK/dV belong to the block (on several GPUs they
- * travel with K and V and arrive home after R hops; here the blocks are read
- * in place and their gradients accumulated in place).
+ * stays with its rank, dK/dV belong to the block and travel with it ([ZZ]:
+ * each rank passes on what it holds while it computes).
  *   q_sh, k_sh, v_sh, R, rank0, n_ranks, B, Hq, Hkv, n, d, scale, causal,
  *   layout: as in ra_ring_args (16-bit dtypes only)
+ *   handoff COPY: before hop h+1 each computed rank's receive buffers are
+ *     filled on the `copy` stream with what its ring predecessor held at hop
+ *     h: K, V and the transposed K while hop h computes, then the block's
+ *     fp32 dK/dV accumulators once hop h's kernels are done (they arrive
+ *     while hop h+1's dQ kernel runs); a block leaving the computed ranks
+ *     (or the ring's end) puts its accumulators back home.  SWAP reads and
+ *     accumulates every block in place.  Both give bitwise-identical results.
+ *     Stream ordering as in ra_ring_fwd (same stream twice is allowed).
  *   o_sh, dout_sh  device [n_ranks][B][Hq][n][d]: the forward's O and the
  *                  upstream gradient of the computed ranks
  *   lse            device fp32 [n_ranks][B][Hq][n]: the forward's LSE
@@ -333,7 +340,8 @@ ra_status ra_block_bwd(const ra_block_bwd_args *a, void *workspace, size_t works
  *   dk_sh, dv_sh   device [R][B][Hkv][n][d] in dtype (written): gradients of
  *                  every source block from the computed query ranks
  * Workspace: ra_ring_bwd_workspace_size bytes, 256-byte aligned (transposed
- * copies of Q, dO, K; D and -lse log2(e) per query row; fp32 accumulators).  Asynchronous on `stream`.
+ * copies of Q, dO, K; D and -lse log2(e) per query row; fp32 accumulators;
+ * with COPY the two receive buffers).  Asynchronous on the streams.
  * Errors: as ra_ring_fwd, plus RA_ERR_UNSUPPORTED for fp32.
  */
 typedef struct {
@@ -345,12 +353,13 @@ typedef struct {
   float scale;
   int32_t causal;
   int32_t layout;
+  int32_t handoff; /* ra_handoff */
   void *dq_sh, *dk_sh, *dv_sh;
 } ra_ring_bwd_args;
 
 size_t ra_ring_bwd_workspace_size(const ra_ring_bwd_args *a);
 ra_status ra_ring_bwd(const ra_ring_bwd_args *a, void *workspace, size_t workspace_bytes,
-                      ra_stream stream);
+                      ra_stream compute, ra_stream copy);
 
 /*
  * ra_decode_fwd -- nq new query tokens against a KV cache split over R ranks:

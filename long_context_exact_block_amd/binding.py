@@ -77,7 +77,8 @@ class RingBwdArgs(ctypes.Structure):
     _fields_ = [("q_sh", P), ("k_sh", P), ("v_sh", P), ("o_sh", P), ("dout_sh", P), ("lse", P),
                 ("dtype", I32), ("R", I32), ("rank0", I32), ("n_ranks", I32), ("B", I32),
                 ("Hq", I32), ("Hkv", I32), ("n", I32), ("d", I32), ("scale", ctypes.c_float),
-                ("causal", I32), ("layout", I32), ("dq_sh", P), ("dk_sh", P), ("dv_sh", P)]
+                ("causal", I32), ("layout", I32), ("handoff", I32), ("dq_sh", P), ("dk_sh", P),
+                ("dv_sh", P)]
 
 
 _lib = None
@@ -105,7 +106,7 @@ def lib():
     L.ra_block_bwd.argtypes = [ctypes.POINTER(BlockBwdArgs), P, ctypes.c_size_t, P]
     L.ra_ring_bwd_workspace_size.argtypes = [ctypes.POINTER(RingBwdArgs)]
     L.ra_ring_bwd_workspace_size.restype = ctypes.c_size_t
-    L.ra_ring_bwd.argtypes = [ctypes.POINTER(RingBwdArgs), P, ctypes.c_size_t, P]
+    L.ra_ring_bwd.argtypes = [ctypes.POINTER(RingBwdArgs), P, ctypes.c_size_t, P, P]
     L.ra_decode_fwd_workspace_size.argtypes = [ctypes.POINTER(DecodeArgs)]
     L.ra_decode_fwd_workspace_size.restype = ctypes.c_size_t
     L.ra_decode_fwd.argtypes = [ctypes.POINTER(DecodeArgs), P, ctypes.c_size_t, P]
@@ -311,7 +312,7 @@ def ra_block_bwd(args: BlockBwdArgs, workspace, stream=None):
 
 
 def ring_bwd_args(q_sh, k_sh, v_sh, o_sh, dout_sh, lse, dq_sh, dk_sh, dv_sh, R, rank0, n_ranks,
-                  scale, causal, layout) -> RingBwdArgs:
+                  scale, causal, layout, handoff=HANDOFF_COPY) -> RingBwdArgs:
     """Shards as for ra_ring_fwd: q_sh, o_sh, dout_sh, dq_sh [n_ranks][B][Hq][n][d];
     k_sh, v_sh, dk_sh, dv_sh [R][B][Hkv][n][d]; lse fp32 [n_ranks][B][Hq][n]."""
     _, B, Hq, n, d = q_sh.shape
@@ -324,6 +325,7 @@ def ring_bwd_args(q_sh, k_sh, v_sh, o_sh, dout_sh, lse, dq_sh, dk_sh, dv_sh, R, 
     a.B, a.Hq, a.Hkv, a.n, a.d = B, Hq, Hkv, n, d
     a.scale, a.causal = float(scale), int(bool(causal))
     a.layout = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    a.handoff = int(handoff)
     a.dq_sh, a.dk_sh, a.dv_sh = _ptr(dq_sh), _ptr(dk_sh), _ptr(dv_sh)
     return a
 
@@ -335,10 +337,12 @@ def ra_ring_bwd_workspace_size(args: RingBwdArgs) -> int:
     return nb
 
 
-def ra_ring_bwd(args: RingBwdArgs, workspace, stream=None):
+def ra_ring_bwd(args: RingBwdArgs, workspace, compute_stream=None, copy_stream=None):
     ws_ptr = _ptr(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib().ra_ring_bwd(ctypes.byref(args), ws_ptr, ws_bytes, _stream(stream)))
+    cs = _stream(compute_stream)
+    xs = _stream(copy_stream) if copy_stream is not None else cs
+    _check(lib().ra_ring_bwd(ctypes.byref(args), ws_ptr, ws_bytes, cs, xs))
 
 
 def decode_args(q, k, vp, o, lse, scale, causal, q_gid0) -> DecodeArgs:

@@ -71,23 +71,66 @@ ra_status hip_fail(hipError_t e, const char *what) {
 
 constexpr int64_t kMaxI32 = 2147483647;
 
-// Events used by the ring driver, created once per (thread, device) and
-// reused by later calls on the same thread.
-std::vector<hipEvent_t> *event_pool(int device, size_t need, hipError_t *err) {
-  static thread_local std::map<int, std::vector<hipEvent_t>> pools;
-  auto &v = pools[device];
-  while (v.size() < need) {
-    hipEvent_t e;
-    hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
-    if (r != hipSuccess) {
-      *err = r;
-      return nullptr;
+// Events with which the ring drivers order their two streams.  A call leases
+// a set while it enqueues its work and hands it back when it returns: a
+// stream wait binds to the record that precedes it, so the same events can
+// serve the next call at once.  Sets are cached per device behind a mutex --
+// as many sets as calls ever ran at the same time -- and kept until the
+// process ends (destroying them at exit could outlive the HIP runtime).
+class EventSets {
+ public:
+  hipError_t acquire(int dev, size_t n, std::vector<hipEvent_t> *out) {
+    {
+      std::lock_guard<std::mutex> g(mu_);
+      auto &fl = free_[dev];
+      if (!fl.empty()) {
+        *out = std::move(fl.back());
+        fl.pop_back();
+      }
     }
-    v.push_back(e);
+    while (out->size() < n) {
+      hipEvent_t e;
+      const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+      if (r != hipSuccess) return r;
+      out->push_back(e);
+      std::lock_guard<std::mutex> g(mu_);
+      ++created_;
+    }
+    return hipSuccess;
   }
-  *err = hipSuccess;
-  return &v;
+  void release(int dev, std::vector<hipEvent_t> *ev) {
+    if (ev->empty()) return;
+    std::lock_guard<std::mutex> g(mu_);
+    free_[dev].push_back(std::move(*ev));
+    ev->clear();
+  }
+  size_t created() {
+    std::lock_guard<std::mutex> g(mu_);
+    return created_;
+  }
+
+ private:
+  std::mutex mu_;
+  std::map<int, std::vector<std::vector<hipEvent_t>>> free_;
+  size_t created_ = 0;
+};
+
+EventSets &event_sets() {
+  static EventSets *sets = new EventSets;  // intentionally never destroyed
+  return *sets;
 }
+
+// A leased event set, handed back on every exit path of the call.
+struct EventLease {
+  int dev = 0;
+  std::vector<hipEvent_t> ev;
+  ~EventLease() { event_sets().release(dev, &ev); }
+  hipError_t acquire(size_t n) {
+    hipError_t r = hipGetDevice(&dev);
+    if (r != hipSuccess) return r;
+    return event_sets().acquire(dev, n, &ev);
+  }
+};
 
 struct WsLayout {
   size_t vpack, kbuf[2], vbuf[2], o_acc, m_acc, l_acc, o_blk, m_blk, l_blk, total;
@@ -200,6 +243,8 @@ ra_status check_ring_bwd(const ra_ring_bwd_args *a) {
     return fail(RA_ERR_DTYPE, "unknown dtype %d", a->dtype);
   }
   if (!known_layout(a->layout)) return fail(RA_ERR_INVALID_ARG, "unknown layout %d", a->layout);
+  if (a->handoff != RA_HANDOFF_COPY && a->handoff != RA_HANDOFF_SWAP)
+    return fail(RA_ERR_INVALID_ARG, "unknown handoff %d", a->handoff);
   if (a->R < 1) return fail(RA_ERR_SHAPE, "R must be >= 1 (got %d)", a->R);
   if (a->n_ranks < 1 || a->n_ranks > a->R || a->rank0 < 0 || a->rank0 + a->n_ranks > a->R)
     return fail(RA_ERR_SHAPE, "ranks [rank0, rank0+n_ranks) must lie in [0, R)");
@@ -228,6 +273,9 @@ ra_status check_ring_bwd(const ra_ring_bwd_args *a) {
 
 struct RingBwdWs {
   size_t qT, doT, kT, D, nl, dq, dk, dv, total;
+  // COPY hand-off: two receive buffers (n_ranks blocks each) for K, V, packed
+  // K^T and the fp32 dK, dV accumulators that travel with the block
+  size_t kbuf[2], vbuf[2], kTbuf[2], dkbuf[2], dvbuf[2];
 };
 RingBwdWs ring_bwd_ws(const ra_ring_bwd_args *a) {
   RingBwdWs w{};
@@ -248,6 +296,16 @@ RingBwdWs ring_bwd_ws(const ra_ring_bwd_args *a) {
   w.dq = take(qrows * a->n * a->d * 4);
   w.dk = take(kblocks * a->n * a->d * 4);
   w.dv = take(kblocks * a->n * a->d * 4);
+  if (a->handoff == RA_HANDOFF_COPY && a->R > 1) {
+    const size_t rblocks = (size_t)a->n_ranks * a->B * a->Hkv;
+    for (int b = 0; b < 2; ++b) {
+      w.kbuf[b] = take(rblocks * a->n * a->d * 2);
+      w.vbuf[b] = take(rblocks * a->n * a->d * 2);
+      w.kTbuf[b] = take(rblocks * a->d * np * 2);
+      w.dkbuf[b] = take(rblocks * a->n * a->d * 4);
+      w.dvbuf[b] = take(rblocks * a->n * a->d * 4);
+    }
+  }
   w.total = off;
   return w;
 }
@@ -651,14 +709,12 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
   char *kb[2] = {ws + L.kbuf[0], ws + L.kbuf[1]};
   char *vb[2] = {ws + L.vbuf[0], ws + L.vbuf[1]};
 
-  int dev = 0;
-  RA_HIP(hipGetDevice(&dev), "hipGetDevice");
-  hipError_t herr;
-  std::vector<hipEvent_t> *ev = event_pool(dev, (size_t)2 * R + 2, &herr);
-  if (!ev) return hip_fail(herr, "hipEventCreate");
-  hipEvent_t ev_entry = (*ev)[0], ev_join = (*ev)[1];
-  auto ev_comp = [&](int h) { return (*ev)[2 + 2 * h]; };
-  auto ev_copy = [&](int h) { return (*ev)[3 + 2 * h]; };
+  EventLease lease;
+  RA_HIP(lease.acquire((size_t)2 * R + 2), "hipEventCreate");
+  const std::vector<hipEvent_t> &ev = lease.ev;
+  hipEvent_t ev_entry = ev[0], ev_join = ev[1];
+  auto ev_comp = [&](int h) { return ev[2 + 2 * h]; };
+  auto ev_copy = [&](int h) { return ev[3 + 2 * h]; };
 
   // V of every source block in the packed layout the block kernel reads
   if (packed)
@@ -877,7 +933,7 @@ size_t ra_ring_bwd_workspace_size(const ra_ring_bwd_args *a) {
 }
 
 ra_status ra_ring_bwd(const ra_ring_bwd_args *a, void *workspace, size_t workspace_bytes,
-                      ra_stream stream) {
+                      ra_stream compute_s, ra_stream copy_s) {
   clear_error();
   ra_status st = check_ring_bwd(a);
   if (st != RA_OK) return st;
@@ -885,15 +941,20 @@ ra_status ra_ring_bwd(const ra_ring_bwd_args *a, void *workspace, size_t workspa
   const RingBwdWs L = ring_bwd_ws(a);
   if (!workspace || workspace_bytes < L.total || (uintptr_t)workspace % 256)
     return fail(RA_ERR_WORKSPACE, "workspace must be >= %zu bytes, 256-byte aligned", L.total);
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = (hipStream_t)compute_s, xs = (hipStream_t)copy_s;
   char *ws = (char *)workspace;
   const int R = a->R, n = a->n, nr = a->n_ranks, r0 = a->rank0;
+  const bool copy = a->handoff == RA_HANDOFF_COPY && R > 1;
   const int64_t d = a->d;
   const bool contig = a->layout == RA_LAYOUT_CONTIGUOUS;
   const int64_t qz = (int64_t)a->B * a->Hq * n * d;   // elements of one query shard
   const int64_t kz = (int64_t)a->B * a->Hkv * n * d;  // elements of one K/V block
   const int64_t n_pad = packed_n(n);
+  const int64_t kTz = (int64_t)a->B * a->Hkv * d * n_pad;  // elements of one packed K^T block
   float *dq = (float *)(ws + L.dq), *dk = (float *)(ws + L.dk), *dv = (float *)(ws + L.dv);
+  EventLease lease;
+  if (copy) RA_HIP(lease.acquire((size_t)3 * R + 2), "hipEventCreate");
+  const std::vector<hipEvent_t> &ev = lease.ev;
   RA_HIP(launch_zero(dq, nr * qz, s), "zero dq");
   RA_HIP(launch_zero(dk, R * kz, s), "zero dk");
   RA_HIP(launch_zero(dv, R * kz, s), "zero dv");
@@ -908,8 +969,6 @@ ra_status ra_ring_bwd(const ra_ring_bwd_args *a, void *workspace, size_t workspa
   BwdParams P{};
   BatchParams &p = P.a;
   p.q = a->q_sh;
-  p.k = a->k_sh;
-  p.v = a->v_sh;
   p.q_zstride = qz;
   p.kv_zstride = kz;
   p.kv_vzstride = kz;
@@ -935,7 +994,6 @@ ra_status ra_ring_bwd(const ra_ring_bwd_args *a, void *workspace, size_t workspa
   p.kg_mult = contig ? n : 1;
   p.k_step = contig ? 1 : R;
   p.kg_smod = R;
-  p.kv_idx_mod = R;
   if (a->layout == RA_LAYOUT_ZIGZAG) {
     p.zz_c = n / 2;
     p.zz_R = R;
@@ -945,22 +1003,153 @@ ra_status ra_ring_bwd(const ra_ring_bwd_args *a, void *workspace, size_t workspa
   P.dout = a->dout_sh;
   P.qT = ws + L.qT;
   P.doT = ws + L.doT;
-  P.kT = ws + L.kT;
   P.qT_zstride = (int64_t)a->B * a->Hq * d * n_pad;
-  P.kT_zstride = (int64_t)a->B * a->Hkv * d * n_pad;
+  P.kT_zstride = kTz;
   P.nl = (const float *)(ws + L.nl);
   P.nD = (const float *)(ws + L.D);
   P.dq = dq;
-  P.dk = dk;
-  P.dv = dv;
   P.dq_zstride = qz;
   P.dk_zstride = kz;
+
+  // One travelling quantity of a block: its copy at home (block index s of a
+  // home array with `bytes` per block) and the two receive buffers (computed
+  // rank k at offset k*bytes).  At hop h computed rank k holds, in COPY mode,
+  // home[(r0 + k) mod R] for h = 0 and buf[(h - 1) & 1][k] after that.
+  struct Part {
+    char *home;
+    char *buf[2];
+    size_t bytes;
+  };
+  const Part parts[5] = {
+      {(char *)a->k_sh, {ws + L.kbuf[0], ws + L.kbuf[1]}, (size_t)kz * 2},
+      {(char *)a->v_sh, {ws + L.vbuf[0], ws + L.vbuf[1]}, (size_t)kz * 2},
+      {ws + L.kT, {ws + L.kTbuf[0], ws + L.kTbuf[1]}, (size_t)kTz * 2},
+      {(char *)dk, {ws + L.dkbuf[0], ws + L.dkbuf[1]}, (size_t)kz * 4},
+      {(char *)dv, {ws + L.dvbuf[0], ws + L.dvbuf[1]}, (size_t)kz * 4}};
+  auto front = [&](const Part &x, int h, int k) -> char * {
+    if (h == 0) return x.home + (size_t)((r0 + k) % R) * x.bytes;
+    return x.buf[(h - 1) & 1] + (size_t)k * x.bytes;
+  };
+  // copies merged into contiguous runs (one launch per run)
+  struct Runs {
+    char *dst = nullptr;
+    const char *src = nullptr;
+    size_t len = 0;
+  };
+  auto add_copy = [&](Runs &r, char *dst, const char *src, size_t bytes) -> ra_status {
+    if (r.len && src == r.src + r.len && dst == r.dst + r.len) {
+      r.len += bytes;
+      return RA_OK;
+    }
+    if (r.len) RA_HIP(launch_copy(r.dst, r.src, r.len, xs), "hand-off copy");
+    r.dst = dst;
+    r.src = src;
+    r.len = bytes;
+    return RA_OK;
+  };
+  auto flush = [&](Runs &r) -> ra_status {
+    if (r.len) RA_HIP(launch_copy(r.dst, r.src, r.len, xs), "hand-off copy");
+    r.len = 0;
+    return RA_OK;
+  };
+  // before hop h+1 rank k receives what its ring predecessor held at hop h:
+  // the front of computed rank k-1, or (predecessor not computed here) the
+  // block's home copy -- where a block's accumulators also wait while it
+  // passes ranks outside the computed set
+  auto hand_off = [&](int h, int first, int last) -> ra_status {
+    for (int pi = first; pi <= last; ++pi) {
+      const Part &x = parts[pi];
+      Runs run;
+      for (int k = 0; k < nr; ++k) {
+        const int r = r0 + k;
+        const int kp = ((r - 1 - r0) % R + R) % R;
+        const char *src = kp < nr ? front(x, h, kp)
+                                  : x.home + (size_t)(((r - 1 - h) % R + R) % R) * x.bytes;
+        if ((st = add_copy(run, x.buf[h & 1] + (size_t)k * x.bytes, src, x.bytes)) != RA_OK)
+          return st;
+      }
+      if ((st = flush(run)) != RA_OK) return st;
+    }
+    return RA_OK;
+  };
+  // accumulators of computed rank k's block go home (it leaves the computed
+  // set, or the ring has ended); at h = 0 the front is the home copy
+  auto send_home = [&](int h, int k) -> ra_status {
+    if (h == 0) return RA_OK;
+    const int src_rank = ((r0 + k - h) % R + R) % R;
+    for (int pi = 3; pi <= 4; ++pi)
+      RA_HIP(launch_copy(parts[pi].home + (size_t)src_rank * parts[pi].bytes, front(parts[pi], h, k),
+                         parts[pi].bytes, xs),
+             "hand-off copy");
+    return RA_OK;
+  };
+
+  hipEvent_t ev_entry = copy ? ev[0] : nullptr, ev_join = copy ? ev[1] : nullptr;
+  auto ev_comp = [&](int h) { return ev[2 + 3 * h]; };     // hop h's kernels done
+  auto ev_kv = [&](int h) { return ev[3 + 3 * h]; };       // K, V, K^T of hop h+1 in place
+  auto ev_acc = [&](int h) { return ev[4 + 3 * h]; };      // dK, dV of hop h+1 in place
+  if (copy) {
+    RA_HIP(hipEventRecord(ev_entry, s), "hipEventRecord");
+    RA_HIP(hipStreamWaitEvent(xs, ev_entry, 0), "hipStreamWaitEvent");
+  }
   for (int h = 0; h < R; ++h) {
-    // hop h: computed rank r0 + z meets the block of source (r0 + z - h) mod R;
-    // within a hop every rank reads (and accumulates into) a different block
+    // hop h: computed rank r0 + z meets the block of source (r0 + z - h) mod R
     p.kg_s0 = ((r0 - h) % R + R) % R;
-    p.kv_idx0 = p.kg_s0;
-    RA_HIP(launch_bwd(P, a->dtype, s), "backward kernels");
+    if (copy) {
+      p.k = front(parts[0], h, 0);
+      p.v = front(parts[1], h, 0);
+      P.kT = front(parts[2], h, 0);
+      P.dk = (float *)front(parts[3], h, 0);
+      P.dv = (float *)front(parts[4], h, 0);
+      p.kv_idx0 = 0;
+      p.kv_idx_mod = h == 0 ? R : nr;
+      if (h == 0) {  // blocks at home: computed rank z holds block (r0 + z) mod R
+        p.k = a->k_sh;
+        p.v = a->v_sh;
+        P.kT = ws + L.kT;
+        P.dk = dk;
+        P.dv = dv;
+        p.kv_idx0 = r0;
+      }
+    } else {  // in place: rank z's block is (kg_s0 + z) mod R of the home arrays
+      p.k = a->k_sh;
+      p.v = a->v_sh;
+      P.kT = ws + L.kT;
+      P.dk = dk;
+      P.dv = dv;
+      p.kv_idx0 = p.kg_s0;
+      p.kv_idx_mod = R;
+    }
+    // dQ needs only the block's K and V; dK/dV also the block's accumulators
+    if (copy && h > 0) RA_HIP(hipStreamWaitEvent(s, ev_kv(h - 1), 0), "hipStreamWaitEvent");
+    RA_HIP(launch_bwd(P, a->dtype, s, kBwdQ), "backward dq kernel");
+    if (copy && h > 0) RA_HIP(hipStreamWaitEvent(s, ev_acc(h - 1), 0), "hipStreamWaitEvent");
+    RA_HIP(launch_bwd(P, a->dtype, s, kBwdKV), "backward dk/dv kernels");
+    if (!copy) continue;
+    RA_HIP(hipEventRecord(ev_comp(h), s), "hipEventRecord");
+    if (h + 1 < R) {
+      // K, V, K^T for hop h+1: read-only this hop, so they move while hop h
+      // computes; the receive buffer was last read by hop h-1
+      if (h >= 1) RA_HIP(hipStreamWaitEvent(xs, ev_comp(h - 1), 0), "hipStreamWaitEvent");
+      if ((st = hand_off(h, 0, 2)) != RA_OK) return st;
+      RA_HIP(hipEventRecord(ev_kv(h), xs), "hipEventRecord");
+      // the accumulators are final for hop h once its kernels are done; they
+      // move during hop h+1's dQ kernel
+      RA_HIP(hipStreamWaitEvent(xs, ev_comp(h), 0), "hipStreamWaitEvent");
+      if ((st = hand_off(h, 3, 4)) != RA_OK) return st;
+      const int next = (r0 + nr) % R;  // the rank after the computed set
+      if (nr < R && !(next >= r0 && next < r0 + nr))
+        if ((st = send_home(h, nr - 1)) != RA_OK) return st;
+      RA_HIP(hipEventRecord(ev_acc(h), xs), "hipEventRecord");
+    } else {
+      RA_HIP(hipStreamWaitEvent(xs, ev_comp(h), 0), "hipStreamWaitEvent");
+      for (int k = 0; k < nr; ++k)
+        if ((st = send_home(h, k)) != RA_OK) return st;
+    }
+  }
+  if (copy) {
+    RA_HIP(hipEventRecord(ev_join, xs), "hipEventRecord");
+    RA_HIP(hipStreamWaitEvent(s, ev_join, 0), "hipStreamWaitEvent");
   }
   RA_HIP(launch_cast(dq, a->dq_sh, a->dtype, nr * qz, s), "cast dq");
   RA_HIP(launch_cast(dk, a->dk_sh, a->dtype, R * kz, s), "cast dk");

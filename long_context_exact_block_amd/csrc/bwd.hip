@@ -724,8 +724,9 @@ __global__ void __launch_bounds__(256) cast_kernel(const float4 *__restrict__ x,
   o[3] = (T)v.w;
 }
 
+// parts: bit 0 the dK/dV kernels, bit 1 the dQ kernel
 template <int D, bool BF16>
-hipError_t launch_bwd_d(const BwdParams &P, hipStream_t s) {
+hipError_t launch_bwd_d(const BwdParams &P, hipStream_t s, int parts) {
   const BatchParams &p = P.a;
   const int64_t groups = (int64_t)p.nz * p.B;
   constexpr size_t lv = 2 * kv_stage_bytes<D, kRoleV>(), lk = 2 * kv_stage_bytes<D, kRoleK>(),
@@ -743,7 +744,7 @@ hipError_t launch_bwd_d(const BwdParams &P, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  if (p.nk > 0) {
+  if (p.nk > 0 && (parts & 1)) {
     const int64_t n1 = groups * p.Hkv * ((p.nk + kKW * 32 - 1) / (kKW * 32));
     hipLaunchKernelGGL((bwd_kv_kernel<D, BF16, kRoleV>), dim3((unsigned)n1), dim3(kKW * 64), lv,
                        s, P);
@@ -754,6 +755,7 @@ hipError_t launch_bwd_d(const BwdParams &P, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (!(parts & 2)) return hipSuccess;
   const int64_t n2 = groups * p.Hq * ((p.nq + kQW * 32 - 1) / (kQW * 32));
   hipLaunchKernelGGL((bwd_dq_kernel<D, BF16>), dim3((unsigned)n2), dim3(kQW * 64), l2, s, P);
   return hipGetLastError();
@@ -794,11 +796,11 @@ hipError_t launch_cast(const float *x, void *y, int dtype, int64_t n, hipStream_
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdParams &p, int dtype, hipStream_t s) {
+hipError_t launch_bwd(const BwdParams &p, int dtype, hipStream_t s, int parts) {
   if (p.a.nq == 0) return hipSuccess;
   if (dtype == RA_DT_BF16)
-    return p.a.d == 64 ? launch_bwd_d<64, true>(p, s) : launch_bwd_d<128, true>(p, s);
-  return p.a.d == 64 ? launch_bwd_d<64, false>(p, s) : launch_bwd_d<128, false>(p, s);
+    return p.a.d == 64 ? launch_bwd_d<64, true>(p, s, parts) : launch_bwd_d<128, true>(p, s, parts);
+  return p.a.d == 64 ? launch_bwd_d<64, false>(p, s, parts) : launch_bwd_d<128, false>(p, s, parts);
 }
 
 }  // namespace ra

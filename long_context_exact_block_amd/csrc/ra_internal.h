@@ -132,7 +132,9 @@ struct BwdParams {
 };
 hipError_t launch_bwd_prep(const void *o, const void *dout, const float *lse, float *nD,
                            float *nl, int dtype, int64_t rows, int32_t d, hipStream_t s);
-hipError_t launch_bwd(const BwdParams &p, int dtype, hipStream_t s);
+// parts: kBwdKV (the dK and dV kernels), kBwdQ (the dQ kernel) or both
+constexpr int kBwdKV = 1, kBwdQ = 2, kBwdAll = 3;
+hipError_t launch_bwd(const BwdParams &p, int dtype, hipStream_t s, int parts = kBwdAll);
 hipError_t launch_zero(float *x, int64_t n, hipStream_t s);  // n % 4 == 0
 hipError_t launch_cast(const float *x, void *y, int dtype, int64_t n, hipStream_t s);
 

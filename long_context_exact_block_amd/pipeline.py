@@ -92,11 +92,12 @@ class RingAttention:
             self.dv_sh = torch.empty_like(self.v_sh)
             self.bargs = rb.ring_bwd_args(self.q_sh, self.k_sh, self.v_sh, self.o_sh, self.do_sh,
                                           self.lse_sh, self.dq_sh, self.dk_sh, self.dv_sh, R,
-                                          self.rank0, nr, self.scale, self.causal, self.layout)
+                                          self.rank0, nr, self.scale, self.causal, self.layout,
+                                          self.handoff)
             nb = rb.ra_ring_bwd_workspace_size(self.bargs)
             self.bworkspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
         rb.ra_layout_gather(dout, self.do_sh, self.fwd, R, self.rank0, nr, stream)
-        rb.ra_ring_bwd(self.bargs, self.bworkspace, stream)
+        rb.ra_ring_bwd(self.bargs, self.bworkspace, stream, self.copy_stream)
         rb.ra_layout_scatter(self.dq_sh, dq, self.fwd, R, self.rank0, nr, stream)
         rb.ra_layout_scatter(self.dk_sh, dk, self.fwd, R, 0, R, stream)
         rb.ra_layout_scatter(self.dv_sh, dv, self.fwd, R, 0, R, stream)

@@ -274,31 +274,42 @@ def _ring_bwd(**kw):
     a.dtype, a.R, a.rank0, a.n_ranks = rb.DT_BF16, 8, 0, 8
     a.B, a.Hq, a.Hkv, a.n, a.d = 1, 4, 2, 256, 128
     a.scale, a.causal, a.layout = 0.088, 1, rb.LAYOUT_STRIPED
+    a.handoff = rb.HANDOFF_COPY
     for k, v in kw.items():
         setattr(a, k, v)
     return a
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("dtype", rb.DT_FP32, 6), ("dtype", 9, 3), ("layout", 5, 1), ("R", 0, 2), ("n_ranks", 9, 2),
+    ("dtype", rb.DT_FP32, 6), ("dtype", 9, 3), ("layout", 5, 1), ("handoff", 2, 1),
+    ("R", 0, 2), ("n_ranks", 9, 2),
     ("rank0", 1, 2), ("d", 32, 2), ("Hkv", 3, 2), ("n", (1 << 23) + 2, 6),
     ("scale", float("inf"), 1), ("dout_sh", 0, 1), ("lse", 0, 1), ("dv_sh", 4104, 4),
 ])
 def test_ring_bwd_rejects(lib, field, value, status):
     a = _ring_bwd(**{field: value})
-    st = lib.ra_ring_bwd(ctypes.byref(a), ctypes.c_void_p(4096), 1 << 40, None)
+    st = lib.ra_ring_bwd(ctypes.byref(a), ctypes.c_void_p(4096), 1 << 40, None, None)
     assert st == status, (st, rb.last_error())
     assert lib.ra_ring_bwd_workspace_size(ctypes.byref(a)) == 0
 
 
 def test_ring_bwd_zigzag_needs_even_blocks_and_workspace(lib):
     odd = _ring_bwd(layout=rb.LAYOUT_ZIGZAG, n=255)
-    assert lib.ra_ring_bwd(ctypes.byref(odd), ctypes.c_void_p(4096), 1 << 40, None) == 2
+    assert lib.ra_ring_bwd(ctypes.byref(odd), ctypes.c_void_p(4096), 1 << 40, None, None) == 2
     a = _ring_bwd()
     need = lib.ra_ring_bwd_workspace_size(ctypes.byref(a))
     rows = 8 * 1 * 4 * 256
     # fp32 dq of the computed rows and dk, dv of every block, plus the per-row -D and nl
     assert need >= rows * 128 * 4 + 2 * 8 * 1 * 2 * 256 * 128 * 4 + 2 * rows * 4
-    assert lib.ra_ring_bwd(ctypes.byref(a), None, need, None) == 5
-    assert lib.ra_ring_bwd(ctypes.byref(a), ctypes.c_void_p(4096), need - 1, None) == 5
-    assert lib.ra_ring_bwd(ctypes.byref(a), ctypes.c_void_p(4096 + 16), need, None) == 5
+    assert lib.ra_ring_bwd(ctypes.byref(a), None, need, None, None) == 5
+    assert lib.ra_ring_bwd(ctypes.byref(a), ctypes.c_void_p(4096), need - 1, None, None) == 5
+    assert lib.ra_ring_bwd(ctypes.byref(a), ctypes.c_void_p(4096 + 16), need, None, None) == 5
+    # COPY adds two receive buffers per computed rank: K, V, transposed K (16-bit) and the
+    # fp32 dK, dV accumulators that travel with the block
+    swap = _ring_bwd(handoff=rb.HANDOFF_SWAP)
+    blk = 1 * 2 * 256 * 128
+    assert need - lib.ra_ring_bwd_workspace_size(ctypes.byref(swap)) >= 2 * 8 * blk * (3 * 2 + 2 * 4)
+    one = _ring_bwd(R=1, n_ranks=1)
+    one_swap = _ring_bwd(R=1, n_ranks=1, handoff=rb.HANDOFF_SWAP)
+    assert lib.ra_ring_bwd_workspace_size(ctypes.byref(one)) == \
+        lib.ra_ring_bwd_workspace_size(ctypes.byref(one_swap))  # nothing travels on one rank

@@ -27,7 +27,7 @@ CASES = [
 ]
 
 
-def run(case, seed=0):
+def run(case, seed=0, handoff=rb.HANDOFF_COPY, raw=False):
     import torch
     name, B, Hq, Hkv, S, d, R, layout, dtype, causal, rank0, nr = case
     xs = {}
@@ -36,7 +36,8 @@ def run(case, seed=0):
         xs[nm] = inputs.to_dtype(inputs.normal(shape, 4000 + 10 * seed + sd), dtype)
     td = parity.torch_dtype(dtype)
     q, k, v, g = (parity.to_device(xs[nm][0], dtype) for nm in ("q", "k", "v", "g"))
-    ra = RingAttention(B, Hq, Hkv, S, d, R, layout, td, causal, rank0=rank0, n_ranks=nr)
+    ra = RingAttention(B, Hq, Hkv, S, d, R, layout, td, causal, rank0=rank0, n_ranks=nr,
+                       handoff=handoff)
     o = torch.zeros((B, Hq, S, d), dtype=td, device="cuda")
     lse = torch.zeros((B, Hq, S), dtype=torch.float32, device="cuda")
     ra.run(q, k, v, o, lse)
@@ -45,6 +46,8 @@ def run(case, seed=0):
     dv = torch.zeros((B, Hkv, S, d), dtype=td, device="cuda")
     ra.backward(g, dq, dk, dv)
     torch.cuda.synchronize()
+    if raw:
+        return dq.cpu(), dk.cpu(), dv.cpu()
     fwd, _ = oracle.layout_maps(rb.LAYOUTS[layout], S, R)
     n = S // R
     owned = np.sort(fwd[rank0 * n:(rank0 + nr) * n])
@@ -77,3 +80,33 @@ def test_ring_bwd_deterministic():
     b = run(CASES[0])
     for x, y in zip(a[0::2], b[0::2]):
         assert np.array_equal(x, y)
+
+
+# COPY moves K, V, the transposed K and the fp32 dK/dV accumulators with each
+# block; SWAP reads and accumulates in place.  Every accumulator receives the
+# same contributions in the same hop order either way, so the results must be
+# bitwise equal.  The extra cases have blocks that leave the computed ranks
+# and come back (ranks 1-2 of 4) or enter from ranks outside them.
+SUBSET_CASES = [
+    ("bf16_striped_ranks1-2_of_4", 1, 2, 2, 2048, 128, 4, "striped", "bf16", True, 1, 2),
+    ("fp16_contig_ranks0-1_of_3_d64", 1, 2, 1, 1536, 64, 3, "contiguous", "fp16", True, 0, 2),
+    ("bf16_zigzag_ranks2-4_of_5", 1, 2, 2, 2560, 128, 5, "zigzag", "bf16", True, 2, 3),
+]
+
+
+@pytest.mark.parametrize("case", CASES + SUBSET_CASES, ids=lambda c: c[0])
+def test_ring_bwd_copy_equals_swap(case):
+    import torch
+    a = run(case, handoff=rb.HANDOFF_COPY, raw=True)
+    b = run(case, handoff=rb.HANDOFF_SWAP, raw=True)
+    for name, x, y in zip(("dq", "dk", "dv"), a, b):
+        assert torch.equal(x, y), (case[0], name)
+
+
+@pytest.mark.parametrize("case", SUBSET_CASES, ids=lambda c: c[0])
+def test_ring_bwd_rank_subsets_match_oracle(case):
+    gq, rq, gk, rk, gv, rv = run(case)
+    rm = REL_MEAN[case[8]]
+    check_grad(gq, rq, case[0] + " dq", rel_mean=rm)
+    check_grad(gk, rk, case[0] + " dk", rel_mean=rm)
+    check_grad(gv, rv, case[0] + " dv", rel_mean=rm)
