@@ -399,6 +399,23 @@ ra_status ra_decode_fwd(const ra_decode_args *a, void *workspace, size_t workspa
                         ra_stream stream);
 
 /*
+ * ra_decode_fwd_noalloc -- ra_decode_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, kernels and results (bitwise) as
+ * ra_decode_fwd, but the fp32 partials live in a device array the library
+ * holds per GPU (32 MiB each, kept until the process ends; the address is
+ * looked up on a device's first call).  The call allocates nothing.
+ * Arguments whose partials (ra_decode_fwd_workspace_size) exceed 32 MiB are
+ * rejected with RA_ERR_UNSUPPORTED; the 1M-token cache with 32 query heads
+ * over 8 K/V heads and 4 new tokens needs about 2 MiB.  Every call on a GPU
+ * uses that GPU's one array, so calls that overlap on one GPU (different
+ * streams, or host threads) race and must be serialised by the caller;
+ * nothing in the array needs to start at zero.
+ * Errors: as ra_decode_fwd, except RA_ERR_WORKSPACE.
+ */
+ra_status ra_decode_fwd_noalloc(const ra_decode_args *a, ra_stream stream);
+
+/*
  * ra_causal_work -- per-rank count of allowed causal (query, key) pairs over
  * the whole ring, W[r] for r < R (host int64 array of R entries), from the
  * same block classification the kernels use ([ZZ]: the interleaved layout

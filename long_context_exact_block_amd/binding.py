@@ -28,7 +28,7 @@ EXPORTED = ("ra_version", "ra_status_string", "ra_last_error", "ra_layout_permut
             "ra_pack_v", "ra_merge", "ra_finalize", "ra_ring_fwd_workspace_size", "ra_ring_fwd",
             "ra_causal_work", "ra_decode_fwd_workspace_size", "ra_decode_fwd",
             "ra_block_bwd_workspace_size", "ra_block_bwd", "ra_ring_bwd_workspace_size",
-            "ra_ring_bwd", "ra_handoff_copy")
+            "ra_ring_bwd", "ra_handoff_copy", "ra_decode_fwd_noalloc")
 
 
 class RAError(RuntimeError):
@@ -110,6 +110,7 @@ def lib():
     L.ra_decode_fwd_workspace_size.argtypes = [ctypes.POINTER(DecodeArgs)]
     L.ra_decode_fwd_workspace_size.restype = ctypes.c_size_t
     L.ra_decode_fwd.argtypes = [ctypes.POINTER(DecodeArgs), P, ctypes.c_size_t, P]
+    L.ra_decode_fwd_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), P]
     L.ra_packed_v_bytes.argtypes = [I32, I32, I32, I32, I32]
     L.ra_packed_v_bytes.restype = ctypes.c_size_t
     L.ra_pack_v.argtypes = [P, P, I32, I32, I32, I32, I32, ctypes.POINTER(I64), P]
@@ -370,6 +371,11 @@ def ra_decode_fwd(args: DecodeArgs, workspace, stream=None):
     ws_ptr = _ptr(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().ra_decode_fwd(ctypes.byref(args), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def ra_decode_fwd_noalloc(args: DecodeArgs, stream=None):
+    """ra_decode_fwd with the partials in the library's per-GPU device array (no workspace)."""
+    _check(lib().ra_decode_fwd_noalloc(ctypes.byref(args), _stream(stream)))
 
 
 def ra_causal_work(layout: int, S: int, R: int):

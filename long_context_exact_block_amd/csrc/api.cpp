@@ -383,6 +383,21 @@ size_t decode_ws_bytes(const DecodeParams &p) {
   return align256((size_t)p.P * rows * p.d * 4) + 2 * align256((size_t)p.P * rows * 4);
 }
 
+// Decode with its partials at ws (decode_ws_bytes(p) bytes, 256-byte
+// aligned).  Every partial is written before it is read, so ws needs no
+// clearing.
+ra_status run_decode(const ra_decode_args *a, DecodeParams p, char *ws, hipStream_t s) {
+  const size_t rows = (size_t)p.B * p.Hq * p.nq;
+  p.po = (float *)ws;
+  p.pm = (float *)(ws + align256((size_t)p.P * rows * p.d * 4));
+  p.pl = (float *)((char *)p.pm + align256((size_t)p.P * rows * 4));
+  p.q = a->q;
+  p.k = a->n > 0 ? a->k : a->q;  // never read when n == 0
+  p.v = a->n > 0 ? a->v : a->q;
+  RA_HIP(launch_decode(p, a->dtype, a->o, a->lse, s), "decode kernels");
+  return RA_OK;
+}
+
 ra_status check_ring(const ra_ring_args *a) {
   if (!a) return fail(RA_ERR_INVALID_ARG, "args is NULL");
   if (!elt_bytes(a->dtype)) return fail(RA_ERR_DTYPE, "unknown dtype %d", a->dtype);
@@ -1172,16 +1187,23 @@ ra_status ra_decode_fwd(const ra_decode_args *a, void *workspace, size_t workspa
   const size_t need = decode_ws_bytes(p);
   if (!workspace || workspace_bytes < need || (uintptr_t)workspace % 256)
     return fail(RA_ERR_WORKSPACE, "workspace must be >= %zu bytes, 256-byte aligned", need);
-  const size_t rows = (size_t)p.B * p.Hq * p.nq;
-  char *ws = (char *)workspace;
-  p.po = (float *)ws;
-  p.pm = (float *)(ws + align256((size_t)p.P * rows * p.d * 4));
-  p.pl = (float *)((char *)p.pm + align256((size_t)p.P * rows * 4));
-  p.q = a->q;
-  p.k = a->n > 0 ? a->k : a->q;  // never read when n == 0
-  p.v = a->n > 0 ? a->v : a->q;
-  RA_HIP(launch_decode(p, a->dtype, a->o, a->lse, (hipStream_t)stream), "decode kernels");
-  return RA_OK;
+  return run_decode(a, p, (char *)workspace, (hipStream_t)stream);
+}
+
+ra_status ra_decode_fwd_noalloc(const ra_decode_args *a, ra_stream stream) {
+  clear_error();
+  ra_status st = check_decode(a);
+  if (st != RA_OK) return st;
+  DecodeParams p = decode_plan(a);
+  const size_t need = decode_ws_bytes(p);
+  if (need > kDecodeScratchBytes)
+    return fail(RA_ERR_UNSUPPORTED,
+                "these arguments need %zu bytes of partials; the allocation-free decode holds %zu "
+                "(use ra_decode_fwd with a workspace)",
+                need, kDecodeScratchBytes);
+  void *ws = nullptr;
+  RA_HIP(decode_scratch(&ws), "scratch address");
+  return run_decode(a, p, (char *)ws, (hipStream_t)stream);
 }
 
 ra_status ra_causal_work(int32_t layout, int64_t S, int32_t R, int64_t *W) {

@@ -26,6 +26,8 @@
 #include <cfloat>
 #include <cmath>
 
+#include <mutex>
+
 #include "attn_common.h"
 
 namespace ra {
@@ -401,6 +403,30 @@ hipError_t launch_decode_d(const DecodeParams &p, hipStream_t s) {
 }
 
 }  // namespace
+
+// Partials of the allocation-free decode entry point.  The array's name is a
+// host-side stand-in on the host: kernels get the device address that
+// hipGetSymbolAddress returns, looked up once per device (each device holds
+// its own copy) and kept for the life of the process.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void **ptr) {
+  static std::mutex mu;
+  static void *addr[kMaxScratchDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void *a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeParams &p, int dtype, void *o, float *lse, hipStream_t s) {
   const int rows = p.B * p.Hq * p.nq;

@@ -95,6 +95,12 @@ struct DecodeParams {
 };
 hipError_t launch_decode(const DecodeParams &p, int dtype, void *o, float *lse,
                          hipStream_t s);
+// Device-resident scratch of the allocation-free decode entry point: one
+// array of kDecodeScratchBytes per device (devices 0 .. kMaxScratchDevices-1),
+// its address looked up on the current device's first use.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+constexpr int kMaxScratchDevices = 64;
+hipError_t decode_scratch(void **ptr);
 hipError_t launch_merge(float *o_acc, float *m_acc, float *l_acc, const float *o_blk,
                         const float *m_blk, const float *l_blk, int64_t rows, int32_t d,
                         hipStream_t s);

@@ -313,3 +313,17 @@ def test_ring_bwd_zigzag_needs_even_blocks_and_workspace(lib):
     one_swap = _ring_bwd(R=1, n_ranks=1, handoff=rb.HANDOFF_SWAP)
     assert lib.ra_ring_bwd_workspace_size(ctypes.byref(one)) == \
         lib.ra_ring_bwd_workspace_size(ctypes.byref(one_swap))  # nothing travels on one rank
+
+
+def test_decode_noalloc_rejects_before_any_gpu_call(lib):
+    """Validation of the allocation-free decode runs on the host: bad arguments
+    and partials beyond its 32 MiB device array are refused without a GPU."""
+    a = rb.DecodeArgs()
+    a.q = a.k = a.v = a.o = a.lse = 4096
+    a.dtype, a.R, a.B, a.Hq, a.Hkv, a.nq, a.n, a.d = rb.DT_BF16, 2, 64, 64, 64, 16, 128, 128
+    a.scale, a.causal, a.q_gid0 = 0.088, 1, 0
+    assert lib.ra_decode_fwd_noalloc(None, None) == 1
+    assert lib.ra_decode_fwd_workspace_size(ctypes.byref(a)) > 32 << 20
+    assert lib.ra_decode_fwd_noalloc(ctypes.byref(a), None) == 6
+    a.d = 96
+    assert lib.ra_decode_fwd_noalloc(ctypes.byref(a), None) == 2
