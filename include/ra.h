@@ -267,9 +267,11 @@ typedef struct {
   int32_t merge_mode; /* ra_merge_mode */
   void *o;
   float *lse;
-  /* Optional timing hook (host array of 2*R hipEvent_t created by the caller,
-   * or NULL): event 2h is recorded on `compute` right before hop h's block
-   * kernel and event 2h+1 right after it. */
+  /* Instrumentation, not part of the computation: an optional host array of
+   * 2*R hipEvent_t created by the caller (or NULL).  Event 2h is recorded on
+   * `compute` right before hop h's block kernel and event 2h+1 right after
+   * it, so a caller can time the block kernel on the stream it runs on.
+   * Results do not depend on it. */
   void **hop_events;
 } ra_ring_args;
 
