@@ -228,21 +228,24 @@ def overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse, t_c
     v_bytes = (w.ranks * w.B * w.Hkv * w.d * ((w.n + 63) // 64 * 64) * elt
                if w.dtype != "fp32" else k_bytes)
     per_hop = k_bytes + v_bytes
+    # the form of the copy the ring picks for this workload (same rule as the library)
+    pairs = w.ranks * w.B * w.Hq * float(w.n) * w.n * (0.5 if w.causal else 1.0)
+    thin = rb.thin_handoff(2.0 * per_hop, pairs, w.d)
     src = torch.empty(per_hop, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
-    rb.ra_handoff_copy(dst, src)
+    rb.ra_handoff_copy(dst, src, thin=thin)
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     c0.record()
     for _ in range(w.R - 1):
-        rb.ra_handoff_copy(dst, src)
+        rb.ra_handoff_copy(dst, src, thin=thin)
     c1.record()
     torch.cuda.synchronize()
     t_copies = c0.elapsed_time(c1)
     del src, dst
     moved = 2.0 * per_hop * (w.R - 1)  # read + write
     return {"step_ms_copy": round(t_copy_ms, 3), "step_ms_swap": round(t_swap, 3),
-            "copies_alone_ms": round(t_copies, 3),
+            "copies_alone_ms": round(t_copies, 3), "copy_form": "thin" if thin else "wide",
             "bytes_per_hop": per_hop, "copy_GB/s": round(moved / (t_copies * 1e-3) / 1e9, 1),
             "overlap": round(1.0 - (t_copy_ms - t_swap) / t_copies, 3) if t_copies > 0 else None}
 
@@ -286,15 +289,17 @@ def backward_bench(torch, ra, w, layout_code, q, k, v, iters=2):
         n_pad = (w.n + 63) // 64 * 64
         per_hop = w.ranks * (2 * kz * 2 + 2 * w.B * w.Hkv * w.d * n_pad + 2 * kz * 4)
         home = w.ranks * 2 * kz * 4
+        pairs = w.ranks * w.B * w.Hq * float(w.n) * w.n * (0.5 if w.causal else 1.0)
+        thin = rb.thin_handoff(2.0 * per_hop, pairs, w.d, 3.2)
         src = torch.empty(per_hop, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
-        rb.ra_handoff_copy(dst, src)
+        rb.ra_handoff_copy(dst, src, thin=thin)
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         c0.record()
         for _ in range(w.R - 1):
-            rb.ra_handoff_copy(dst, src)
-        rb.ra_handoff_copy(dst, src, home)
+            rb.ra_handoff_copy(dst, src, thin=thin)
+        rb.ra_handoff_copy(dst, src, home, thin=thin)
         c1.record()
         torch.cuda.synchronize()
         t_copies = c0.elapsed_time(c1)
@@ -302,7 +307,8 @@ def backward_bench(torch, ra, w, layout_code, q, k, v, iters=2):
         t_copy, t_swap = float(np.median(ms)), float(np.median(ms_swap))
         moved = 2.0 * (per_hop * (w.R - 1) + home)
         handoff = {"ms_copy": round(t_copy, 3), "ms_swap": round(t_swap, 3),
-                   "copies_alone_ms": round(t_copies, 3), "bytes_per_hop": per_hop,
+                   "copies_alone_ms": round(t_copies, 3), "copy_form": "thin" if thin else "wide",
+                   "bytes_per_hop": per_hop,
                    "copy_GB/s": round(moved / (t_copies * 1e-3) / 1e9, 1),
                    "overlap": round(1.0 - (t_copy - t_swap) / t_copies, 3) if t_copies > 0 else None}
     pairs = sum(hop_pairs(w, layout_code))
@@ -359,6 +365,40 @@ def rank_share_bench(torch, rb, RingAttention, w, iters=3):
         out[layout] = {"rank_ms": [round(x, 3) for x in ms],
                        "max_over_mean": round(float(a.max() / a.mean()), 4)}
     del q, k, v, o, lse
+    return out
+
+
+def length_sweep_bench(torch, rb, RingAttention, w, lengths, iters=3):
+    """The headline shape (w: one rank's share, striped, causal) at shorter total
+    lengths S, to expose cliffs as the sequence grows (the stress tier of the
+    ruibaoantu accelerator-adaptation article, section 4.3).  Per S: the ring call
+    (R hops, COPY hand-off, fused fold) on device-side random shards, TFLOP/s with
+    the metric's FLOP count for one rank's share (4 B Hq (S/R) S d, halved causal)."""
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
+    out = []
+    for S in lengths:
+        if S % w.R or (w.layouts[0] == "zigzag" and S % (2 * w.R)):
+            continue
+        ra = RingAttention(w.B, w.Hq, w.Hkv, S, w.d, w.R, w.layouts[0], tdt, w.causal, w.scale,
+                           rank0=w.rank0, n_ranks=w.ranks)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(w.seed + S)
+        for t in (ra.q_sh, ra.k_sh, ra.v_sh):
+            t.copy_(torch.randn(t.shape, device="cuda", generator=g).to(tdt))
+        ra.ring()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        torch.cuda.synchronize()
+        e[0].record()
+        for i in range(iters):
+            ra.ring()
+            e[i + 1].record()
+        torch.cuda.synchronize()
+        ms = float(np.median([e[i].elapsed_time(e[i + 1]) for i in range(iters)]))
+        flops = 4.0 * w.B * w.Hq * (S // w.R) * w.ranks * S * w.d / (2 if w.causal else 1)
+        tf = flops / (ms * 1e-3) / 1e12
+        out.append({"S": S, "ms": round(ms, 3), "TFLOP/s": round(tf, 1),
+                    "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+        del ra
     return out
 
 
@@ -467,6 +507,8 @@ def main():
                     help="skip the hand-off overlap measurement (SWAP steps + copies alone)")
     ap.add_argument("--no-parts-bench", action="store_true",
                     help="skip timing the maps, gather, scatter and finalize alone")
+    ap.add_argument("--no-length-sweep", action="store_true",
+                    help="skip the headline shape at S = 8k .. 1M")
     ap.add_argument("--no-rank-bench", action="store_true",
                     help="skip timing each rank's share of the causal 32k MHA ring alone")
     ap.add_argument("--block-only", action="store_true",
@@ -567,6 +609,11 @@ def main():
         log("backward")
         backward = backward_bench(torch, ra, w, lcode, q, k, v)
     decode = None if args.no_decode_bench else decode_bench(torch, rb, configs.DECODE_1M)
+    sweep = None
+    if not args.no_length_sweep and w.name == configs.SHARE_1M.name:
+        log("length sweep")
+        sweep = length_sweep_bench(torch, rb, RingAttention, w,
+                                   [1 << e for e in range(13, 21)])
     rank_share = None
     if not args.no_rank_bench:
         log("rank shares of %s alone" % configs.MHA_32K.name)
@@ -632,6 +679,7 @@ def main():
         "step_parts": parts,
         "backward": backward,
         "decode": decode,
+        "length_sweep": sweep,
         "causal_imbalance_max_over_mean": imbalance,
         "rank_share_alone": (None if rank_share is None else
                              {"workload": configs.MHA_32K.name, **rank_share}),

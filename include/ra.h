@@ -204,15 +204,23 @@ ra_status ra_merge(float *o_acc, float *m_acc, float *l_acc, const float *o_blk,
  * ra_handoff_copy -- the K/V hand-off between hops (highthink.cn article,
  * section on Zig Zag Ring Attention: each rank passes the K/V it holds to its
  * ring successor while attending to the current block): a device-to-device
- * copy of `bytes` bytes on `stream`, as ra_ring_fwd issues it on its copy
- * stream.  It runs on a small grid with non-temporal loads and stores, so next
- * to a block kernel it takes few compute units and does not evict the K/V
- * tiles that kernel reuses from L2.  dst, src: device pointers, not
- * overlapping; 16-byte aligned pointers and a multiple of 16 bytes take the
- * kernel, anything else falls back to hipMemcpyAsync.  Asynchronous.
- * Errors: RA_ERR_INVALID_ARG (null pointer with bytes > 0), RA_ERR_HIP.
+ * copy of `bytes` bytes on `stream`, in either of the two forms the rings
+ * issue on their copy stream, with non-temporal loads and stores:
+ *   thin = 1: one-wave workgroups of 16 VGPRs that fit in the registers the
+ *     attention kernels leave free, so they run beside them without
+ *     displacing their workgroups.  The rings use it when a hop's estimated
+ *     MFMA time (4 d flop per allowed pair and query head at 1.3 PFLOP/s;
+ *     3.2 times that for the backward) is at least four times the time the
+ *     hop's bytes take at 1 TB/s.
+ *   thin = 0: 64 workgroups of 256 threads, for short hops.
+ * dst, src: device pointers, not overlapping; 16-byte aligned pointers and a
+ * multiple of 16 bytes take the kernels, anything else falls back to
+ * hipMemcpyAsync.  Asynchronous.
+ * Errors: RA_ERR_INVALID_ARG (thin not 0 or 1; null pointer with bytes > 0),
+ * RA_ERR_HIP.
  */
-ra_status ra_handoff_copy(void *dst, const void *src, size_t bytes, ra_stream stream);
+ra_status ra_handoff_copy(void *dst, const void *src, size_t bytes, int32_t thin,
+                          ra_stream stream);
 
 /*
  * ra_finalize -- running state to outputs: out = O rounded to nearest even
@@ -425,6 +433,15 @@ ra_status ra_decode_fwd_noalloc(const ra_decode_args *a, ra_stream stream);
  * Errors: RA_ERR_INVALID_ARG, RA_ERR_SHAPE.
  */
 ra_status ra_causal_work(int32_t layout, int64_t S, int32_t R, int64_t *W);
+
+/*
+ * ra_cached_events -- diagnostic: how many HIP events the library holds.  The
+ * ring drivers lease their events from a per-device cache behind a mutex and
+ * hand them back when the call returns, so the count grows only with the
+ * number of ring calls that ever ran at the same time, never per call or per
+ * host thread.  Host-only.
+ */
+size_t ra_cached_events(void);
 
 #ifdef __cplusplus
 }

@@ -10,7 +10,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libra.so")
+# RA_LIBRARY names another build of the same library (the tests' host-only
+# sanitizer build); by default the in-tree libra.so
+LIB_PATH = os.environ.get("RA_LIBRARY") or os.path.join(PKG, "libra.so")
 
 RA_OK = 0
 STATUS_NAMES = {0: "RA_OK", 1: "RA_ERR_INVALID_ARG", 2: "RA_ERR_SHAPE", 3: "RA_ERR_DTYPE",
@@ -28,7 +30,7 @@ EXPORTED = ("ra_version", "ra_status_string", "ra_last_error", "ra_layout_permut
             "ra_pack_v", "ra_merge", "ra_finalize", "ra_ring_fwd_workspace_size", "ra_ring_fwd",
             "ra_causal_work", "ra_decode_fwd_workspace_size", "ra_decode_fwd",
             "ra_block_bwd_workspace_size", "ra_block_bwd", "ra_ring_bwd_workspace_size",
-            "ra_ring_bwd", "ra_handoff_copy", "ra_decode_fwd_noalloc")
+            "ra_ring_bwd", "ra_handoff_copy", "ra_decode_fwd_noalloc", "ra_cached_events")
 
 
 class RAError(RuntimeError):
@@ -111,10 +113,11 @@ def lib():
     L.ra_decode_fwd_workspace_size.restype = ctypes.c_size_t
     L.ra_decode_fwd.argtypes = [ctypes.POINTER(DecodeArgs), P, ctypes.c_size_t, P]
     L.ra_decode_fwd_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), P]
+    L.ra_cached_events.restype = ctypes.c_size_t
     L.ra_packed_v_bytes.argtypes = [I32, I32, I32, I32, I32]
     L.ra_packed_v_bytes.restype = ctypes.c_size_t
     L.ra_pack_v.argtypes = [P, P, I32, I32, I32, I32, I32, ctypes.POINTER(I64), P]
-    L.ra_handoff_copy.argtypes = [P, P, ctypes.c_size_t, P]
+    L.ra_handoff_copy.argtypes = [P, P, ctypes.c_size_t, I32, P]
     L.ra_merge.argtypes = [P, P, P, P, P, P, I64, I32, P]
     L.ra_finalize.argtypes = [P, P, P, P, P, I32, I64, I32, P]
     L.ra_ring_fwd_workspace_size.argtypes = [ctypes.POINTER(RingArgs)]
@@ -227,10 +230,17 @@ def ra_pack_v(v, vp, stream=None):
     _check(lib().ra_pack_v(_ptr(v), _ptr(vp), dtype_code(v), B, H, n, d, st, _stream(stream)))
 
 
-def ra_handoff_copy(dst, src, nbytes=None, stream=None):
-    """Device copy of nbytes (default: all of src) from src to dst, as the ring's hand-off."""
+def ra_handoff_copy(dst, src, nbytes=None, stream=None, thin=False):
+    """Device copy of nbytes (default: all of src) from src to dst, as the ring's hand-off
+    (thin: the one-wave form the rings use for long hops)."""
     nb = src.numel() * src.element_size() if nbytes is None else int(nbytes)
-    _check(lib().ra_handoff_copy(_ptr(dst), _ptr(src), nb, _stream(stream)))
+    _check(lib().ra_handoff_copy(_ptr(dst), _ptr(src), nb, int(bool(thin)), _stream(stream)))
+
+
+def thin_handoff(moved_bytes, pairs_heads, d, work=1.0):
+    """Whether a ring uses the thin hand-off copy: the same rule as the library
+    (hop MFMA time at 1.3 PFLOP/s at least four times the thin copy's at 1 TB/s)."""
+    return work * 4.0 * d * pairs_heads / 1.3e15 > 4.0 * moved_bytes / 1.0e12
 
 
 def ra_merge(o_acc, m_acc, l_acc, o_blk, m_blk, l_blk, stream=None):
@@ -384,3 +394,8 @@ def ra_causal_work(layout: int, S: int, R: int):
     _check(lib().ra_causal_work(int(layout), int(S), int(R),
                                 W.ctypes.data_as(ctypes.c_void_p)))
     return W
+
+
+def ra_cached_events() -> int:
+    """Number of HIP events the library caches for its ring drivers (diagnostic)."""
+    return int(lib().ra_cached_events())

@@ -50,5 +50,24 @@ def build(force: bool = True, verbose: bool = False) -> str:
     return LIB
 
 
+MICROBENCH = os.path.join(PKG, "microbench")
+
+
+def build_microbench(verbose: bool = False) -> str:
+    """Build the issue-mix microbenchmark (a standalone gfx950 executable)."""
+    src = os.path.join(MICROBENCH, "issue_mix.hip")
+    out = os.path.join(MICROBENCH, "issue_mix")
+    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=" + ARCH, "-Xclang", "-target-feature",
+           "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form",
+           "-Wno-unused-command-line-argument", src, "-o", out]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+    return out
+
+
 if __name__ == "__main__":
     print(build(force=True, verbose=True))
+    print(build_microbench(verbose=True))

@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -131,6 +132,41 @@ struct EventLease {
     return event_sets().acquire(dev, n, &ev);
   }
 };
+
+// Debug aid for the stream ordering of the ring drivers: the environment
+// variables RA_DEBUG_DELAY_COPY and RA_DEBUG_DELAY_COMPUTE (a step count, at
+// most 100000, of about 4 us each) put a bounded sleeping kernel on the copy
+// stream before each hand-off, or on the compute stream before each hop's
+// kernels.  Results must not change: only the timing of the two streams
+// relative to each other does.  Read at every call; unset means no delay.
+struct DebugDelay {
+  int copy = 0, compute = 0;
+};
+DebugDelay debug_delay() {
+  auto get = [](const char *name) {
+    const char *v = std::getenv(name);
+    if (!v || !*v) return 0;
+    const long x = std::strtol(v, nullptr, 10);
+    return (int)std::min<long>(std::max<long>(x, 0), 100000);
+  };
+  DebugDelay d;
+  d.copy = get("RA_DEBUG_DELAY_COPY");
+  d.compute = get("RA_DEBUG_DELAY_COMPUTE");
+  return d;
+}
+
+// Which hand-off copy a ring uses: the thin one, which runs beside the hop's
+// kernels without taking their compute units, when the hop's MFMA work (4 d
+// flop per allowed (query, key) pair and query head at 1.3 PFLOP/s; a causal
+// block has about half its pairs; `work` scales for the backward's kernels)
+// lasts at least four times as long as moving the hop's bytes at a
+// deliberately low 1 TB/s -- the 1M-token share's hops, not the short hops
+// of 4096- or 512-token blocks, where the copy competes with the hop for
+// memory and the 64-workgroup copy costs less (measured side by side).
+bool thin_handoff(double moved_bytes, double pairs_heads, int d, double work) {
+  const double t_hop = work * 4.0 * d * pairs_heads / 1.3e15;
+  return t_hop > 4.0 * moved_bytes / 1.0e12;
+}
 
 struct WsLayout {
   size_t vpack, kbuf[2], vbuf[2], o_acc, m_acc, l_acc, o_blk, m_blk, l_blk, total;
@@ -483,6 +519,8 @@ extern "C" {
 
 int ra_version(void) { return 100; }
 
+size_t ra_cached_events(void) { return event_sets().created(); }
+
 const char *ra_status_string(ra_status s) {
   switch (s) {
     case RA_OK:
@@ -647,11 +685,13 @@ ra_status ra_pack_v(const void *v, void *vp, int32_t dtype, int32_t B, int32_t H
   return RA_OK;
 }
 
-ra_status ra_handoff_copy(void *dst, const void *src, size_t bytes, ra_stream stream) {
+ra_status ra_handoff_copy(void *dst, const void *src, size_t bytes, int32_t thin,
+                          ra_stream stream) {
   clear_error();
+  if (thin != 0 && thin != 1) return fail(RA_ERR_INVALID_ARG, "thin must be 0 or 1");
   if (bytes == 0) return RA_OK;
   if (!dst || !src) return fail(RA_ERR_INVALID_ARG, "null pointer");
-  RA_HIP(launch_copy(dst, src, bytes, (hipStream_t)stream), "hand-off copy");
+  RA_HIP(launch_handoff_copy(dst, src, bytes, (hipStream_t)stream, thin != 0), "hand-off copy");
   return RA_OK;
 }
 
@@ -794,9 +834,15 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
   p.os_t = a->d;
   p.ml_zstride = (int64_t)a->B * a->Hq * n;
 
+  const DebugDelay dbg = debug_delay();
+  const bool thin = thin_handoff(2.0 * (double)nr * (blk_bytes + blkv_bytes),
+                                 (double)nr * a->B * a->Hq * (double)n * n *
+                                     (a->causal ? 0.5 : 1.0),
+                                 a->d, 1.0);
   for (int h = 0; h < R; ++h) {
     // ---- compute hop h: every computed rank r attends to the block of source (r - h) mod R
     if (copy && h > 0) RA_HIP(hipStreamWaitEvent(cs, ev_copy(h - 1), 0), "hipStreamWaitEvent");
+    RA_HIP(launch_delay(dbg.compute, cs), "delay kernel");
     p.kg_s0 = ((r0 - h) % R + R) % R;
     if (copy && h > 0) {
       p.k = kb[(h - 1) & 1];
@@ -835,6 +881,7 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
     // ring predecessor r-1 holds now.  The destination buffer was last read by
     // hop h-1's compute.
     if (h >= 1) RA_HIP(hipStreamWaitEvent(xs, ev_comp(h - 1), 0), "hipStreamWaitEvent");
+    RA_HIP(launch_delay(dbg.copy, xs), "delay kernel");
     for (int t = 0; t < 2; ++t) {
       const char *sh = t ? vsh : ksh;
       char *const *buf = t ? vb : kb;
@@ -854,12 +901,12 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
           run_len += bb;
           continue;
         }
-        if (run_len) RA_HIP(launch_copy(run_dst, run_src, run_len, xs), "hand-off copy");
+        if (run_len) RA_HIP(launch_handoff_copy(run_dst, run_src, run_len, xs, thin), "hand-off copy");
         run_src = src;
         run_dst = dst;
         run_len = bb;
       }
-      if (run_len) RA_HIP(launch_copy(run_dst, run_src, run_len, xs), "hand-off copy");
+      if (run_len) RA_HIP(launch_handoff_copy(run_dst, run_src, run_len, xs, thin), "hand-off copy");
     }
     RA_HIP(hipEventRecord(ev_copy(h), xs), "hipEventRecord");
   }
@@ -1051,19 +1098,24 @@ ra_status ra_ring_bwd(const ra_ring_bwd_args *a, void *workspace, size_t workspa
     const char *src = nullptr;
     size_t len = 0;
   };
+  // the backward hop's kernels do about 3.2 times the forward's MFMA work
+  const bool thin = thin_handoff(
+      2.0 * (double)nr * (parts[0].bytes + parts[1].bytes + parts[2].bytes + parts[3].bytes +
+                          parts[4].bytes),
+      (double)nr * a->B * a->Hq * (double)n * n * (a->causal ? 0.5 : 1.0), a->d, 3.2);
   auto add_copy = [&](Runs &r, char *dst, const char *src, size_t bytes) -> ra_status {
     if (r.len && src == r.src + r.len && dst == r.dst + r.len) {
       r.len += bytes;
       return RA_OK;
     }
-    if (r.len) RA_HIP(launch_copy(r.dst, r.src, r.len, xs), "hand-off copy");
+    if (r.len) RA_HIP(launch_handoff_copy(r.dst, r.src, r.len, xs, thin), "hand-off copy");
     r.dst = dst;
     r.src = src;
     r.len = bytes;
     return RA_OK;
   };
   auto flush = [&](Runs &r) -> ra_status {
-    if (r.len) RA_HIP(launch_copy(r.dst, r.src, r.len, xs), "hand-off copy");
+    if (r.len) RA_HIP(launch_handoff_copy(r.dst, r.src, r.len, xs, thin), "hand-off copy");
     r.len = 0;
     return RA_OK;
   };
@@ -1093,8 +1145,8 @@ ra_status ra_ring_bwd(const ra_ring_bwd_args *a, void *workspace, size_t workspa
     if (h == 0) return RA_OK;
     const int src_rank = ((r0 + k - h) % R + R) % R;
     for (int pi = 3; pi <= 4; ++pi)
-      RA_HIP(launch_copy(parts[pi].home + (size_t)src_rank * parts[pi].bytes, front(parts[pi], h, k),
-                         parts[pi].bytes, xs),
+      RA_HIP(launch_handoff_copy(parts[pi].home + (size_t)src_rank * parts[pi].bytes,
+                                 front(parts[pi], h, k), parts[pi].bytes, xs, thin),
              "hand-off copy");
     return RA_OK;
   };
@@ -1107,6 +1159,7 @@ ra_status ra_ring_bwd(const ra_ring_bwd_args *a, void *workspace, size_t workspa
     RA_HIP(hipEventRecord(ev_entry, s), "hipEventRecord");
     RA_HIP(hipStreamWaitEvent(xs, ev_entry, 0), "hipStreamWaitEvent");
   }
+  const DebugDelay dbg = debug_delay();
   for (int h = 0; h < R; ++h) {
     // hop h: computed rank r0 + z meets the block of source (r0 + z - h) mod R
     p.kg_s0 = ((r0 - h) % R + R) % R;
@@ -1137,6 +1190,7 @@ ra_status ra_ring_bwd(const ra_ring_bwd_args *a, void *workspace, size_t workspa
     }
     // dQ needs only the block's K and V; dK/dV also the block's accumulators
     if (copy && h > 0) RA_HIP(hipStreamWaitEvent(s, ev_kv(h - 1), 0), "hipStreamWaitEvent");
+    RA_HIP(launch_delay(dbg.compute, s), "delay kernel");
     RA_HIP(launch_bwd(P, a->dtype, s, kBwdQ), "backward dq kernel");
     if (copy && h > 0) RA_HIP(hipStreamWaitEvent(s, ev_acc(h - 1), 0), "hipStreamWaitEvent");
     RA_HIP(launch_bwd(P, a->dtype, s, kBwdKV), "backward dk/dv kernels");
@@ -1146,11 +1200,13 @@ ra_status ra_ring_bwd(const ra_ring_bwd_args *a, void *workspace, size_t workspa
       // K, V, K^T for hop h+1: read-only this hop, so they move while hop h
       // computes; the receive buffer was last read by hop h-1
       if (h >= 1) RA_HIP(hipStreamWaitEvent(xs, ev_comp(h - 1), 0), "hipStreamWaitEvent");
+      RA_HIP(launch_delay(dbg.copy, xs), "delay kernel");
       if ((st = hand_off(h, 0, 2)) != RA_OK) return st;
       RA_HIP(hipEventRecord(ev_kv(h), xs), "hipEventRecord");
       // the accumulators are final for hop h once its kernels are done; they
       // move during hop h+1's dQ kernel
       RA_HIP(hipStreamWaitEvent(xs, ev_comp(h), 0), "hipStreamWaitEvent");
+      RA_HIP(launch_delay(dbg.copy, xs), "delay kernel");
       if ((st = hand_off(h, 3, 4)) != RA_OK) return st;
       const int next = (r0 + nr) % R;  // the rank after the computed set
       if (nr < R && !(next >= r0 && next < r0 + nr))

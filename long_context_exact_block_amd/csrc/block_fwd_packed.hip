@@ -19,7 +19,8 @@
 //    gfx950's 64 LDS banks so every read pattern is conflict-free.
 //  * 8 waves x 32 queries per workgroup (256 rows), two waves per SIMD; QK of
 //    tile t+1 is interleaved with the exponentials of tile t; K fragments are
-//    read two k-steps ahead and V^T fragments one PV group ahead.  In the
+//    read one k-step ahead (247 VGPRs: two waves leave room on each SIMD for
+//    the one-wave hand-off copy) and V^T fragments one PV group ahead.  In the
 //    fused ring the upper four waves run PV half a tile late (before instead
 //    of after the QK/exponential phase), so the waves sharing a SIMD are in
 //    opposite phases.
@@ -97,7 +98,7 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
   constexpr int VPW = VTILE / 1024 / kLW;
   constexpr int KRPI = 1024 / KROW;      // K rows per wave-load
   constexpr int CPR = D / 8;             // 16-byte chunks per K row
-  constexpr int KA = 2;                  // K fragment read-ahead (k-steps)
+  constexpr int KA = 1;                  // K fragment read-ahead (k-steps)
   static_assert(KPW * kLW * 1024 == KTILE && VPW * kLW * 1024 == VTILE, "tile must split over the waves");
   extern __shared__ __attribute__((aligned(1024))) char lds[];
 

@@ -311,13 +311,67 @@ hipError_t launch_layout_move(bool gather, const void *src, void *dst, const int
   return hipGetLastError();
 }
 
-hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s) {
+// The ring's hand-off copy for long hops, shaped to run beside the hop's kernels
+// instead of taking compute units from them: one-wave workgroups of 16 VGPRs fit
+// in the registers the attention kernels leave free on each SIMD (two of their
+// waves hold 496 of the 512), so a copy wave shares a SIMD's issue slots and
+// the memory system but displaces no attention workgroup.  Each workgroup
+// copies one contiguous run of 1 KB units, two units in flight, with
+// non-temporal loads and stores.  Alone it moves 3.5-4.6 TB/s of reads plus
+// writes; next to a short, memory-heavy hop (512-token blocks) it costs more
+// than the 64-workgroup copy above, which those hops take instead.
+constexpr int kThinGrid = 1024;
+__global__ void __launch_bounds__(64) copy16_thin_kernel(const u32x4 *__restrict__ src,
+                                                         u32x4 *__restrict__ dst, int64_t n16) {
+  const int64_t units = (n16 + 63) >> 6;
+  const int64_t per = (units + gridDim.x - 1) / gridDim.x;
+  const int64_t u0 = (int64_t)blockIdx.x * per;
+  const int64_t u1 = u0 + per < units ? u0 + per : units;
+  int64_t i = (u0 << 6) + threadIdx.x;
+  const int64_t iend = (u1 << 6) < n16 ? (u1 << 6) : n16;
+  for (; i + 64 < iend; i += 128) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = __builtin_nontemporal_load(src + i + 64);
+    __builtin_nontemporal_store(a, dst + i);
+    __builtin_nontemporal_store(b, dst + i + 64);
+  }
+  if (i < iend) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+hipError_t launch_handoff_copy(void *dst, const void *src, size_t bytes, hipStream_t s,
+                               bool thin) {
+  if (!thin) return launch_copy(dst, src, bytes, s);
+  if (bytes == 0) return hipSuccess;
+  if (((uintptr_t)dst | (uintptr_t)src | bytes) & 15)
+    return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+  const int64_t n16 = (int64_t)(bytes / 16);
+  const int64_t units = (n16 + 63) / 64;
+  const unsigned grid = (unsigned)(units < kThinGrid ? units : kThinGrid);
+  hipLaunchKernelGGL(copy16_thin_kernel, dim3(grid), dim3(64), 0, s, (const u32x4 *)src,
+                     (u32x4 *)dst, n16);
+  return hipGetLastError();
+}
+
+// One wave sleeping `n` times for s_sleep's longest step (64 x 127 clocks):
+// a bounded stall that widens the windows between the ring's two streams.
+__global__ void __launch_bounds__(64) delay_kernel(int n) {
+  for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(127);
+}
+
+hipError_t launch_delay(int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(delay_kernel, dim3(1), dim3(64), 0, s, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s, int max_grid) {
   if (bytes == 0) return hipSuccess;
   if (((uintptr_t)dst | (uintptr_t)src | bytes) & 15)
     return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
   const int64_t n16 = (int64_t)(bytes / 16);
   const int64_t need = (n16 + 255) / 256;
-  const unsigned grid = (unsigned)(need < kCopyGrid ? need : kCopyGrid);
+  const int64_t cap = max_grid > 0 ? max_grid : kCopyGrid;
+  const unsigned grid = (unsigned)(need < cap ? need : cap);
   hipLaunchKernelGGL(copy16_kernel, dim3(grid), dim3(256), 0, s, (const u32x4 *)src, (u32x4 *)dst,
                      n16);
   return hipGetLastError();

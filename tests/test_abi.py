@@ -163,9 +163,11 @@ def test_layout_rejects(lib):
 
 
 def test_handoff_copy_rejects(lib):
-    assert lib.ra_handoff_copy(None, 4096, 16, None) == 1
-    assert lib.ra_handoff_copy(4096, None, 16, None) == 1
-    assert lib.ra_handoff_copy(None, None, 0, None) == 0  # nothing to copy: no GPU call
+    for thin in (0, 1):
+        assert lib.ra_handoff_copy(None, 4096, 16, thin, None) == 1
+        assert lib.ra_handoff_copy(4096, None, 16, thin, None) == 1
+        assert lib.ra_handoff_copy(None, None, 0, thin, None) == 0  # nothing to copy: no GPU call
+    assert lib.ra_handoff_copy(4096, 4096, 16, 2, None) == 1
 
 
 def test_merge_finalize_reject(lib):

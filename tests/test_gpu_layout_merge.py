@@ -129,13 +129,17 @@ def test_finalize(dtype, rows, d, off):
     parity.check_lse(lse.cpu().numpy(), expect, "finalize")
 
 
+@pytest.mark.parametrize("thin", [False, True])
 @pytest.mark.parametrize("nbytes,dst_off,src_off", [
     (16, 0, 0), (4096, 0, 0), (256 * 64 * 16 * 4 + 48, 0, 0), (536870912 // 64, 0, 0),
-    (1000, 0, 0), (4096, 2, 0), (4096, 0, 6), (37, 1, 3), (0, 0, 0)])
-def test_handoff_copy_bit_exact(nbytes, dst_off, src_off):
-    """ra_handoff_copy moves exactly `nbytes` bytes: 16-byte aligned copies take
-    the kernel (sizes below, at and past the grid's stride and unroll, and a
-    ragged tail), the rest the runtime copy; bytes around the destination stay."""
+    (1024 * 1024 * 3 + 1024 * 5 + 16 * 7, 0, 0), (1000, 0, 0), (4096, 2, 0), (4096, 0, 6),
+    (37, 1, 3), (0, 0, 0)])
+def test_handoff_copy_bit_exact(nbytes, dst_off, src_off, thin):
+    """ra_handoff_copy moves exactly `nbytes` bytes in both forms: 16-byte aligned
+    copies take the kernels (sizes below, at and past the grids' strides and
+    unrolls, runs of an odd number of 1 KB units per workgroup, workgroups past
+    the data, and ragged tails), the rest the runtime copy; bytes around the
+    destination stay."""
     import torch
     g = torch.Generator(device="cuda")
     g.manual_seed(nbytes + 7 * dst_off + src_off)
@@ -143,7 +147,7 @@ def test_handoff_copy_bit_exact(nbytes, dst_off, src_off):
                         generator=g)
     dst = torch.full((nbytes + dst_off + 32,), 0xA5, dtype=torch.uint8, device="cuda")
     before = dst.clone()
-    rb.ra_handoff_copy(dst[dst_off:], src[src_off:], nbytes)
+    rb.ra_handoff_copy(dst[dst_off:], src[src_off:], nbytes, thin=thin)
     torch.cuda.synchronize()
     got, ref = dst.cpu().numpy(), before.cpu().numpy()
     ref[dst_off:dst_off + nbytes] = src.cpu().numpy()[src_off:src_off + nbytes]

@@ -158,8 +158,74 @@ def test_repeated_calls_do_not_grow_memory():
     v = parity.to_device(x["v"], dtype)
     torch.cuda.synchronize()
     free0, _ = torch.cuda.mem_get_info()
-    for _ in range(50):
+    ev0 = rb.ra_cached_events()
+    for _ in range(100):
         ra.run(q, k, v, o, lse)
     torch.cuda.synchronize()
     free1, _ = torch.cuda.mem_get_info()
     assert free0 - free1 < (64 << 20)
+    assert rb.ra_cached_events() == ev0  # each call hands its events back
+
+
+def test_stream_delays_keep_results():
+    """A bounded sleep on the copy stream before each hand-off, or on the compute
+    stream before each hop, shifts the two streams against each other; with the
+    events ordering them correctly the outputs stay bitwise equal."""
+    import os
+    import torch
+    for case in (CASES[1], CASES[5], CASES[7], CASES[11]):
+        name, B, Hq, Hkv, S, d, R, layout, dtype, causal, rank0, n_ranks = case
+        x = make_inputs(B, Hq, Hkv, S, d, dtype, 81)
+        _, o0, l0 = run_ring(case, x)
+        for var in ("RA_DEBUG_DELAY_COPY", "RA_DEBUG_DELAY_COMPUTE"):
+            os.environ[var] = "40"
+            try:
+                _, o1, l1 = run_ring(case, x)
+            finally:
+                del os.environ[var]
+            # rows of ranks that are not computed stay NaN in every run
+            assert torch.equal(o0, o1), (name, var)
+            assert torch.equal(torch.nan_to_num(l0, nan=7.0), torch.nan_to_num(l1, nan=7.0)), (
+                name, var)
+
+
+def test_rings_on_several_host_threads():
+    """Ring calls from several host threads at once, each with its own streams,
+    give the single-threaded results, and the event cache grows at most by one
+    set per concurrent call."""
+    import threading
+    import torch
+    case = CASES[1]
+    name, B, Hq, Hkv, S, d, R, layout, dtype, causal, rank0, n_ranks = case
+    x = make_inputs(B, Hq, Hkv, S, d, dtype, 82)
+    _, o_ref, l_ref = run_ring(case, x)
+    ev0 = rb.ra_cached_events()
+    nthreads, calls = 4, 6
+    results, errors = [None] * nthreads, []
+
+    def worker(t):
+        try:
+            with torch.cuda.stream(torch.cuda.Stream()):
+                ra = RingAttention(B, Hq, Hkv, S, d, R, layout, parity.torch_dtype(dtype), causal,
+                                   rank0=rank0, n_ranks=n_ranks)
+                q = parity.to_device(x["q"], dtype)
+                k = parity.to_device(x["k"], dtype)
+                v = parity.to_device(x["v"], dtype)
+                o = torch.zeros_like(o_ref)
+                lse = torch.zeros_like(l_ref)
+                for _ in range(calls):
+                    ra.run(q, k, v, o, lse, torch.cuda.current_stream())
+                torch.cuda.current_stream().synchronize()
+                results[t] = (o, lse)
+        except Exception as e:  # noqa: BLE001 -- reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(nthreads)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    for o, lse in results:
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+    assert rb.ra_cached_events() - ev0 <= nthreads * (2 * R + 2)

@@ -110,3 +110,21 @@ def test_ring_bwd_rank_subsets_match_oracle(case):
     check_grad(gq, rq, case[0] + " dq", rel_mean=rm)
     check_grad(gk, rk, case[0] + " dk", rel_mean=rm)
     check_grad(gv, rv, case[0] + " dv", rel_mean=rm)
+
+
+
+def test_ring_bwd_stream_delays_keep_results():
+    """Bounded sleeps on either stream of the backward ring leave the gradients
+    bitwise unchanged (the events order every hand-off)."""
+    import os
+    import torch
+    for case in (CASES[0], CASES[3], SUBSET_CASES[0]):
+        a = run(case, raw=True)
+        for var in ("RA_DEBUG_DELAY_COPY", "RA_DEBUG_DELAY_COMPUTE"):
+            os.environ[var] = "40"
+            try:
+                b = run(case, raw=True)
+            finally:
+                del os.environ[var]
+            for name, x, y in zip(("dq", "dk", "dv"), a, b):
+                assert torch.equal(x, y), (case[0], var, name)
