@@ -121,7 +121,8 @@ int ora_layout_maps(int layout, int64_t S, int32_t R, int32_t *fwd,
  *     l   = sum_{j in A} exp(s_j - m)
  *     O   = sum_{j in A} exp(s_j - m) v[b][g][j] / l
  *     LSE = m + ln l
- *   Two passes over the keys per row: the max, then the sums.
+ *   Two passes over the keys per row: the scores and their max, then the
+ *   sums (the scores of the first pass are kept for the second).
  *   Outputs o_rows [nrows][d] and lse_rows [nrows], double.
  */
 void ora_attention_rows(const float *q_rows, const int64_t *row_b,
@@ -140,24 +141,24 @@ void ora_attention_rows(const float *q_rows, const int64_t *row_b,
     const float *kb = k + (b * Hkv + g) * S * d;
     const float *vb = v + (b * Hkv + g) * S * d;
     int64_t last = causal ? t : S - 1; /* allowed keys are 0..last */
+    double *sc = (double *)malloc((size_t)(last + 1) * sizeof(double));
     double m = -INFINITY;
     for (int64_t j = 0; j <= last; ++j) {
       double s = 0.0;
       for (int64_t c = 0; c < d; ++c) s += (double)q[c] * (double)kb[j * d + c];
       s *= scale;
+      sc[j] = s;
       if (s > m) m = s;
     }
     double l = 0.0;
     double *o = o_rows + r * d;
     for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
     for (int64_t j = 0; j <= last; ++j) {
-      double s = 0.0;
-      for (int64_t c = 0; c < d; ++c) s += (double)q[c] * (double)kb[j * d + c];
-      s *= scale;
-      double p = exp(s - m);
+      double p = exp(sc[j] - m);
       l += p;
       for (int64_t c = 0; c < d; ++c) o[c] += p * (double)vb[j * d + c];
     }
+    free(sc);
     for (int64_t c = 0; c < d; ++c) o[c] /= l;
     lse_rows[r] = m + log(l);
   }

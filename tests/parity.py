@@ -52,7 +52,8 @@ def sample_tokens(fwd, n, rank0, n_ranks, count, seed):
     """Global tokens owned by the computed ranks: token 0 and S-1 when owned,
     the first and last local row of every computed rank (under the striped
     layout the first local row is the one with no key in blocks from higher
-    ranks), plus `count` seeded uniform picks."""
+    ranks), plus `count` seeded picks spread evenly over the eight 32-row
+    wave slots of a 256-row workgroup."""
     owned = np.asarray(fwd[rank0 * n:(rank0 + n_ranks) * n], np.int64)
     S = len(fwd)
     special = set()
@@ -65,6 +66,14 @@ def sample_tokens(fwd, n, rank0, n_ranks, count, seed):
     for r in range(rank0, rank0 + n_ranks):
         special.add(int(fwd[r * n]))
         special.add(int(fwd[r * n + n - 1]))
+    # picks spread evenly over the eight 32-row wave slots of the kernels' 256-row
+    # workgroups (the waves that lead and lag within a tile), by local row index
     rng = np.random.default_rng(seed)
-    picks = rng.choice(owned, size=min(count, owned.size), replace=False)
+    slot = (np.arange(owned.size) % n) % 256 // 32
+    picks = []
+    for c in range(8):
+        pool = owned[slot == c]
+        take = min(pool.size, count // 8 + (1 if c < count % 8 else 0))
+        if take:
+            picks.extend(rng.choice(pool, size=take, replace=False).tolist())
     return sorted(special), np.asarray(picks, np.int64)

@@ -23,6 +23,8 @@ RANDOM_ROWS = {1: 256, 2: 192, 3: 128, 4: 48, 5: 256}
 
 def _cases():
     for w in configs.ALL:
+        if w is configs.MHA_32K:  # compared on every row below
+            continue
         for layout in w.layouts:
             yield pytest.param(w, layout, id="%s-%s" % (w.name, layout))
     # the 2R-chunk zig-zag layout on the 1M-token share (rank 3 holds chunks 3 and 12)
@@ -76,3 +78,62 @@ def test_full_size_workload(w, layout):
     del data, q32, q, k, v, o, lse, ra
     gc.collect()
     torch.cuda.empty_cache()
+
+
+_MHA_OUT = {}
+
+
+def _mha_32k_outputs():
+    """Both layouts' outputs of the 32k MHA workload (computed once, kept on the host)."""
+    import torch
+    if _MHA_OUT:
+        return _MHA_OUT
+    w = configs.MHA_32K
+    data = inputs.qkv(w.B, w.Hq, w.Hkv, w.S, w.d, w.seed, w.dtype, w.q_scale)
+    tdt = parity.torch_dtype(w.dtype)
+    q = parity.to_device(data["q"], w.dtype)
+    k = parity.to_device(data["k"], w.dtype)
+    v = parity.to_device(data["v"], w.dtype)
+    for layout in w.layouts:
+        o = torch.zeros((w.B, w.Hq, w.S, w.d), dtype=tdt, device="cuda")
+        lse = torch.full((w.B, w.Hq, w.S), float("nan"), dtype=torch.float32, device="cuda")
+        ra = RingAttention(w.B, w.Hq, w.Hkv, w.S, w.d, w.R, layout, tdt, w.causal, w.scale,
+                           rank0=w.rank0, n_ranks=w.ranks)
+        ra.run(q, k, v, o, lse)
+        torch.cuda.synchronize()
+        _MHA_OUT[layout] = (o.cpu().double().numpy(), lse.cpu().double().numpy())
+        del ra, o, lse
+    del q, k, v
+    torch.cuda.empty_cache()
+    _MHA_OUT["data"] = data
+    return _MHA_OUT
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("heads", [(0, 8), (8, 16), (16, 24), (24, 32)],
+                         ids=lambda h: "heads%d-%d" % h)
+def test_32k_mha_every_row_both_layouts(heads):
+    """The 32k MHA workload compared on every query row, for the contiguous and
+    the striped layout, against the fp64 oracle over the whole sequence in the
+    original token order (1.7e10 allowed pairs in all; a quarter of the heads
+    per test)."""
+    w = configs.MHA_32K
+    h0, h1 = heads
+    print("\n[full] %s heads %d-%d: rings" % (w.name, h0, h1), flush=True)
+    out = _mha_32k_outputs()
+    data = out["data"]
+    print("[full] %s heads %d-%d: oracle on every row" % (w.name, h0, h1), flush=True)
+    ro, rl = oracle.attention_full(np.ascontiguousarray(data["q32"][:, h0:h1]),
+                                   np.ascontiguousarray(data["k32"][:, h0:h1]),
+                                   np.ascontiguousarray(data["v32"][:, h0:h1]), w.scale, w.causal)
+    for layout in w.layouts:
+        o, lse = out[layout]
+        err = np.abs(o[:, h0:h1] - ro)
+        mx, mean = float(err.max()), float(err.mean())
+        assert np.isfinite(err).all() and mx <= parity.O_MAX_ABS and mean <= parity.O_MEAN_ABS, (
+            layout, mx, mean)
+        lmx = parity.check_lse(lse[:, h0:h1], rl, w.name + " " + layout)
+        print("[full] %s %s heads %d-%d every row: O max %.3e mean %.3e LSE max %.3e" % (
+            w.name, layout, h0, h1, mx, mean, lmx), flush=True)
+    if h1 == w.Hq:
+        _MHA_OUT.clear()
