@@ -92,7 +92,8 @@ def cpu_baseline(w, data, layout_code, seconds_target, seed=4242):
     q32, k32, v32 = data["q32"], data["k32"], data["v32"]
     # calibrate with a few rows, then size the sample for ~seconds_target
     def run(nrows):
-        t = rng.choice(owned, size=nrows, replace=False)
+        # distinct tokens while the workload has enough of them (small ones repeat)
+        t = rng.choice(owned, size=nrows, replace=nrows > owned.size)
         b = rng.integers(0, w.B, nrows)
         hh = rng.integers(0, w.Hq, nrows)
         qrows = q32[b, hh, t]
