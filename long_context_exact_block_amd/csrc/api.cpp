@@ -159,13 +159,15 @@ DebugDelay debug_delay() {
 // kernels without taking their compute units, when the hop's MFMA work (4 d
 // flop per allowed (query, key) pair and query head at 1.3 PFLOP/s; a causal
 // block has about half its pairs; `work` scales for the backward's kernels)
-// lasts at least four times as long as moving the hop's bytes at a
-// deliberately low 1 TB/s -- the 1M-token share's hops, not the short hops
-// of 4096- or 512-token blocks, where the copy competes with the hop for
-// memory and the 64-workgroup copy costs less (measured side by side).
+// lasts at least half as long as moving the hop's bytes at a deliberately low
+// 1 TB/s -- the hops of the 1M-token share and of 4096-token blocks (32k
+// causal MHA over 8 ranks: 6.6 % shorter steps contiguous, 2 % striped), not
+// those of 512-token blocks, which are short and memory-heavy: there the copy
+// competes with the hop for HBM and the 64-workgroup copy costs less
+// (measured side by side).
 bool thin_handoff(double moved_bytes, double pairs_heads, int d, double work) {
   const double t_hop = work * 4.0 * d * pairs_heads / 1.3e15;
-  return t_hop > 4.0 * moved_bytes / 1.0e12;
+  return t_hop > 0.5 * moved_bytes / 1.0e12;
 }
 
 struct WsLayout {

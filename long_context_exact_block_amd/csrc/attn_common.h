@@ -184,41 +184,41 @@ __device__ __forceinline__ Work decode(const BatchParams &p, int ntq) {
 
 // Row-state load/store shared by both kernels.  The lane owns query row i and,
 // in each 32x32 O^T tile dt, the 16 values d = 32dt + 8(r/4) + 4*half + r%4.
+// The load has no branch, so m, l and O are requested together (and a kernel
+// can issue its first tile loads before them); a row that has seen no key yet
+// (l = 0) starts from O = 0 whatever its stored O holds.
 template <int D>
 __device__ __forceinline__ void load_state(const BatchParams &p, const Work &w, int i, bool valid,
                                            float c, f32x16 (&O)[D / 32], float &m_run,
                                            float &m_top, float &lsum) {
   const int hl = (threadIdx.x >> 5) & 1;
-  float m_acc = -INFINITY, l_acc = 0.f;
-  if (valid) {
-    const int64_t mi = w.z * p.ml_zstride + ((int64_t)w.b * p.Hq + w.h) * p.nq + i;
-    m_acc = p.m[mi];
-    l_acc = p.l[mi];
-  }
-  if (l_acc > 0.f) {
-    m_run = m_acc * kLog2e;
-    m_top = m_run;
-    lsum = hl ? 0.f : l_acc;
-    const float *orow = p.o + w.z * p.o_zstride + w.b * p.os_b + w.h * p.os_h + (int64_t)i * p.os_t;
+  // Lanes past the end of the block read row 0 (every block that has work
+  // has one) and drop what they read.
+  const int ii = valid ? i : 0;
+  const int64_t mi = w.z * p.ml_zstride + ((int64_t)w.b * p.Hq + w.h) * p.nq + ii;
+  const float m_ld = p.m[mi];
+  const float l_ld = p.l[mi];
+  const float *orow = p.o + w.z * p.o_zstride + w.b * p.os_b + w.h * p.os_h + (int64_t)ii * p.os_t;
+  float4 v[D / 32][4];
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const float4 v = *(const float4 *)(orow + 32 * dt + 8 * rg + 4 * hl);
-        O[dt][4 * rg + 0] = v.x * l_acc;
-        O[dt][4 * rg + 1] = v.y * l_acc;
-        O[dt][4 * rg + 2] = v.z * l_acc;
-        O[dt][4 * rg + 3] = v.w * l_acc;
-      }
-  } else {
-    m_run = -FLT_MAX;
-    m_top = -FLT_MAX;
-    lsum = 0.f;
+    for (int rg = 0; rg < 4; ++rg) v[dt][rg] = *(const float4 *)(orow + 32 * dt + 8 * rg + 4 * hl);
+  const float m_acc = valid ? m_ld : -INFINITY;
+  const float l_acc = valid ? l_ld : 0.f;
+  const bool seen = l_acc > 0.f;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
-  }
+    for (int rg = 0; rg < 4; ++rg) {
+      O[dt][4 * rg + 0] = seen ? v[dt][rg].x * l_acc : 0.f;
+      O[dt][4 * rg + 1] = seen ? v[dt][rg].y * l_acc : 0.f;
+      O[dt][4 * rg + 2] = seen ? v[dt][rg].z * l_acc : 0.f;
+      O[dt][4 * rg + 3] = seen ? v[dt][rg].w * l_acc : 0.f;
+    }
+  m_run = seen ? m_acc * kLog2e : -FLT_MAX;
+  m_top = m_run;
+  lsum = (seen && hl == 0) ? l_acc : 0.f;
   (void)c;
 }
 

@@ -65,7 +65,6 @@ __device__ __forceinline__ int chunk_swz(int row) {
 constexpr int kBufWord3 = 0x00020000;
 // s_waitcnt immediate waiting for vmcnt == 0 only (lgkmcnt, expcnt at max)
 constexpr int kWaitVm0 = 0x0F70;
-
 typedef __attribute__((address_space(3))) void lds_void;
 
 // 16 bytes per lane from a raw buffer straight into LDS: lane l's bytes land
@@ -135,31 +134,21 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
 
   f32x16 O[DT];
   float m_run, m_top, lsum;
-  if (p.accumulate) {
-    load_state<D>(p, w, i, valid, c, O, m_run, m_top, lsum);
-  } else {
-    m_run = -FLT_MAX;
-    m_top = -FLT_MAX;
-    lsum = 0.f;
+  auto init_state = [&]() {  // the running state, or an empty one
+    if (p.accumulate) {
+      load_state<D>(p, w, i, valid, c, O, m_run, m_top, lsum);
+    } else {
+      m_run = -FLT_MAX;
+      m_top = -FLT_MAX;
+      lsum = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
-  }
+        for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
+    }
+  };
 
   if (ntiles > 0) {
-    // Q fragments (B operand of S^T = K Q^T): d = 16ks + 8hl .. +7 of this lane's row
-    s16x8 qf[KS];
-    {
-      const short *qrow = qp + (int64_t)(valid ? i : 0) * p.qs_t;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s16x8 v = *(const s16x8 *)(qrow + 16 * ks + 8 * hl);
-        if (!valid) v = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
-        qf[ks] = v;
-      }
-    }
-
     // Tile loads go through buffer descriptors: the per-lane byte offsets are
     // fixed, the tile moves the (scalar) base, and K rows past the end of the
     // block read as zero (they are masked).  Offsets fit in 32 bits: the host
@@ -210,6 +199,27 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
               tv * VTILE);
     };
 
+    // The first tiles, the Q fragments and the running state are requested
+    // together, so their latencies overlap: K tiles 0 and 1 and V^T tile 0
+    // (awaited before the prologue's barrier) ...
+    load_k(0, 0);
+    if (ntiles > 1) load_k(1, 1);
+    load_v(0, 0);
+    // ... Q fragments (B operand of S^T = K Q^T): d = 16ks + 8hl .. +7 of
+    // this lane's row ...
+    s16x8 qf[KS];
+    {
+      const short *qrow = qp + (int64_t)(valid ? i : 0) * p.qs_t;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s16x8 v = *(const s16x8 *)(qrow + 16 * ks + 8 * hl);
+        if (!valid) v = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
+        qf[ks] = v;
+      }
+    }
+    // ... and the running state.
+    init_state();
+
     // Per-lane LDS read offsets.  Row kh*32 + c32 (K) and 32dt + c32 (V^T)
     // share the swizzle of row c32, so kh, dt and the stage are immediates.
     int koff[KS];
@@ -258,9 +268,6 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
     };
 
     // Prologue: K tiles 0 and 1, V^T tile 0 resident; S^T of tile 0.
-    load_k(0, 0);
-    if (ntiles > 1) load_k(1, 1);
-    load_v(0, 0);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     f32x16 S[2], S1[2];
@@ -424,6 +431,8 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
     }
     // the lagging waves' PV of the last tile (no stage is reloaded any more)
     if (lag && ntiles_w == ntiles) pv((vst == 0 ? 2 : vst - 1) * VTILE, S);
+  } else {
+    init_state();
   }
   store_state<D>(p, w, i, valid, O, m_run, EXACT ? m_top : m_run, lsum);
 }
