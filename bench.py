@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA
 
 
 def traffic_from_profile(kernel_sources, summary):
@@ -57,25 +58,52 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def kernel_name(w):
+    """The block kernel a ring of this workload runs."""
+    if w.dtype == "fp32":
+        return "attn_block32_kernel<%d>" % w.d
+    return "attn_packed_kernel<%d,%s>" % (w.d, w.dtype)
+
+
+def rank_hop_pairs(w, layout_code, r, h):
+    """Allowed (query, key) pairs per head of computed rank r at hop h."""
+    n, R = w.n, w.R
+    s = (r - h) % R
+    if not w.causal:
+        return n * n
+    if layout_code == 0:  # contiguous: past block full, own block triangle, future none
+        return n * n if s < r else (n * (n + 1) // 2 if s == r else 0)
+    if layout_code == 1:  # striped: key j allowed iff j*R+s <= i*R+r
+        return n * (n + 1) // 2 if s <= r else n * (n - 1) // 2
+    c = n // 2  # zig-zag: chunks {r, 2R-1-r} x {s, 2R-1-s}, c tokens each
+    tot = 0
+    for X in (r, 2 * R - 1 - r):
+        for Y in (s, 2 * R - 1 - s):
+            tot += c * c if Y < X else (c * (c + 1) // 2 if Y == X else 0)
+    return tot
+
+
 def hop_pairs(w, layout_code):
     """Allowed (query, key) pairs per head at each hop, summed over computed ranks."""
-    n, R = w.n, w.R
+    return [sum(rank_hop_pairs(w, layout_code, r, h) for r in range(w.rank0, w.rank0 + w.ranks))
+            for h in range(w.R)]
+
+
+def hop_bytes(w, layout_code, fused):
+    """Algorithmic HBM bytes of the block kernel at each hop, summed over computed ranks:
+    for every rank whose block has allowed pairs, its Q shard and the K/V block read once,
+    the fp32 O and the row statistics m, l written, and read back when the kernel folds
+    into the running state (fused fold, every hop after the first).  A rank whose block
+    has no allowed pair moves nothing."""
+    elt = {"bf16": 2, "fp16": 2, "fp32": 4}[w.dtype]
+    qkv = (w.Hq + 2 * w.Hkv) * w.B * w.n * w.d * elt
+    state = w.B * w.Hq * w.n * (w.d + 2) * 4
     out = []
-    for h in range(R):
+    for h in range(w.R):
         tot = 0
         for r in range(w.rank0, w.rank0 + w.ranks):
-            s = (r - h) % R
-            if not w.causal:
-                tot += n * n
-            elif layout_code == 0:  # contiguous: past block full, own block triangle, future none
-                tot += n * n if s < r else (n * (n + 1) // 2 if s == r else 0)
-            elif layout_code == 1:  # striped: key j allowed iff j*R+s <= i*R+r
-                tot += n * (n + 1) // 2 if s <= r else n * (n - 1) // 2
-            else:  # zig-zag: chunks {r, 2R-1-r} x {s, 2R-1-s}, c tokens each
-                c = n // 2
-                for X in (r, 2 * R - 1 - r):
-                    for Y in (s, 2 * R - 1 - s):
-                        tot += c * c if Y < X else (c * (c + 1) // 2 if Y == X else 0)
+            if rank_hop_pairs(w, layout_code, r, h) > 0:
+                tot += qkv + state * (2 if (fused and h > 0) else 1)
         out.append(tot)
     return out
 
@@ -592,6 +620,11 @@ def main():
     pairs = hop_pairs(w, lcode)
     flops_per_launch = [4.0 * w.d * w.B * w.Hq * p for p in pairs]
     achieved = sum(flops_per_launch) * K / (hop_ms.sum() * 1e-3) / 1e12
+    bytes_per_launch = hop_bytes(w, lcode, args.merge == "fused")
+    achieved_gbs = sum(bytes_per_launch) * K / (hop_ms.sum() * 1e-3) / 1e9
+    peak_dt = PEAK_BF16_TFLOPS if w.dtype != "fp32" else PEAK_FP32_TFLOPS
+    # the kernel's roof: MFMA time or HBM time of its algorithmic work, whichever is longer
+    hbm_bound = sum(bytes_per_launch) / (PEAK_HBM_GBS * 1e9) > sum(flops_per_launch) / (peak_dt * 1e12)
     value = w.metric_flops() / (ms_per_step * 1e-3) / 1e12
     exact_flops = 4.0 * w.d * w.B * w.Hq * sum(pairs)
     log("step %.2f ms, %.1f TFLOP/s; block kernel %.1f TFLOP/s" % (ms_per_step, value, achieved))
@@ -666,11 +699,20 @@ def main():
                    "merge": args.merge},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "exact_pair_tflops": round(exact_flops / (ms_per_step * 1e-3) / 1e12, 3),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "attn_packed_kernel<128,bf16>" if w.dtype != "fp32" else "attn_block32_kernel",
-                     "launches": R * K, "avg_launch_ms": round(float(hop_ms.mean()), 4),
-                     "algorithmic_flops_per_launch": sum(flops_per_launch) / R},
+        "roofline": dict(
+            ({"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS,
+              "unit": "GB/s", "frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
+              "mfma_view": {"achieved": round(achieved, 3), "peak": peak_dt, "unit": "TFLOP/s",
+                            "frac": round(achieved / peak_dt, 4)}}
+             if hbm_bound else
+             {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak_dt,
+              "unit": "TFLOP/s", "frac": round(achieved / peak_dt, 4),
+              "hbm_view": {"achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": round(achieved_gbs / PEAK_HBM_GBS, 4)}}),
+            traffic=traffic, kernel=kernel_name(w), launches=R * K,
+            avg_launch_ms=round(float(hop_ms.mean()), 4),
+            algorithmic_flops_per_launch=sum(flops_per_launch) / R,
+            algorithmic_bytes_per_launch=sum(bytes_per_launch) / R),
         "step_ms_median": round(float(np.median(step_ms)), 3),
         "step_ms_min": round(float(step_ms.min()), 3),
         "hop_ms": [round(float(x), 3) for x in hop_ms.mean(axis=0)],
