@@ -235,22 +235,29 @@ def step_parts_bench(torch, rb, ra, w, q, k, v, o, lse, iters=10):
     return parts
 
 
-def overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse, t_copy_ms,
-                  steps=3):
-    """How much of the K/V hand-off the compute hides: the same step with the
-    blocks read in place (SWAP, no transfer), and the hop copies alone (the
-    library's hand-off copy of the hand-off bytes, once per hop, on one stream)."""
+def overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse, ra_copy,
+                  pairs=5):
+    """How much of the K/V hand-off the compute hides: steps with the hand-off
+    (COPY) and with the blocks read in place (SWAP, no transfer) alternate, so
+    clock drift falls on both alike, and the hop copies alone (the library's
+    hand-off copy of the hand-off bytes, once per hop, on one stream).
+    overlap = 1 - median(step_copy - step_swap) / copies alone."""
     ra = RingAttention(w.B, w.Hq, w.Hkv, w.S, w.d, w.R, layout, tdt, w.causal, w.scale,
                        rank0=w.rank0, n_ranks=w.ranks, handoff=rb.HANDOFF_SWAP)
     ra.run(q, k, v, o, lse)
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ra_copy.run(q, k, v, o, lse)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4 * pairs)]
     torch.cuda.synchronize()
-    e[0].record()
-    for s in range(steps):
-        ra.run(q, k, v, o, lse)
-        e[s + 1].record()
+    for s in range(pairs):
+        for j, r in enumerate((ra_copy, ra)):
+            e[4 * s + 2 * j].record()
+            r.run(q, k, v, o, lse)
+            e[4 * s + 2 * j + 1].record()
     torch.cuda.synchronize()
-    t_swap = float(np.median([e[s].elapsed_time(e[s + 1]) for s in range(steps)]))
+    t_c = np.array([e[4 * s].elapsed_time(e[4 * s + 1]) for s in range(pairs)])
+    t_s = np.array([e[4 * s + 2].elapsed_time(e[4 * s + 3]) for s in range(pairs)])
+    t_copy_ms, t_swap = float(np.median(t_c)), float(np.median(t_s))
+    t_diff = float(np.median(t_c - t_s))
     del ra
     elt = 4 if w.dtype == "fp32" else 2
     k_bytes = w.ranks * w.B * w.Hkv * w.n * w.d * elt
@@ -276,10 +283,10 @@ def overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse, t_c
     return {"step_ms_copy": round(t_copy_ms, 3), "step_ms_swap": round(t_swap, 3),
             "copies_alone_ms": round(t_copies, 3), "copy_form": "thin" if thin else "wide",
             "bytes_per_hop": per_hop, "copy_GB/s": round(moved / (t_copies * 1e-3) / 1e9, 1),
-            "overlap": round(1.0 - (t_copy_ms - t_swap) / t_copies, 3) if t_copies > 0 else None}
+            "overlap": round(1.0 - t_diff / t_copies, 3) if t_copies > 0 else None}
 
 
-def backward_bench(torch, ra, w, layout_code, q, k, v, iters=2):
+def backward_bench(torch, ra, w, layout_code, q, k, v, iters=3):
     """ra_ring_bwd after the forward ring (same shards): MFMA roofline with the
     algorithmic count of the backward, 10*d FLOP per allowed pair per query head
     (S = QK^T, dP = dO V^T, dV, dK, dQ; recomputing S and dP for dQ is not credited).
@@ -296,23 +303,25 @@ def backward_bench(torch, ra, w, layout_code, q, k, v, iters=2):
     dv = torch.empty_like(v)
     ra.backward(dout, dq, dk, dv)  # warm-up, allocates the workspace
 
-    def timed(handoff):
-        ra.bargs.handoff = handoff
-        rb_ring_bwd(ra)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    def timed(handoffs):
+        """One pass per entry of `handoffs`, in that order; the pass times."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(handoffs))]
         torch.cuda.synchronize()
-        ev[0].record()
-        for i in range(iters):
+        for i, hm in enumerate(handoffs):
+            ra.bargs.handoff = hm
+            ev[2 * i].record()
             rb_ring_bwd(ra)
-            ev[i + 1].record()
+            ev[2 * i + 1].record()
         torch.cuda.synchronize()
-        return np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(iters)])
+        return np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(len(handoffs))])
 
     handoff0 = ra.bargs.handoff
-    ms = timed(handoff0)
+    rb_ring_bwd(ra)
     handoff = None
     if handoff0 == rb.HANDOFF_COPY and w.R > 1:
-        ms_swap = timed(rb.HANDOFF_SWAP)
+        # passes with the hand-off and with the blocks in place alternate
+        t = timed([handoff0, rb.HANDOFF_SWAP] * iters)
+        ms, ms_swap = t[0::2], t[1::2]
         ra.bargs.handoff = handoff0
         kz = w.B * w.Hkv * w.n * w.d
         n_pad = (w.n + 63) // 64 * 64
@@ -334,12 +343,15 @@ def backward_bench(torch, ra, w, layout_code, q, k, v, iters=2):
         t_copies = c0.elapsed_time(c1)
         del src, dst
         t_copy, t_swap = float(np.median(ms)), float(np.median(ms_swap))
+        t_diff = float(np.median(ms - ms_swap))
         moved = 2.0 * (per_hop * (w.R - 1) + home)
         handoff = {"ms_copy": round(t_copy, 3), "ms_swap": round(t_swap, 3),
                    "copies_alone_ms": round(t_copies, 3), "copy_form": "thin" if thin else "wide",
                    "bytes_per_hop": per_hop,
                    "copy_GB/s": round(moved / (t_copies * 1e-3) / 1e9, 1),
-                   "overlap": round(1.0 - (t_copy - t_swap) / t_copies, 3) if t_copies > 0 else None}
+                   "overlap": round(1.0 - t_diff / t_copies, 3) if t_copies > 0 else None}
+    else:
+        ms = timed([handoff0] * iters)
     pairs = sum(hop_pairs(w, layout_code))
     flops = 10.0 * w.d * w.B * w.Hq * pairs
     med = float(np.median(ms))
@@ -631,8 +643,7 @@ def main():
 
     handoff = None
     if args.handoff == "copy" and w.R > 1 and not args.no_overlap_bench:
-        handoff = overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse,
-                                float(np.median(step_ms)))
+        handoff = overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse, ra)
     merge = None if args.no_merge_bench else merge_bench(torch, rb)
     parts = None
     if not args.no_parts_bench:

@@ -208,11 +208,9 @@ ra_status ra_merge(float *o_acc, float *m_acc, float *l_acc, const float *o_blk,
  * issue on their copy stream, with non-temporal loads and stores:
  *   thin = 1: one-wave workgroups of 16 VGPRs that fit in the registers the
  *     attention kernels leave free, so they run beside them without
- *     displacing their workgroups.  The rings use it when a hop's estimated
- *     MFMA time (4 d flop per allowed pair and query head at 1.3 PFLOP/s;
- *     3.2 times that for the backward) is at least four times the time the
- *     hop's bytes take at 1 TB/s.
- *   thin = 0: 64 workgroups of 256 threads, for short hops.
+ *     displacing their workgroups.  The rings use it where ra_handoff_thin
+ *     says so.
+ *   thin = 0: 64 workgroups of 256 threads, for short, memory-heavy hops.
  * dst, src: device pointers, not overlapping; 16-byte aligned pointers and a
  * multiple of 16 bytes take the kernels, anything else falls back to
  * hipMemcpyAsync.  Asynchronous.
@@ -221,6 +219,17 @@ ra_status ra_merge(float *o_acc, float *m_acc, float *l_acc, const float *o_blk,
  */
 ra_status ra_handoff_copy(void *dst, const void *src, size_t bytes, int32_t thin,
                           ra_stream stream);
+
+/*
+ * ra_handoff_thin -- which hand-off copy form the rings use for a hop
+ * (instrumentation: lets a benchmark time the copies alone in that form).
+ * Returns 1 (thin) when the hop's estimated MFMA time -- `work` times 4 d flop
+ * per allowed (query, key) pair and query head, `pairs_heads` of them, at
+ * 1.3 PFLOP/s; work = 1 for the forward, 3.2 for the backward's kernels -- is
+ * at least half the time the hop's `moved_bytes` (read plus written) take at
+ * 1 TB/s; else 0.  Host-only arithmetic: no device call, no error.
+ */
+int32_t ra_handoff_thin(double moved_bytes, double pairs_heads, int32_t d, double work);
 
 /*
  * ra_finalize -- running state to outputs: out = O rounded to nearest even

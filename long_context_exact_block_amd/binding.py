@@ -30,7 +30,8 @@ EXPORTED = ("ra_version", "ra_status_string", "ra_last_error", "ra_layout_permut
             "ra_pack_v", "ra_merge", "ra_finalize", "ra_ring_fwd_workspace_size", "ra_ring_fwd",
             "ra_causal_work", "ra_decode_fwd_workspace_size", "ra_decode_fwd",
             "ra_block_bwd_workspace_size", "ra_block_bwd", "ra_ring_bwd_workspace_size",
-            "ra_ring_bwd", "ra_handoff_copy", "ra_decode_fwd_noalloc", "ra_cached_events")
+            "ra_ring_bwd", "ra_handoff_copy", "ra_handoff_thin", "ra_decode_fwd_noalloc",
+            "ra_cached_events")
 
 
 class RAError(RuntimeError):
@@ -118,6 +119,8 @@ def lib():
     L.ra_packed_v_bytes.restype = ctypes.c_size_t
     L.ra_pack_v.argtypes = [P, P, I32, I32, I32, I32, I32, ctypes.POINTER(I64), P]
     L.ra_handoff_copy.argtypes = [P, P, ctypes.c_size_t, I32, P]
+    L.ra_handoff_thin.argtypes = [ctypes.c_double, ctypes.c_double, I32, ctypes.c_double]
+    L.ra_handoff_thin.restype = I32
     L.ra_merge.argtypes = [P, P, P, P, P, P, I64, I32, P]
     L.ra_finalize.argtypes = [P, P, P, P, P, I32, I64, I32, P]
     L.ra_ring_fwd_workspace_size.argtypes = [ctypes.POINTER(RingArgs)]
@@ -238,9 +241,8 @@ def ra_handoff_copy(dst, src, nbytes=None, stream=None, thin=False):
 
 
 def thin_handoff(moved_bytes, pairs_heads, d, work=1.0):
-    """Whether a ring uses the thin hand-off copy: the same rule as the library
-    (hop MFMA time at 1.3 PFLOP/s at least four times the thin copy's at 1 TB/s)."""
-    return work * 4.0 * d * pairs_heads / 1.3e15 > 4.0 * moved_bytes / 1.0e12
+    """Whether a ring uses the thin hand-off copy (the library's rule, ra_handoff_thin)."""
+    return bool(lib().ra_handoff_thin(float(moved_bytes), float(pairs_heads), int(d), float(work)))
 
 
 def ra_merge(o_acc, m_acc, l_acc, o_blk, m_blk, l_blk, stream=None):

@@ -697,6 +697,10 @@ ra_status ra_handoff_copy(void *dst, const void *src, size_t bytes, int32_t thin
   return RA_OK;
 }
 
+int32_t ra_handoff_thin(double moved_bytes, double pairs_heads, int32_t d, double work) {
+  return thin_handoff(moved_bytes, pairs_heads, d, work) ? 1 : 0;
+}
+
 ra_status ra_merge(float *o_acc, float *m_acc, float *l_acc, const float *o_blk,
                    const float *m_blk, const float *l_blk, int64_t rows, int32_t d,
                    ra_stream stream) {

@@ -170,6 +170,23 @@ def test_handoff_copy_rejects(lib):
     assert lib.ra_handoff_copy(4096, 4096, 16, 2, None) == 1
 
 
+def test_handoff_form_rule(lib):
+    """The copy form the rings pick (ra_handoff_thin): the thin copy beside long hops
+    (the 1M-token share, 4096-token blocks, the backward on the 1M share), the
+    64-workgroup copy for 512-token shards and tiny rings."""
+    def form(B, Hq, Hkv, n, d, ranks, causal, elt=2, work=1.0):
+        moved = 2.0 * ranks * 2 * B * Hkv * n * d * elt
+        pairs = ranks * B * Hq * float(n) * n * (0.5 if causal else 1.0)
+        return rb.thin_handoff(moved, pairs, d, work)
+    assert form(1, 8, 8, 131072, 128, 1, True)                   # 1M share, rank 3 of 8
+    assert form(1, 8, 8, 131072, 128, 1, True, work=3.2)         # its backward
+    assert form(1, 32, 32, 4096, 128, 8, True)                   # 32k MHA, R = 8
+    assert form(1, 32, 8, 16384, 128, 8, True)                   # 128k GQA, R = 8
+    assert not form(4, 16, 16, 512, 64, 64, False)               # 512-token shards, R = 64
+    assert not form(1, 2, 2, 256, 64, 4, True, elt=4)            # tiny fp32 ring
+    assert lib.ra_handoff_thin(0.0, 0.0, 128, 1.0) == 0          # nothing to hide behind
+
+
 def test_merge_finalize_reject(lib):
     assert lib.ra_merge(4096, 4096, 4096, 4096, 4096, 4096, 10, 6, None) == 2
     assert lib.ra_merge(4100, 4096, 4096, 4096, 4096, 4096, 10, 8, None) == 4
