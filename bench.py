@@ -243,7 +243,8 @@ def overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse, ra_
     hand-off copy of the hand-off bytes, once per hop, on one stream).
     overlap = 1 - median(step_copy - step_swap) / copies alone."""
     ra = RingAttention(w.B, w.Hq, w.Hkv, w.S, w.d, w.R, layout, tdt, w.causal, w.scale,
-                       rank0=w.rank0, n_ranks=w.ranks, handoff=rb.HANDOFF_SWAP)
+                       rank0=w.rank0, n_ranks=w.ranks, handoff=rb.HANDOFF_SWAP,
+                       merge_mode=ra_copy.merge_mode)
     ra.run(q, k, v, o, lse)
     ra_copy.run(q, k, v, o, lse)
     e = [torch.cuda.Event(enable_timing=True) for _ in range(4 * pairs)]
