@@ -478,13 +478,13 @@ hipError_t launch_packed(const BatchParams &p, hipStream_t s) {
   const int ntq = (p.nq + kPBM - 1) / kPBM;
   const int64_t nwg = (int64_t)ntq * p.nz * p.B * p.Hq;
   const size_t lds = (size_t)2 * kPBN * D * 2 + (size_t)3 * D * kPBN * 2;
-  static bool attr_set = false;  // more than 64 KB of LDS per workgroup must be opted into
-  if (!attr_set && lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void *)attn_packed_kernel<D, BF16, EXACT>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // more than 64 KB of LDS per workgroup must be opted into, once per process
+  // (a function-local static: initialised once even with several host threads)
+  static const hipError_t attr =
+      lds > 65536 ? hipFuncSetAttribute((const void *)attn_packed_kernel<D, BF16, EXACT>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
+                  : hipSuccess;
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((attn_packed_kernel<D, BF16, EXACT>), dim3((unsigned)nwg), dim3(512), lds, s,
                      p, ntq);
   return hipGetLastError();

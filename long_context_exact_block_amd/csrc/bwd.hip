@@ -731,8 +731,9 @@ hipError_t launch_bwd_d(const BwdParams &P, hipStream_t s, int parts) {
   const int64_t groups = (int64_t)p.nz * p.B;
   constexpr size_t lv = 2 * kv_stage_bytes<D, kRoleV>(), lk = 2 * kv_stage_bytes<D, kRoleK>(),
                    l2 = 2 * dq_stage_bytes<D>();
-  static bool attr_set = false;  // more than 64 KB of LDS per workgroup must be opted into
-  if (!attr_set) {
+  // more than 64 KB of LDS per workgroup must be opted into, once per process
+  // (a function-local static: initialised once even with several host threads)
+  static const hipError_t attr = [] {
     hipError_t e = hipFuncSetAttribute((const void *)bwd_kv_kernel<D, BF16, kRoleV>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lv);
     if (e == hipSuccess)
@@ -741,9 +742,9 @@ hipError_t launch_bwd_d(const BwdParams &P, hipStream_t s, int parts) {
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void *)bwd_dq_kernel<D, BF16>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)l2);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+    return e;
+  }();
+  if (attr != hipSuccess) return attr;
   if (p.nk > 0 && (parts & 1)) {
     const int64_t n1 = groups * p.Hkv * ((p.nk + kKW * 32 - 1) / (kKW * 32));
     hipLaunchKernelGGL((bwd_kv_kernel<D, BF16, kRoleV>), dim3((unsigned)n1), dim3(kKW * 64), lv,

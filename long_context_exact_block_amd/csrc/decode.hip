@@ -390,13 +390,13 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(const float *__restr
 template <int D, bool BF16>
 hipError_t launch_decode_d(const DecodeParams &p, hipStream_t s) {
   constexpr size_t lds = decode_lds_bytes<D>();
-  static bool attr_set = false;  // more than 64 KB of LDS per workgroup must be opted into
-  if (!attr_set && lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void *)decode_kernel<D, BF16>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // more than 64 KB of LDS per workgroup must be opted into, once per process
+  // (a function-local static: initialised once even with several host threads)
+  static const hipError_t attr =
+      lds > 65536 ? hipFuncSetAttribute((const void *)decode_kernel<D, BF16>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
+                  : hipSuccess;
+  if (attr != hipSuccess) return attr;
   dim3 grid((unsigned)(p.R * p.B * p.Hkv * p.splits), (unsigned)p.col_blocks);
   hipLaunchKernelGGL((decode_kernel<D, BF16>), grid, dim3(kDW * 64), lds, s, p);
   return hipGetLastError();
