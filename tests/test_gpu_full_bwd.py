@@ -1,7 +1,7 @@
 """The backward pass at full size, in the configuration the benchmark times (the
 forward ring with its default hand-off and fused fold, then ra_ring_bwd over
 the same shards), checked against the fp64 oracle on gradients it can compute
-one at a time, and on two identities that hold at any size.
+one at a time, and on identities that hold at any size.
 
 * dq of sampled query rows of the computed ranks (the first and last local row
   of each, token 0 and S-1 when owned, seeded picks): a row needs only its own
@@ -20,6 +20,12 @@ one at a time, and on two identities that hold at any size.
   so they move the sum by about 2^-9 of that norm per stage; the bound of 5e-2
   is some 25 times that spread, while a dropped or doubled share of the pairs
   moves it by a sizeable fraction of the norm or more.
+* Over every row and key, sum_i <dq_i, q_i> = sum_j <dk_j, k_j> (both are
+  scale * sum_ij dS_ij <q_i, k_j>) and sum_j <dv_j, v_j> = sum_i <dO_i, O_i>
+  (each row's probabilities average its values), per batch and K/V head, with
+  the same bound against the root sum of squares of the per-row and per-key
+  terms: they tie the dq kernel to the dk kernel, and dv to the forward output,
+  on every key rather than the tail only.
 """
 import gc
 import math
@@ -51,7 +57,8 @@ def _dout(w):
 
 
 def ring_grads(w, layout, data, g_st, tag):
-    """Forward ring then ra_ring_bwd on the GPU; returns dq, dk, dv (device tensors)."""
+    """Forward ring then ra_ring_bwd on the GPU; returns dq, dk, dv and the forward's O
+    (device tensors)."""
     import torch
     tdt = parity.torch_dtype(w.dtype)
     q = parity.to_device(data["q"], w.dtype)
@@ -74,8 +81,8 @@ def ring_grads(w, layout, data, g_st, tag):
     ra.backward(dout, dq, dk, dv)
     torch.cuda.synchronize()
     print("%s: backward done" % tag, flush=True)
-    del q, k, v, dout, o, lse, ra
-    return dq, dk, dv
+    del q, k, v, dout, lse, ra
+    return dq, dk, dv, o
 
 
 @pytest.mark.timeout(900)
@@ -92,7 +99,7 @@ def check_backward(w, layout, kv_heads, tail, n_rand, grads):
     print("\n%s: inputs" % tag, flush=True)
     data = inputs.qkv(w.B, w.Hq, w.Hkv, w.S, w.d, w.seed, w.dtype, w.q_scale)
     g_st, g32 = _dout(w)
-    dq, dk, dv = grads(w, layout, data, g_st, tag)
+    dq, dk, dv, o = grads(w, layout, data, g_st, tag)
     del g_st
 
     fwd, _ = oracle.layout_maps(rb.LAYOUTS[layout], w.S, w.R)
@@ -147,7 +154,40 @@ def check_backward(w, layout, kv_heads, tail, n_rand, grads):
     assert not np.any(gk[unseen]) and not np.any(gv[unseen]), "%s: unseen keys not zero" % tag
     print("%s: tail keys ok (%d never seen), dk max err %.3e, dv max err %.3e" % (
         tag, int(unseen.sum()), np.abs(gk - rk).max(), np.abs(gv - rv).max()), flush=True)
-    del q32, rq, rk, rv, gq, gk, gv
+    del rq, rk, rv, gq, gk, gv
+
+    # --- inner-product identities over every row and key, per (batch, K/V head):
+    #   sum_i <dq_i, q_i> = sum_j <dk_j, k_j>  (both are scale * sum_ij dS_ij <q_i, k_j>),
+    #   sum_j <dv_j, v_j> = sum_i <dO_i, O_i>  (each row's probabilities average its values),
+    # i over the computed ranks' rows of the group's query heads, j over all keys.  They tie
+    # the dq kernel to the dk kernel and dv to the forward output on every key, not only the
+    # tail.  Measured against the root sum of squares of the per-row / per-key terms: the
+    # 16-bit roundings move each term by about 2^-9 of itself, independently.
+    def dots(gpu_rows, host_rows):
+        x = torch.from_numpy(np.ascontiguousarray(host_rows)).to(gpu_rows.device, torch.float64)
+        return (gpu_rows.double() * x).sum(-1)
+
+    worst = [0.0, 0.0]
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            sums, rss = [0.0] * 4, [0.0] * 4
+            terms = [[dots(dq[b, h], q32[b, h]) for h in range(g * group, (g + 1) * group)],
+                     [dots(dk[b, g], k32[b, g])],
+                     [dots(dv[b, g], v32[b, g])],
+                     [dots(o[b, h], g32[b, h]) for h in range(g * group, (g + 1) * group)]]
+            for c, ts in enumerate(terms):
+                sums[c] = float(sum(t.sum() for t in ts))
+                rss[c] = math.sqrt(float(sum((t * t).sum() for t in ts)))
+            e_qk = abs(sums[0] - sums[1]) / (rss[0] + rss[1])
+            e_vo = abs(sums[2] - sums[3]) / (rss[2] + rss[3])
+            worst = [max(worst[0], e_qk), max(worst[1], e_vo)]
+            assert e_qk <= SUM_REL, "%s: sum <dq,q> vs sum <dk,k> off by %.3e (b %d, kv %d)" % (
+                tag, e_qk, b, g)
+            assert e_vo <= SUM_REL, "%s: sum <dv,v> vs sum <dO,O> off by %.3e (b %d, kv %d)" % (
+                tag, e_vo, b, g)
+    print("%s: |sum<dq,q> - sum<dk,k>| %.3e, |sum<dv,v> - sum<dO,O>| %.3e (of the root sum of "
+          "squares of the terms)" % (tag, worst[0], worst[1]), flush=True)
+    del q32, o
     data.clear()
 
     # --- identities over all keys, per (batch, K/V head, component)
