@@ -152,8 +152,9 @@ struct Work {
 // (measured: 4-8 % less time on the 32k MHA, 128k GQA and 512-token-shard
 // workloads than when an XCD's concurrent workgroups span all its groups).
 // Otherwise heaviest tiles first over all groups.
-__device__ __forceinline__ Work decode(const BatchParams &p, int ntq) {
-  const int hpg = p.Hq / p.Hkv;
+// hpg: query heads of a K/V group that are work items of their own (1 when a
+// workgroup serves all the heads of its group).
+__device__ __forceinline__ Work decode_items(const BatchParams &p, int ntq, int hpg) {
   const int NG = p.nz * p.B * p.Hkv;
   const int L = blockIdx.x;
   int trank, g, hh;
@@ -178,8 +179,11 @@ __device__ __forceinline__ Work decode(const BatchParams &p, int ntq) {
   const int zb = g / p.Hkv;
   w.b = zb % p.B;
   w.z = zb / p.B;
-  w.h = w.kvh * hpg + hh;
+  w.h = w.kvh * (p.Hq / p.Hkv) + hh;
   return w;
+}
+__device__ __forceinline__ Work decode(const BatchParams &p, int ntq) {
+  return decode_items(p, ntq, p.Hq / p.Hkv);
 }
 
 // Row-state load/store shared by both kernels.  The lane owns query row i and,

@@ -27,6 +27,10 @@
 //  * Between hops only m + ln l matters, so the fused ring skips the per-tile
 //    row max: exponentials use the running maximum and a tile whose
 //    probabilities grow too large is redone after raising it.
+//  * Grouped heads (2, 4 or 8 query heads per K/V head): a workgroup serves
+//    all query heads of its K/V head from each loaded tile, 256 / group rows of
+//    each (same-run: as fast as one head per workgroup -- each tile already
+//    serves 256 rows, and the heads' workgroups ran together on one XCD).
 #include <cfloat>
 #include <cmath>
 #include <type_traits>
@@ -84,7 +88,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, lds_void *dst
 // whose probabilities would exceed 2^kTau (a larger maximum arrived) is redone
 // after rescaling.
 template <int D, bool BF16, bool EXACT>
-__global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq) {
+__global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq, int hshift) {
   using M = Mfma16<BF16>;
   constexpr int KS = D / 16;             // k-steps of the QK product
   constexpr int DT = D / 32;             // 32-wide d tiles of O
@@ -101,9 +105,13 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
   static_assert(KPW * kLW * 1024 == KTILE && VPW * kLW * 1024 == VTILE, "tile must split over the waves");
   extern __shared__ __attribute__((aligned(1024))) char lds[];
 
-  const Work w = decode(p, ntq);
   // the wave index is uniform: keep it in a scalar register
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // 2^hshift query heads of a K/V group per workgroup (GQA): wave w serves head
+  // w >> (3 - hshift) of the group, rows of its 256 >> hshift
+  Work w = hshift ? decode_items(p, ntq, 1) : decode(p, ntq);
+  w.h += wave >> (3 - hshift);
+  const int wave_r = wave & ((kPW >> hshift) - 1);  // the wave's 32-row slot in its head's rows
   const int lane = threadIdx.x & 63;
   const int hl = lane >> 5, c32 = lane & 31;
 
@@ -114,9 +122,9 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
   const IdMap qid = query_ids(p, w.z), kid = key_ids(p, w.z);
   const float c = p.scale * kLog2e;
 
-  const int i_wg0 = w.qtile * kPBM;
-  const int i_wg1 = min(p.nq, i_wg0 + kPBM) - 1;
-  const int iw0 = i_wg0 + wave * 32;
+  const int i_wg0 = w.qtile * (kPBM >> hshift);
+  const int i_wg1 = min(p.nq, i_wg0 + (kPBM >> hshift)) - 1;
+  const int iw0 = i_wg0 + wave_r * 32;
   const int iw1 = min(p.nq - 1, iw0 + 31);
   const bool wave_rows = iw0 < p.nq;
   const int i = iw0 + c32;
@@ -475,8 +483,11 @@ __global__ void __launch_bounds__(256) pack_v_kernel(const short *__restrict__ v
 
 template <int D, bool BF16, bool EXACT>
 hipError_t launch_packed(const BatchParams &p, hipStream_t s) {
-  const int ntq = (p.nq + kPBM - 1) / kPBM;
-  const int64_t nwg = (int64_t)ntq * p.nz * p.B * p.Hq;
+  const int hpg = p.Hq / p.Hkv;
+  const int hshift = (hpg == 2 || hpg == 4 || hpg == 8) ? (hpg == 2 ? 1 : hpg == 4 ? 2 : 3) : 0;
+  const int rows = kPBM >> hshift;
+  const int ntq = (p.nq + rows - 1) / rows;
+  const int64_t nwg = (int64_t)ntq * p.nz * p.B * p.Hkv * (hshift ? 1 : hpg);
   const size_t lds = (size_t)2 * kPBN * D * 2 + (size_t)3 * D * kPBN * 2;
   // more than 64 KB of LDS per workgroup must be opted into, once per process
   // (a function-local static: initialised once even with several host threads)
@@ -486,7 +497,7 @@ hipError_t launch_packed(const BatchParams &p, hipStream_t s) {
                   : hipSuccess;
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((attn_packed_kernel<D, BF16, EXACT>), dim3((unsigned)nwg), dim3(512), lds, s,
-                     p, ntq);
+                     p, ntq, hshift);
   return hipGetLastError();
 }
 
