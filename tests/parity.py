@@ -8,6 +8,9 @@ import numpy as np
 O_MAX_ABS = 2e-2
 O_MEAN_ABS = 2e-3
 LSE_MAX_ABS = 1e-3
+# Gradient identities over all keys (full-size backward test): the 16-bit roundings move a sum
+# by about 2^-9 of the norm it is measured against per stage; the bound is ~25 times that.
+BWD_SUM_REL = 5e-2
 
 
 def torch_dtype(name):
@@ -77,3 +80,53 @@ def sample_tokens(fwd, n, rank0, n_ranks, count, seed):
         if take:
             picks.extend(rng.choice(pool, size=take, replace=False).tolist())
     return sorted(special), np.asarray(picks, np.int64)
+
+
+def bwd_identity_errors(dq, dk, dv, o, q, k, v, dout, group):
+    """Two identities of the attention gradients over every row and key, per (batch, K/V head)
+    of grouped heads (query head h uses K/V head h // group):
+      sum_i <dq_i, q_i> = sum_j <dk_j, k_j>   (both are scale * sum_ij dS_ij <q_i, k_j>),
+      sum_j <dv_j, v_j> = sum_i <dO_i, O_i>   (each row's probabilities average its values),
+    i over the rows that took part (dq, dO, O zero elsewhere), j over all keys.  Each
+    difference is measured against the root sum of squares of the per-row and per-key terms.
+    dq, dk, dv, o: torch tensors (any device) [B][H][S][d]; q, k, v, dout: numpy arrays of the
+    same shapes.  Returns errors [B][Hkv][2] (the dq/dk identity, the dv/O identity)."""
+    import math
+    import torch
+
+    def dots(x, y):
+        yy = torch.from_numpy(np.ascontiguousarray(y)).to(x.device, torch.float64)
+        return (x.double() * yy).sum(-1)
+
+    B, Hkv = dk.shape[0], dk.shape[1]
+    out = np.zeros((B, Hkv, 2))
+    for b in range(B):
+        for g in range(Hkv):
+            heads = range(g * group, (g + 1) * group)
+            terms = [[dots(dq[b, h], q[b, h]) for h in heads], [dots(dk[b, g], k[b, g])],
+                     [dots(dv[b, g], v[b, g])], [dots(o[b, h], dout[b, h]) for h in heads]]
+            sums = [float(sum(t.sum() for t in ts)) for ts in terms]
+            rss = [math.sqrt(float(sum((t * t).sum() for t in ts))) for ts in terms]
+            out[b, g, 0] = abs(sums[0] - sums[1]) / max(rss[0] + rss[1], 1e-300)
+            out[b, g, 1] = abs(sums[2] - sums[3]) / max(rss[2] + rss[3], 1e-300)
+    return out
+
+
+def bwd_sum_errors(dk, dv, dout, rows, group):
+    """Two sums over all keys, per (batch, K/V head, d component): sum_j dv_j equals the sum of
+    dO over the rows that took part (each row's probabilities sum to one), and sum_j dk_j is zero
+    (each row's dS sums to zero, as D = sum_j P dP), each against the 2-norm over keys of that
+    component of the gradient.  dk, dv: torch tensors (any device) [B][Hkv][S][d]; dout: numpy
+    [B][Hq][S][d]; rows: boolean mask over S of the rows that took part.  Returns the largest
+    error over components, [B][Hkv][2] (the dv sum, the dk sum)."""
+    import torch
+    B, Hkv, _, d = dk.shape
+    want_dv = dout[:, :, rows].sum(2, dtype=np.float64).reshape(B, Hkv, group, d).sum(2)
+    sum_dv = dv.sum(2, dtype=torch.float64).cpu().numpy()
+    sum_dk = dk.sum(2, dtype=torch.float64).cpu().numpy()
+    nrm_dv = torch.linalg.vector_norm(dv, dim=2, dtype=torch.float64).cpu().numpy()
+    nrm_dk = torch.linalg.vector_norm(dk, dim=2, dtype=torch.float64).cpu().numpy()
+    out = np.zeros((B, Hkv, 2))
+    out[..., 0] = (np.abs(sum_dv - want_dv) / np.maximum(nrm_dv, 1e-300)).max(-1)
+    out[..., 1] = (np.abs(sum_dk) / np.maximum(nrm_dk, 1e-300)).max(-1)
+    return out

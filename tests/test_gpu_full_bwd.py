@@ -49,7 +49,7 @@ CASES = [
     (configs.GQA_128K, "striped", (5,), 1088, 96),
 ]
 
-SUM_REL = 5e-2  # of the 2-norm over keys, per (batch, K/V head, component)
+SUM_REL = parity.BWD_SUM_REL  # of the 2-norm over keys, per (batch, K/V head, component)
 
 
 def _dout(w):
@@ -163,50 +163,25 @@ def check_backward(w, layout, kv_heads, tail, n_rand, grads):
     # the dq kernel to the dk kernel and dv to the forward output on every key, not only the
     # tail.  Measured against the root sum of squares of the per-row / per-key terms: the
     # 16-bit roundings move each term by about 2^-9 of itself, independently.
-    def dots(gpu_rows, host_rows):
-        x = torch.from_numpy(np.ascontiguousarray(host_rows)).to(gpu_rows.device, torch.float64)
-        return (gpu_rows.double() * x).sum(-1)
-
-    worst = [0.0, 0.0]
-    for b in range(w.B):
-        for g in range(w.Hkv):
-            sums, rss = [0.0] * 4, [0.0] * 4
-            terms = [[dots(dq[b, h], q32[b, h]) for h in range(g * group, (g + 1) * group)],
-                     [dots(dk[b, g], k32[b, g])],
-                     [dots(dv[b, g], v32[b, g])],
-                     [dots(o[b, h], g32[b, h]) for h in range(g * group, (g + 1) * group)]]
-            for c, ts in enumerate(terms):
-                sums[c] = float(sum(t.sum() for t in ts))
-                rss[c] = math.sqrt(float(sum((t * t).sum() for t in ts)))
-            e_qk = abs(sums[0] - sums[1]) / (rss[0] + rss[1])
-            e_vo = abs(sums[2] - sums[3]) / (rss[2] + rss[3])
-            worst = [max(worst[0], e_qk), max(worst[1], e_vo)]
-            assert e_qk <= SUM_REL, "%s: sum <dq,q> vs sum <dk,k> off by %.3e (b %d, kv %d)" % (
-                tag, e_qk, b, g)
-            assert e_vo <= SUM_REL, "%s: sum <dv,v> vs sum <dO,O> off by %.3e (b %d, kv %d)" % (
-                tag, e_vo, b, g)
+    errs = parity.bwd_identity_errors(dq, dk, dv, o, q32, k32, v32, g32, group)
+    worst = errs.max(axis=(0, 1))
+    assert worst[0] <= SUM_REL, "%s: sum <dq,q> vs sum <dk,k> off by %.3e" % (tag, worst[0])
+    assert worst[1] <= SUM_REL, "%s: sum <dv,v> vs sum <dO,O> off by %.3e" % (tag, worst[1])
     print("%s: |sum<dq,q> - sum<dk,k>| %.3e, |sum<dv,v> - sum<dO,O>| %.3e (of the root sum of "
           "squares of the terms)" % (tag, worst[0], worst[1]), flush=True)
     del q32, o
     data.clear()
 
-    # --- identities over all keys, per (batch, K/V head, component)
+    # --- sums over all keys, per (batch, K/V head, component)
     mask = np.zeros(w.S, bool)
     mask[owned] = True
-    g_own = g32[:, :, mask].astype(np.float64)
-    want_dv = g_own.sum(2).reshape(w.B, w.Hkv, group, w.d).sum(2)
-    del g_own, g32
-    sum_dv = dv.sum(2, dtype=torch.float64).cpu().numpy()
-    sum_dk = dk.sum(2, dtype=torch.float64).cpu().numpy()
-    nrm_dv = torch.linalg.vector_norm(dv, dim=2, dtype=torch.float64).cpu().numpy()
-    nrm_dk = torch.linalg.vector_norm(dk, dim=2, dtype=torch.float64).cpu().numpy()
-    e_dv = np.abs(sum_dv - want_dv) / nrm_dv
-    e_dk = np.abs(sum_dk) / nrm_dk
-    print("%s: |sum dv - sum dO| %.3e, |sum dk| %.3e (of the 2-norm over keys); "
-          "|sum dO| / norm %.1f" % (tag, e_dv.max(), e_dk.max(),
-                                    float(np.median(np.abs(want_dv) / nrm_dv))), flush=True)
-    assert e_dv.max() <= SUM_REL, "%s: sum_j dv_j off by %.3e" % (tag, e_dv.max())
-    assert e_dk.max() <= SUM_REL, "%s: sum_j dk_j off by %.3e" % (tag, e_dk.max())
+    errs = parity.bwd_sum_errors(dk, dv, g32, mask, group)
+    del g32
+    e_dv, e_dk = errs[..., 0].max(), errs[..., 1].max()
+    print("%s: |sum dv - sum dO| %.3e, |sum dk| %.3e (of the 2-norm over keys)" % (
+        tag, e_dv, e_dk), flush=True)
+    assert e_dv <= SUM_REL, "%s: sum_j dv_j off by %.3e" % (tag, e_dv)
+    assert e_dk <= SUM_REL, "%s: sum_j dk_j off by %.3e" % (tag, e_dk)
     del dq, dk, dv
     gc.collect()
     torch.cuda.empty_cache()
