@@ -235,31 +235,40 @@ def step_parts_bench(torch, rb, ra, w, q, k, v, o, lse, iters=10):
     return parts
 
 
-def overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse, ra_copy,
+def overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse, ra_main,
                   pairs=5):
-    """How much of the K/V hand-off the compute hides: steps with the hand-off
-    (COPY) and with the blocks read in place (SWAP, no transfer) alternate, so
-    clock drift falls on both alike, and the hop copies alone (the library's
-    hand-off copy of the hand-off bytes, once per hop, on one stream).
-    overlap = 1 - median(step_copy - step_swap) / copies alone."""
-    ra = RingAttention(w.B, w.Hq, w.Hkv, w.S, w.d, w.R, layout, tdt, w.causal, w.scale,
-                       rank0=w.rank0, n_ranks=w.ranks, handoff=rb.HANDOFF_SWAP,
-                       merge_mode=ra_copy.merge_mode)
-    ra.run(q, k, v, o, lse)
-    ra_copy.run(q, k, v, o, lse)
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(4 * pairs)]
+    """How much of the K/V hand-off the compute hides.  Steps with the hand-off
+    (the run's mode: FORWARD -- blocks written on by the block kernel, side
+    copies only for blocks entering from ranks that are not computed -- or
+    COPY; with FORWARD also COPY) and with the blocks read in place (SWAP, no
+    transfer) alternate, so clock drift falls on all alike; the hop copies
+    alone are the library's hand-off copy of the hand-off bytes, once per hop,
+    on one stream.  overlap = 1 - median(step_mode - step_swap) / copies alone."""
+    runs = {"swap": RingAttention(w.B, w.Hq, w.Hkv, w.S, w.d, w.R, layout, tdt, w.causal,
+                                  w.scale, rank0=w.rank0, n_ranks=w.ranks,
+                                  handoff=rb.HANDOFF_SWAP, merge_mode=ra_main.merge_mode)}
+    main_mode = "forward" if ra_main.handoff == rb.HANDOFF_FORWARD else "copy"
+    runs[main_mode] = ra_main
+    if main_mode == "forward":
+        runs["copy"] = RingAttention(w.B, w.Hq, w.Hkv, w.S, w.d, w.R, layout, tdt, w.causal,
+                                     w.scale, rank0=w.rank0, n_ranks=w.ranks,
+                                     handoff=rb.HANDOFF_COPY, merge_mode=ra_main.merge_mode)
+    names = list(runs)
+    for r in runs.values():
+        r.run(q, k, v, o, lse)
+    e = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * pairs)] for _ in names]
     torch.cuda.synchronize()
     for s in range(pairs):
-        for j, r in enumerate((ra_copy, ra)):
-            e[4 * s + 2 * j].record()
-            r.run(q, k, v, o, lse)
-            e[4 * s + 2 * j + 1].record()
+        for j, nm in enumerate(names):
+            e[j][2 * s].record()
+            runs[nm].run(q, k, v, o, lse)
+            e[j][2 * s + 1].record()
     torch.cuda.synchronize()
-    t_c = np.array([e[4 * s].elapsed_time(e[4 * s + 1]) for s in range(pairs)])
-    t_s = np.array([e[4 * s + 2].elapsed_time(e[4 * s + 3]) for s in range(pairs)])
-    t_copy_ms, t_swap = float(np.median(t_c)), float(np.median(t_s))
-    t_diff = float(np.median(t_c - t_s))
-    del ra
+    t = {nm: np.array([e[j][2 * s].elapsed_time(e[j][2 * s + 1]) for s in range(pairs)])
+         for j, nm in enumerate(names)}
+    for nm in names:
+        if nm != main_mode:
+            del runs[nm]
     elt = 4 if w.dtype == "fp32" else 2
     k_bytes = w.ranks * w.B * w.Hkv * w.n * w.d * elt
     v_bytes = (w.ranks * w.B * w.Hkv * w.d * ((w.n + 63) // 64 * 64) * elt
@@ -281,10 +290,17 @@ def overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse, ra_
     t_copies = c0.elapsed_time(c1)
     del src, dst
     moved = 2.0 * per_hop * (w.R - 1)  # read + write
-    return {"step_ms_copy": round(t_copy_ms, 3), "step_ms_swap": round(t_swap, 3),
-            "copies_alone_ms": round(t_copies, 3), "copy_form": "thin" if thin else "wide",
-            "bytes_per_hop": per_hop, "copy_GB/s": round(moved / (t_copies * 1e-3) / 1e9, 1),
-            "overlap": round(1.0 - t_diff / t_copies, 3) if t_copies > 0 else None}
+    out = {"mode": main_mode}
+    for nm in names:
+        out["step_ms_" + nm] = round(float(np.median(t[nm])), 3)
+    out.update({"copies_alone_ms": round(t_copies, 3), "copy_form": "thin" if thin else "wide",
+                "bytes_per_hop": per_hop,
+                "copy_GB/s": round(moved / (t_copies * 1e-3) / 1e9, 1)})
+    for nm in names:
+        if nm != "swap" and t_copies > 0:
+            key = "overlap" if nm == main_mode else "overlap_" + nm
+            out[key] = round(1.0 - float(np.median(t[nm] - t["swap"])) / t_copies, 3)
+    return out
 
 
 def backward_bench(torch, ra, w, layout_code, q, k, v, iters=3):
@@ -319,7 +335,7 @@ def backward_bench(torch, ra, w, layout_code, q, k, v, iters=3):
     handoff0 = ra.bargs.handoff
     rb_ring_bwd(ra)
     handoff = None
-    if handoff0 == rb.HANDOFF_COPY and w.R > 1:
+    if handoff0 != rb.HANDOFF_SWAP and w.R > 1:  # FORWARD moves like COPY in the backward
         # passes with the hand-off and with the blocks in place alternate
         t = timed([handoff0, rb.HANDOFF_SWAP] * iters)
         ms, ms_swap = t[0::2], t[1::2]
@@ -536,7 +552,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=None, help="workload name (default: 1M-token share)")
     ap.add_argument("--layout", default=None)
-    ap.add_argument("--handoff", default="copy", choices=["copy", "swap"])
+    ap.add_argument("--handoff", default="forward", choices=["forward", "copy", "swap"])
     ap.add_argument("--merge", default="fused", choices=["fused", "separate"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -599,7 +615,8 @@ def main():
     lse = torch.zeros((w.B, w.Hq, w.S), dtype=torch.float32, device="cuda")
     ra = RingAttention(w.B, w.Hq, w.Hkv, w.S, w.d, w.R, layout, tdt, w.causal, w.scale,
                        rank0=w.rank0, n_ranks=w.ranks,
-                       handoff=rb.HANDOFF_COPY if args.handoff == "copy" else rb.HANDOFF_SWAP,
+                       handoff={"forward": rb.HANDOFF_FORWARD, "copy": rb.HANDOFF_COPY,
+                                "swap": rb.HANDOFF_SWAP}[args.handoff],
                        merge_mode=rb.MERGE_FUSED if args.merge == "fused" else rb.MERGE_SEPARATE)
     log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
@@ -643,7 +660,7 @@ def main():
     log("step %.2f ms, %.1f TFLOP/s; block kernel %.1f TFLOP/s" % (ms_per_step, value, achieved))
 
     handoff = None
-    if args.handoff == "copy" and w.R > 1 and not args.no_overlap_bench:
+    if args.handoff != "swap" and w.R > 1 and not args.no_overlap_bench:
         handoff = overlap_bench(torch, rb, RingAttention, w, layout, tdt, q, k, v, o, lse, ra)
     merge = None if args.no_merge_bench else merge_bench(torch, rb)
     parts = None

@@ -65,8 +65,17 @@ typedef enum { RA_LAYOUT_CONTIGUOUS = 0, RA_LAYOUT_STRIPED = 1, RA_LAYOUT_ZIGZAG
 typedef enum { RA_DT_BF16 = 0, RA_DT_FP16 = 1, RA_DT_FP32 = 2 } ra_dtype;
 /* How the next K/V block reaches a rank. COPY: an on-device copy on the copy
  * stream into the rank's receive buffer (the emulated link); SWAP: the rank
- * reads the resident block in place (no transfer; an upper bound). */
-typedef enum { RA_HANDOFF_COPY = 0, RA_HANDOFF_SWAP = 1 } ra_handoff;
+ * reads the resident block in place (no transfer; an upper bound); FORWARD:
+ * as COPY, but on hops too short for the copy to hide beside the block kernel
+ * (ra_handoff_thin returns 0: the copy would compete with the kernel for
+ * memory), a block whose next holder is a computed rank is written to that
+ * rank's receive buffer by the block kernel itself, from the tiles it loads
+ * while it computes (each workgroup writes its share; no copy kernel and no
+ * second stream for those blocks -- in a ring over several GPUs these would be
+ * stores into the peer's buffer).  Long hops, blocks entering from ranks that
+ * are not computed, and the fp32 path are copied as in COPY; ra_ring_bwd
+ * treats FORWARD as COPY.  All three give bitwise equal results. */
+typedef enum { RA_HANDOFF_COPY = 0, RA_HANDOFF_SWAP = 1, RA_HANDOFF_FORWARD = 2 } ra_handoff;
 /* How each hop's partial is folded. FUSED: the block kernel continues the
  * running online softmax from the accumulator; SEPARATE: ra_block_fwd writes
  * the hop's partial and ra_merge folds it in. */
@@ -260,6 +269,12 @@ ra_status ra_finalize(const float *o_acc, const float *m, const float *l, void *
  * `copy` stream, with the block its ring predecessor holds at hop h, while
  * the `compute` stream runs hop h; events order the two streams (no
  * write-after-read on the double buffer).  SWAP reads blocks in place.
+ * FORWARD (16-bit dtypes, hops too short for the thin copy): hop h's block
+ * kernel writes the block of computed rank r to the receive buffer of
+ * computed rank r+1 (on a full ring, rank rank0+n_ranks-1's to rank0) as it
+ * streams it; only blocks whose sender is not computed go through the copy
+ * stream (none when n_ranks = R).  Hop h+1 reads the buffer hop h wrote and
+ * hop h-1 read, on the same stream.  On other hops FORWARD is COPY.
  * The copy stream first waits for work already on the compute stream; the
  * compute stream waits for the copy stream before the call's last kernel,
  * so everything is complete when `compute` is.  Passing the same stream
@@ -267,8 +282,8 @@ ra_status ra_finalize(const float *o_acc, const float *m, const float *l, void *
  * The workspace (device, ra_ring_fwd_workspace_size bytes, 256-byte
  * aligned) holds the packed V blocks (16-bit dtypes; see ra_pack_v), the
  * two receive buffers and the fp32 running state.
- * COPY and SWAP give bitwise-identical outputs; FUSED and SEPARATE agree to
- * rounding.
+ * COPY, SWAP and FORWARD give bitwise-identical outputs; FUSED and SEPARATE
+ * agree to rounding.
  * Errors: RA_ERR_INVALID_ARG, RA_ERR_SHAPE, RA_ERR_DTYPE, RA_ERR_ALIGNMENT,
  * RA_ERR_WORKSPACE, RA_ERR_HIP.
  */
@@ -351,6 +366,7 @@ ra_status ra_block_bwd(const ra_block_bwd_args *a, void *workspace, size_t works
  *     while hop h+1's dQ kernel runs); a block leaving the computed ranks
  *     (or the ring's end) puts its accumulators back home.  SWAP reads and
  *     accumulates every block in place.  Both give bitwise-identical results.
+ *     FORWARD is handled as COPY here.
  *     Stream ordering as in ra_ring_fwd (same stream twice is allowed).
  *   o_sh, dout_sh  device [n_ranks][B][Hq][n][d]: the forward's O and the
  *                  upstream gradient of the computed ranks

@@ -20,7 +20,7 @@ STATUS_NAMES = {0: "RA_OK", 1: "RA_ERR_INVALID_ARG", 2: "RA_ERR_SHAPE", 3: "RA_E
                 7: "RA_ERR_HIP"}
 LAYOUT_CONTIGUOUS, LAYOUT_STRIPED, LAYOUT_ZIGZAG = 0, 1, 2
 DT_BF16, DT_FP16, DT_FP32 = 0, 1, 2
-HANDOFF_COPY, HANDOFF_SWAP = 0, 1
+HANDOFF_COPY, HANDOFF_SWAP, HANDOFF_FORWARD = 0, 1, 2
 MERGE_FUSED, MERGE_SEPARATE = 0, 1
 
 LAYOUTS = {"contiguous": LAYOUT_CONTIGUOUS, "striped": LAYOUT_STRIPED, "zigzag": LAYOUT_ZIGZAG}

@@ -194,7 +194,7 @@ WsLayout ws_layout(const ra_ring_args *a) {
     return at;
   };
   if (ring_packs_v(a)) w.vpack = take((size_t)a->R * blkv * elt);
-  if (a->handoff == RA_HANDOFF_COPY && a->R > 1) {
+  if (a->handoff != RA_HANDOFF_SWAP && a->R > 1) {
     w.kbuf[0] = take(k_bytes);
     w.kbuf[1] = take(k_bytes);
     w.vbuf[0] = take(v_bytes);
@@ -281,7 +281,8 @@ ra_status check_ring_bwd(const ra_ring_bwd_args *a) {
     return fail(RA_ERR_DTYPE, "unknown dtype %d", a->dtype);
   }
   if (!known_layout(a->layout)) return fail(RA_ERR_INVALID_ARG, "unknown layout %d", a->layout);
-  if (a->handoff != RA_HANDOFF_COPY && a->handoff != RA_HANDOFF_SWAP)
+  if (a->handoff != RA_HANDOFF_COPY && a->handoff != RA_HANDOFF_SWAP &&
+      a->handoff != RA_HANDOFF_FORWARD)
     return fail(RA_ERR_INVALID_ARG, "unknown handoff %d", a->handoff);
   if (a->R < 1) return fail(RA_ERR_SHAPE, "R must be >= 1 (got %d)", a->R);
   if (a->n_ranks < 1 || a->n_ranks > a->R || a->rank0 < 0 || a->rank0 + a->n_ranks > a->R)
@@ -334,7 +335,7 @@ RingBwdWs ring_bwd_ws(const ra_ring_bwd_args *a) {
   w.dq = take(qrows * a->n * a->d * 4);
   w.dk = take(kblocks * a->n * a->d * 4);
   w.dv = take(kblocks * a->n * a->d * 4);
-  if (a->handoff == RA_HANDOFF_COPY && a->R > 1) {
+  if (a->handoff != RA_HANDOFF_SWAP && a->R > 1) {
     const size_t rblocks = (size_t)a->n_ranks * a->B * a->Hkv;
     for (int b = 0; b < 2; ++b) {
       w.kbuf[b] = take(rblocks * a->n * a->d * 2);
@@ -440,7 +441,8 @@ ra_status check_ring(const ra_ring_args *a) {
   if (!a) return fail(RA_ERR_INVALID_ARG, "args is NULL");
   if (!elt_bytes(a->dtype)) return fail(RA_ERR_DTYPE, "unknown dtype %d", a->dtype);
   if (!known_layout(a->layout)) return fail(RA_ERR_INVALID_ARG, "unknown layout %d", a->layout);
-  if (a->handoff != RA_HANDOFF_COPY && a->handoff != RA_HANDOFF_SWAP)
+  if (a->handoff != RA_HANDOFF_COPY && a->handoff != RA_HANDOFF_SWAP &&
+      a->handoff != RA_HANDOFF_FORWARD)
     return fail(RA_ERR_INVALID_ARG, "unknown handoff %d", a->handoff);
   if (a->merge_mode != RA_MERGE_FUSED && a->merge_mode != RA_MERGE_SEPARATE)
     return fail(RA_ERR_INVALID_ARG, "unknown merge_mode %d", a->merge_mode);
@@ -751,7 +753,6 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
   char *ws = (char *)workspace;
   const int R = a->R, n = a->n, nr = a->n_ranks, r0 = a->rank0;
   const bool contig = a->layout == RA_LAYOUT_CONTIGUOUS;
-  const bool copy = a->handoff == RA_HANDOFF_COPY && R > 1;
   const int elt = elt_bytes(a->dtype);
   const int64_t blk = (int64_t)a->B * a->Hkv * n * a->d;  // elements of one K block
   const size_t blk_bytes = (size_t)blk * elt;
@@ -759,6 +760,24 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
   const int64_t n_pad = packed ? packed_n(n) : n;
   const int64_t blkv = (int64_t)a->B * a->Hkv * a->d * n_pad;  // elements of one V block
   const size_t blkv_bytes = (size_t)blkv * elt;
+  // The side copy's form: thin where the hop's products outlast its bytes
+  // (it runs beside the block kernel), else the 64-workgroup copy.
+  const bool thin = thin_handoff(2.0 * (double)nr * (blk_bytes + blkv_bytes),
+                                 (double)nr * a->B * a->Hq * (double)n * n *
+                                     (a->causal ? 0.5 : 1.0),
+                                 a->d, 1.0);
+  // moving: blocks travel through the receive buffers (COPY, FORWARD).  In
+  // FORWARD mode, on the packed path and on hops too short for the thin copy
+  // to hide (the side copy would compete with the block kernel for memory),
+  // the block kernel writes each block whose next holder is a computed rank
+  // itself; side copies carry the rest (blocks entering from ranks that are
+  // not computed; none on a full ring).  On long hops FORWARD copies as COPY:
+  // the thin copy costs the kernel nothing there, and the forwarding
+  // instantiation of the d = 128 kernel measured 4 % slower per launch than
+  // the plain one (compiler scheduling of its tile loop), more than the copy.
+  const bool moving = a->handoff != RA_HANDOFF_SWAP && R > 1;
+  const bool in_kernel = moving && a->handoff == RA_HANDOFF_FORWARD && packed && !thin;
+  const bool copy = moving && !(in_kernel && nr == R);
   const int64_t qz = (int64_t)a->B * a->Hq * n * a->d;
   const int64_t rows = (int64_t)nr * a->B * a->Hq * n;
   float *o_acc = (float *)(ws + L.o_acc), *m_acc = (float *)(ws + L.m_acc),
@@ -841,21 +860,17 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
   p.ml_zstride = (int64_t)a->B * a->Hq * n;
 
   const DebugDelay dbg = debug_delay();
-  const bool thin = thin_handoff(2.0 * (double)nr * (blk_bytes + blkv_bytes),
-                                 (double)nr * a->B * a->Hq * (double)n * n *
-                                     (a->causal ? 0.5 : 1.0),
-                                 a->d, 1.0);
   for (int h = 0; h < R; ++h) {
     // ---- compute hop h: every computed rank r attends to the block of source (r - h) mod R
     if (copy && h > 0) RA_HIP(hipStreamWaitEvent(cs, ev_copy(h - 1), 0), "hipStreamWaitEvent");
     RA_HIP(launch_delay(dbg.compute, cs), "delay kernel");
     p.kg_s0 = ((r0 - h) % R + R) % R;
-    if (copy && h > 0) {
+    if (moving && h > 0) {
       p.k = kb[(h - 1) & 1];
       p.v = vb[(h - 1) & 1];
       p.kv_idx0 = 0;
       p.kv_idx_mod = nr;
-    } else if (copy) {
+    } else if (moving) {
       p.k = ksh;
       p.v = vsh;
       p.kv_idx0 = r0;
@@ -873,6 +888,13 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
     p.accumulate = (a->merge_mode == RA_MERGE_FUSED && h > 0) ? 1 : 0;
     // the fused state only needs m + ln l; a separate partial is merged by m
     p.exact_m = a->merge_mode == RA_MERGE_FUSED ? 0 : 1;
+    // FORWARD: computed rank k hands its block to computed rank k + 1 (on a
+    // full ring the last one to rank 0) through buffer h & 1, which hop h+1
+    // reads and hop h-1 was the last to read (same stream)
+    p.fwd = (in_kernel && h + 1 < R) ? 1 : 0;
+    p.fk = kb[h & 1];
+    p.fv = vb[h & 1];
+    p.fwd_wrap = nr == R ? 1 : 0;
     if (a->hop_events)
       RA_HIP(hipEventRecord((hipEvent_t)a->hop_events[2 * h], cs), "hipEventRecord");
     RA_HIP(launch_block_fwd(p, a->dtype, cs), "block kernel");
@@ -900,6 +922,7 @@ ra_status ra_ring_fwd(const ra_ring_args *a, void *workspace, size_t workspace_b
         const int r = r0 + k;
         const int rp = (r - 1 + R) % R;
         const int kp = ((rp - r0) % R + R) % R;
+        if (in_kernel && kp < nr) continue;  // written by the block kernel of rank kp
         const char *src = kp < nr ? front(sh, buf, bb, h, kp)
                                   : sh + (size_t)(((r - 1 - h) % R + R) % R) * bb;
         char *dst = dst_base + (size_t)k * bb;
@@ -1012,7 +1035,7 @@ ra_status ra_ring_bwd(const ra_ring_bwd_args *a, void *workspace, size_t workspa
   hipStream_t s = (hipStream_t)compute_s, xs = (hipStream_t)copy_s;
   char *ws = (char *)workspace;
   const int R = a->R, n = a->n, nr = a->n_ranks, r0 = a->rank0;
-  const bool copy = a->handoff == RA_HANDOFF_COPY && R > 1;
+  const bool copy = a->handoff != RA_HANDOFF_SWAP && R > 1;  // FORWARD moves like COPY here
   const int64_t d = a->d;
   const bool contig = a->layout == RA_LAYOUT_CONTIGUOUS;
   const int64_t qz = (int64_t)a->B * a->Hq * n * d;   // elements of one query shard

@@ -31,6 +31,12 @@
 //    all query heads of its K/V head from each loaded tile, 256 / group rows of
 //    each (same-run: as fast as one head per workgroup -- each tile already
 //    serves 256 rows, and the heads' workgroups ran together on one XCD).
+//  * At d = 64 in the fused ring a lean variant (attn_lean64_kernel) trades the
+//    in-wave pipelining for registers, so two workgroups share a CU.
+//  * Forwarding instantiations (the ring's FORWARD hand-off on short hops)
+//    also write the K/V block they stream to the next rank's receive buffer
+//    (the highthink.cn Ring Attention article, "Zig Zag Ring Attention
+//    通信和计算重叠": a rank passes on the block it holds while it computes).
 #include <cfloat>
 #include <cmath>
 #include <type_traits>
@@ -69,7 +75,24 @@ __device__ __forceinline__ int chunk_swz(int row) {
 constexpr int kBufWord3 = 0x00020000;
 // s_waitcnt immediate waiting for vmcnt == 0 only (lgkmcnt, expcnt at max)
 constexpr int kWaitVm0 = 0x0F70;
+// cache policy of the forwarded tiles' stores (and direct loads): non-temporal, so
+// they do not evict the K/V tiles the workgroups running beside reuse from L2
+constexpr int kNT = 2;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes per lane
+
+// Workgroup barrier for the tile loop of the forwarding kernels: global
+// stores issued before it (the forwarded K/V tiles) stay in flight across it.
+// A memory fence would wait for them too (it cannot tell them from the loads
+// into LDS, which count on the same counter), so the ordering is explicit:
+// each loading wave has waited for its own loads into LDS before it arrives,
+// and every wave's LDS reads are complete (lgkmcnt 0); the asm statement
+// keeps the compiler from moving memory operations across the barrier.
+constexpr int kWaitLgkm0 = 0xC07F;  // s_waitcnt lgkmcnt(0) only
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  asm volatile("s_barrier" ::: "memory");
+}
 
 // 16 bytes per lane from a raw buffer straight into LDS: lane l's bytes land
 // at dst + 16 l (dst is wave-uniform; it goes to M0).  A plain device function:
@@ -87,7 +110,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, lds_void *dst
 // taken against the running maximum without a per-tile row max, and a tile
 // whose probabilities would exceed 2^kTau (a larger maximum arrived) is redone
 // after rescaling.
-template <int D, bool BF16, bool EXACT>
+template <int D, bool BF16, bool EXACT, bool FWD>
 __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq, int hshift) {
   using M = Mfma16<BF16>;
   constexpr int KS = D / 16;             // k-steps of the QK product
@@ -137,8 +160,22 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
   const int ntiles_w = (kv_wl + kPBN - 1) / kPBN;
   const int nfull_w = kv_wf / kPBN;
   const int jlim = key_prefix(p, kid, qid(i));
-
-  if (ntiles == 0 && p.accumulate) return;  // nothing to add to the running state
+  // FWD: this workgroup's share [f0, f1) of the block's 64-key tiles, written
+  // to the next rank's receive buffer (tiles split over the query tiles; one
+  // head of the group when heads are work items of their own)
+  int f0 = 0, f1 = 0;
+  const short *fkp = nullptr, *fvp = nullptr;
+  if (FWD) {
+    const int dz = w.z + 1 < p.nz ? w.z + 1 : (p.fwd_wrap ? 0 : -1);
+    if (dz >= 0 && (hshift || w.h == w.kvh * (p.Hq / p.Hkv))) {
+      const int64_t ntk = (p.nk + kPBN - 1) / kPBN;
+      f0 = (int)(w.qtile * ntk / ntq);
+      f1 = (int)((w.qtile + 1) * ntk / ntq);
+      fkp = (const short *)p.fk + dz * p.kv_zstride + w.b * p.ks_b + w.kvh * p.ks_h;
+      fvp = (const short *)p.fv + dz * p.kv_vzstride + w.b * p.vs_b + w.kvh * p.vs_h;
+    }
+  }
+  if (!FWD && ntiles == 0 && p.accumulate) return;  // nothing to add to the running state
 
   f32x16 O[DT];
   float m_run, m_top, lsum;
@@ -156,44 +193,117 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
     }
   };
 
-  if (ntiles > 0) {
-    // Tile loads go through buffer descriptors: the per-lane byte offsets are
-    // fixed, the tile moves the (scalar) base, and K rows past the end of the
-    // block read as zero (they are masked).  Offsets fit in 32 bits: the host
-    // bounds the K row stride and the packed V row length.
-    // Only waves 0 .. kLW-1 (one per SIMD; in the fused ring the ones that
-    // start a tile with QK and exponentials) issue the loads: a direct-to-LDS
-    // load holds its wave at issue for a long time, and these waves absorb
-    // that best (2 % faster than all eight loading, 1 % faster than the other
-    // four, in same-run comparisons).
-    const bool loader = wave < kLW;
-    const uint32_t krow_b = (uint32_t)p.ks_t * 2;
-    uint32_t kvo[KPW];
+  // Tile loads go through buffer descriptors: the per-lane byte offsets are
+  // fixed, the tile moves the (scalar) base, and K rows past the end of the
+  // block read as zero (they are masked).  Offsets fit in 32 bits: the host
+  // bounds the K row stride and the packed V row length.
+  // Only waves 0 .. kLW-1 (one per SIMD; in the fused ring the ones that
+  // start a tile with QK and exponentials) issue the loads: a direct-to-LDS
+  // load holds its wave at issue for a long time, and these waves absorb
+  // that best (2 % faster than all eight loading, 1 % faster than the other
+  // four, in same-run comparisons).
+  const bool loader = wave < kLW;
+  const uint32_t krow_b = (uint32_t)p.ks_t * 2;
+  uint32_t kvo[KPW];
+#pragma unroll
+  for (int u = 0; u < KPW; ++u) {
+    const int idx = (loader ? wave : 0) + kLW * u;
+    const int row = idx * KRPI + lane / CPR;
+    const int ch = (lane % CPR) ^ chunk_swz<KROW>(row);
+    kvo[u] = row * krow_b + ch * 16;
+  }
+  uint32_t vvo[VPW];
+#pragma unroll
+  for (int u = 0; u < VPW; ++u) {
+    const int idx = (loader ? wave : 0) + kLW * u;
+    const int dr = idx * 8 + (lane >> 3);
+    vvo[u] = dr * VROW + (((lane & 7) ^ chunk_swz<VROW>(dr)) * 16);  // within a V^T tile
+  }
+  // the (b, h) slice of packed V: vs_t = n_pad, tiles of VTILE bytes
+  const uint32_t vslice_b = (uint32_t)D * (uint32_t)p.vs_t * 2u;
+  const auto vrsrc = __builtin_amdgcn_make_buffer_rsrc((void *)vp, 0, (int)vslice_b, kBufWord3);
+  auto k_rsrc = [&](const short *base, int tk) {  // K tile tk: its rows only
+    const int rows = min(p.nk - tk * kPBN, kPBN);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(base + (int64_t)tk * kPBN * p.ks_t), 0,
+                                             (int)(rows * krow_b), kBufWord3);
+  };
+  // FWD: a loading wave writes out what it loaded, from the LDS it landed in,
+  // at the same per-lane offsets (rows past the block end are dropped by the
+  // descriptor's range check).  The stores go out after the wave's tile loads
+  // of the same iteration; memory operations count down in issue order, so
+  // the end-of-tile wait for the loads leaves the stores in flight.  Returns
+  // the number of stores issued.
+  auto fwd_k = [&](int tk, int kstage) {
+    if (!FWD || !loader || tk < f0 || tk >= f1) return 0;
+    const auto dst = k_rsrc(fkp, tk);
 #pragma unroll
     for (int u = 0; u < KPW; ++u) {
-      const int idx = (loader ? wave : 0) + kLW * u;
-      const int row = idx * KRPI + lane / CPR;
-      const int ch = (lane % CPR) ^ chunk_swz<KROW>(row);
-      kvo[u] = row * krow_b + ch * 16;
+      const u32x4 x =
+          *(const u32x4 *)(lds + kstage * KTILE + kLW * 1024 * u + wave * 1024 + 16 * lane);
+      __builtin_amdgcn_raw_buffer_store_b128(x, dst, kvo[u], 0, kNT);
     }
-    uint32_t vvo[VPW];
+    return KPW;
+  };
+  auto fwd_v = [&](int tv, int vso) {  // vso: byte offset of the V^T stage
+    if (!FWD || !loader || tv < f0 || tv >= f1) return 0;
+    const auto dst = __builtin_amdgcn_make_buffer_rsrc((void *)fvp, 0, (int)vslice_b, kBufWord3);
 #pragma unroll
     for (int u = 0; u < VPW; ++u) {
-      const int idx = (loader ? wave : 0) + kLW * u;
-      const int dr = idx * 8 + (lane >> 3);
-      vvo[u] = dr * VROW + (((lane & 7) ^ chunk_swz<VROW>(dr)) * 16);  // within a V^T tile
+      const u32x4 x =
+          *(const u32x4 *)(lds + VBASE + vso + kLW * 1024 * u + wave * 1024 + 16 * lane);
+      __builtin_amdgcn_raw_buffer_store_b128(x, dst, vvo[u], tv * VTILE, kNT);
     }
-    // the (b, h) slice of packed V: vs_t = n_pad, tiles of VTILE bytes
-    const auto vrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)vp, 0, (int)((uint32_t)D * (uint32_t)p.vs_t * 2u), kBufWord3);
+    return VPW;
+  };
+  static_assert(KPW == VPW, "the waits below take 0, KPW or 2 KPW stores");
+  auto wait_loads = [&](int stores) {  // this wave's loads have landed
+    if (stores == 0)
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    else if (stores == KPW)
+      __builtin_amdgcn_s_waitcnt(kWaitVm0 | KPW);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm0 | (2 * KPW));
+  };
+  // tiles [max(f0, t0), f1), which this workgroup does not stream: global to
+  // global through registers, each tile's 1 KB pieces spread over the eight
+  // waves with all of a wave's loads in flight together
+  auto fwd_direct = [&](int t0) {
+    if (!FWD) return;
+    constexpr int KC = KTILE / 1024 / kPW, VC = VTILE / 1024 / kPW;
+    const auto vdst = __builtin_amdgcn_make_buffer_rsrc((void *)fvp, 0, (int)vslice_b, kBufWord3);
+    for (int t = max(f0, t0); t < f1; ++t) {
+      const auto ksrc = k_rsrc(kp, t), kdst = k_rsrc(fkp, t);
+      u32x4 xk[KC], xv[VC];
+      uint32_t ko[KC];
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        ko[j] = ((wave + kPW * j) * KRPI + lane / CPR) * krow_b + (lane % CPR) * 16;
+        xk[j] = __builtin_amdgcn_raw_buffer_load_b128(ksrc, ko[j], 0, kNT);
+      }
+#pragma unroll
+      for (int j = 0; j < VC; ++j)
+        xv[j] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, (wave + kPW * j) * 1024 + 16 * lane,
+                                                      t * VTILE, kNT);
+#pragma unroll
+      for (int j = 0; j < KC; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(xk[j], kdst, ko[j], 0, kNT);
+#pragma unroll
+      for (int j = 0; j < VC; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(xv[j], vdst, (wave + kPW * j) * 1024 + 16 * lane,
+                                               t * VTILE, kNT);
+    }
+  };
+  if (FWD && ntiles == 0 && p.accumulate) {
+    fwd_direct(0);
+    return;
+  }
+  if (ntiles > 0) {
     // A loading wave's share of K tile tk / V^T tile tv goes straight into an LDS
     // stage (buffer loads with the LDS destination in M0: lane l's 16 bytes
     // land at base + 16 l, so the swizzle is applied on the source side).
     // Completion is awaited (vmcnt) before the barrier that publishes the stage.
     auto load_k = [&](int tk, int kstage) {
-      const int rows = min(p.nk - tk * kPBN, kPBN);
-      const auto krsrc = __builtin_amdgcn_make_buffer_rsrc(
-          (void *)(kp + (int64_t)tk * kPBN * p.ks_t), 0, (int)(rows * krow_b), kBufWord3);
+      const auto krsrc = k_rsrc(kp, tk);
       if (!loader) return;
 #pragma unroll
       for (int u = 0; u < KPW; ++u)
@@ -278,6 +388,7 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
     // Prologue: K tiles 0 and 1, V^T tile 0 resident; S^T of tile 0.
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
+    fwd_k(0, 0);
     f32x16 S[2], S1[2];
     float mx = -INFINITY;  // EXACT: row max of the next tile's S (before masking)
     if (0 < ntiles_w) {
@@ -337,12 +448,17 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
     auto tile = [&](auto par_c, const int t, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
       constexpr int PAR = decltype(par_c)::value;
       // also at t = 0: K stage 0 is read by the prologue's QK of tile 0
-      __syncthreads();
+      if constexpr (FWD)
+        lds_barrier();
+      else
+        __syncthreads();
       const int vcur = vst * VTILE;
       const int vnext = (vst == 2 ? 0 : vst + 1) * VTILE;
       const int vprev = (vst == 0 ? 2 : vst - 1) * VTILE;
       if (t + 2 < ntiles) load_k(t + 2, PAR);
       if (t + 1 < ntiles) load_v(t + 1, vnext);
+      int stores = t + 1 < ntiles ? fwd_k(t + 1, PAR ^ 1) : 0;
+      stores += fwd_v(t, vcur);
       if (lag && t >= 1 && t - 1 < ntiles_w) {
         const float m2 = pv(vprev, Sc);
         if (EXACT) mx = m2;
@@ -427,7 +543,7 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
           if (EXACT) mx = m2;
         }
       }
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's tile loads have landed
+      wait_loads(stores);  // this wave's tile loads have landed
       vst = vnext / VTILE;
     };
     // two tiles per iteration so the K stages are immediates and the S
@@ -439,10 +555,311 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
     }
     // the lagging waves' PV of the last tile (no stage is reloaded any more)
     if (lag && ntiles_w == ntiles) pv((vst == 0 ? 2 : vst - 1) * VTILE, S);
+    fwd_direct(ntiles);
   } else {
+    fwd_direct(0);
     init_state();
   }
   store_state<D>(p, w, i, valid, O, m_run, EXACT ? m_top : m_run, lsum);
+}
+
+
+// Lean variant for d = 64 in the fused ring (running maximum, no exact row
+// maximum).  At d = 64 a 64-key tile is 16 MFMAs against 32 exponentials per
+// wave, and a workgroup's key blocks are short (the 512-token shards: 8
+// tiles), so per-workgroup costs -- the running state in and out, the first
+// loads, the tile barrier -- weigh as much as the products.  This variant
+// gives up the in-wave pipelining (QK of the next tile under the exponentials
+// of this one, lagging waves) for registers: at <= 128 VGPRs two workgroups
+// share a CU, four waves per SIMD, and one workgroup's state traffic and
+// barrier waits run beside the other's products.  Same arithmetic in the same
+// order as attn_packed_kernel<64, *, false>; K and V^T tiles one tile ahead,
+// two stages each (32 KB of LDS).
+template <bool BF16, bool FWD>
+__global__ void __launch_bounds__(512, 4) attn_lean64_kernel(BatchParams p, int ntq, int hshift) {
+  using M = Mfma16<BF16>;
+  constexpr int D = 64;
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int KROW = D * 2;
+  constexpr int KTILE = kPBN * KROW;
+  constexpr int VROW = kPBN * 2;
+  constexpr int VTILE = D * VROW;
+  constexpr int VBASE = 2 * KTILE;  // LDS: K stages 0, 1, then V^T stages 0, 1
+  constexpr int KPW = KTILE / 1024 / kLW;
+  constexpr int VPW = VTILE / 1024 / kLW;
+  constexpr int KRPI = 1024 / KROW;
+  constexpr int CPR = D / 8;
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Work w = hshift ? decode_items(p, ntq, 1) : decode(p, ntq);
+  w.h += wave >> (3 - hshift);
+  const int wave_r = wave & ((kPW >> hshift) - 1);
+  const int lane = threadIdx.x & 63;
+  const int hl = lane >> 5, c32 = lane & 31;
+
+  const short *qp = (const short *)p.q + w.z * p.q_zstride + w.b * p.qs_b + w.h * p.qs_h;
+  const int kvi = (p.kv_idx0 + w.z) % p.kv_idx_mod;
+  const short *kp = (const short *)p.k + kvi * p.kv_zstride + w.b * p.ks_b + w.kvh * p.ks_h;
+  const short *vp = (const short *)p.v + kvi * p.kv_vzstride + w.b * p.vs_b + w.kvh * p.vs_h;
+  const IdMap qid = query_ids(p, w.z), kid = key_ids(p, w.z);
+  const float c = p.scale * kLog2e;
+
+  const int i_wg0 = w.qtile * (kPBM >> hshift);
+  const int i_wg1 = min(p.nq, i_wg0 + (kPBM >> hshift)) - 1;
+  const int iw0 = i_wg0 + wave_r * 32;
+  const int iw1 = min(p.nq - 1, iw0 + 31);
+  const bool wave_rows = iw0 < p.nq;
+  const int i = iw0 + c32;
+  const bool valid = i < p.nq;
+
+  const int kv_wg = key_prefix(p, kid, qid(i_wg1));
+  const int ntiles = (kv_wg + kPBN - 1) / kPBN;
+  const int kv_wl = wave_rows ? key_prefix(p, kid, qid(iw1)) : 0;
+  const int kv_wf = wave_rows ? key_prefix(p, kid, qid(iw0)) : 0;
+  const int ntiles_w = (kv_wl + kPBN - 1) / kPBN;
+  const int nfull_w = kv_wf / kPBN;
+  const int jlim = key_prefix(p, kid, qid(i));
+  // FWD: as in attn_packed_kernel
+  int f0 = 0, f1 = 0;
+  const short *fkp = nullptr, *fvp = nullptr;
+  if (FWD) {
+    const int dz = w.z + 1 < p.nz ? w.z + 1 : (p.fwd_wrap ? 0 : -1);
+    if (dz >= 0 && (hshift || w.h == w.kvh * (p.Hq / p.Hkv))) {
+      const int64_t ntk = (p.nk + kPBN - 1) / kPBN;
+      f0 = (int)(w.qtile * ntk / ntq);
+      f1 = (int)((w.qtile + 1) * ntk / ntq);
+      fkp = (const short *)p.fk + dz * p.kv_zstride + w.b * p.ks_b + w.kvh * p.ks_h;
+      fvp = (const short *)p.fv + dz * p.kv_vzstride + w.b * p.vs_b + w.kvh * p.vs_h;
+    }
+  }
+  if (!FWD && ntiles == 0 && p.accumulate) return;
+
+  f32x16 O[DT];
+  float m_run, m_top, lsum;
+  auto init_state = [&]() {
+    if (p.accumulate) {
+      load_state<D>(p, w, i, valid, c, O, m_run, m_top, lsum);
+    } else {
+      m_run = -FLT_MAX;
+      m_top = -FLT_MAX;
+      lsum = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
+    }
+  };
+
+  static_assert(KROW == 128 && VROW == 128 && KPW == 2 && VPW == 2, "d = 64 layout");
+  // A loading wave's two 1 KB pieces of a tile are 32 rows apart, which
+  // keeps the row swizzle: the second offset is the first plus 32 rows.
+  const bool loader = wave < kLW;
+  const uint32_t krow_b = (uint32_t)p.ks_t * 2;
+  uint32_t kvo0, vvo0;
+  {
+    const int row = (loader ? wave : 0) * KRPI + lane / CPR;
+    kvo0 = row * krow_b + (((lane % CPR) ^ chunk_swz<KROW>(row)) * 16);
+    const int dr = (loader ? wave : 0) * 8 + (lane >> 3);
+    vvo0 = dr * VROW + (((lane & 7) ^ chunk_swz<VROW>(dr)) * 16);
+  }
+  const uint32_t vslice_b = (uint32_t)D * (uint32_t)p.vs_t * 2u;
+  const auto vrsrc = __builtin_amdgcn_make_buffer_rsrc((void *)vp, 0, (int)vslice_b, kBufWord3);
+  auto k_rsrc = [&](const short *base, int tk) {  // K tile tk: its rows only
+    const int rows = min(p.nk - tk * kPBN, kPBN);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(base + (int64_t)tk * kPBN * p.ks_t), 0,
+                                             (int)(rows * krow_b), kBufWord3);
+  };
+  // FWD: tile t, resident in LDS stage st, written out by the waves that
+  // loaded it, at the offsets they loaded it from: read before, and stored
+  // after, the same waves' loads of the next tile (as in attn_packed_kernel)
+  struct Fwd {
+    u32x4 x[4];
+    bool on;
+  };
+  auto fwd_read = [&](int t, int st) {
+    Fwd f;
+    f.on = FWD && loader && t >= f0 && t < f1;
+    if (f.on) {
+      const char *ks = lds + st * KTILE + wave * 1024 + 16 * lane;
+      const char *vs = lds + VBASE + st * VTILE + wave * 1024 + 16 * lane;
+      f.x[0] = *(const u32x4 *)ks;
+      f.x[1] = *(const u32x4 *)(ks + kLW * 1024);
+      f.x[2] = *(const u32x4 *)vs;
+      f.x[3] = *(const u32x4 *)(vs + kLW * 1024);
+    }
+    return f;
+  };
+  auto fwd_store = [&](const Fwd &f, int t) {
+    if (!f.on) return 0;
+    const auto kdst = k_rsrc(fkp, t);
+    const auto vdst = __builtin_amdgcn_make_buffer_rsrc((void *)fvp, 0, (int)vslice_b, kBufWord3);
+    __builtin_amdgcn_raw_buffer_store_b128(f.x[0], kdst, kvo0, 0, kNT);
+    __builtin_amdgcn_raw_buffer_store_b128(f.x[1], kdst, kvo0 + 32 * krow_b, 0, kNT);
+    __builtin_amdgcn_raw_buffer_store_b128(f.x[2], vdst, vvo0, t * VTILE, kNT);
+    __builtin_amdgcn_raw_buffer_store_b128(f.x[3], vdst, vvo0, t * VTILE + 32 * VROW, kNT);
+    return 4;
+  };
+  // tiles [max(f0, t0), f1) this workgroup does not stream: global to global,
+  // one 1 KB piece of K and one of V^T per wave and tile
+  auto fwd_direct = [&](int t0) {
+    if (!FWD) return;
+    static_assert(KTILE == kPW * 1024 && VTILE == kPW * 1024, "one piece per wave");
+    const auto vdst = __builtin_amdgcn_make_buffer_rsrc((void *)fvp, 0, (int)vslice_b, kBufWord3);
+    for (int t = max(f0, t0); t < f1; ++t) {
+      const auto ksrc = k_rsrc(kp, t), kdst = k_rsrc(fkp, t);
+      const uint32_t ko = (wave * KRPI + lane / CPR) * krow_b + (lane % CPR) * 16;
+      const uint32_t vo = wave * 1024 + 16 * lane;
+      const u32x4 xk = __builtin_amdgcn_raw_buffer_load_b128(ksrc, ko, 0, kNT);
+      const u32x4 xv = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, vo, t * VTILE, kNT);
+      __builtin_amdgcn_raw_buffer_store_b128(xk, kdst, ko, 0, kNT);
+      __builtin_amdgcn_raw_buffer_store_b128(xv, vdst, vo, t * VTILE, kNT);
+    }
+  };
+  if (FWD && ntiles == 0 && p.accumulate) {
+    fwd_direct(0);
+    return;
+  }
+  if (ntiles > 0) {
+    auto load_k = [&](int tk, int kstage) {
+      const auto krsrc = k_rsrc(kp, tk);
+      if (!loader) return;
+      char *dst = lds + kstage * KTILE + wave * 1024;
+      dma16(krsrc, (lds_void *)dst, kvo0, 0);
+      dma16(krsrc, (lds_void *)(dst + kLW * 1024), kvo0 + 32 * krow_b, 0);
+    };
+    auto load_v = [&](int tv, int vstage) {
+      if (!loader) return;
+      char *dst = lds + VBASE + vstage * VTILE + wave * 1024;
+      dma16(vrsrc, (lds_void *)dst, vvo0, tv * VTILE);
+      dma16(vrsrc, (lds_void *)(dst + kLW * 1024), vvo0, tv * VTILE + 32 * VROW);
+    };
+    load_k(0, 0);
+    load_v(0, 0);
+    s16x8 qf[KS];
+    {
+      const short *qrow = qp + (int64_t)(valid ? i : 0) * p.qs_t;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s16x8 v = *(const s16x8 *)(qrow + 16 * ks + 8 * hl);
+        if (!valid) v = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
+        qf[ks] = v;
+      }
+    }
+    init_state();
+    // LDS read offsets: K row c32 (+32 kh) chunk 2 ks + hl and V^T row c32
+    // (+32 dt) chunk 2 q4 + hl, both swizzled by row c32: base ^ (j << 5)
+    // for j = ks or q4 (the chunk index sits in bits 4-6)
+    const int rbase = c32 * KROW + ((hl ^ chunk_swz<KROW>(c32)) << 4);
+
+    auto rowmax = [&](const f32x16 (&x)[2]) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, x[kh][r]);
+      return m;
+    };
+    auto probs = [&](const f32x16 (&S)[2], s16x8 (&P)[4]) {
+      const float nm = -m_run;
+      float ls = 0.f;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x16 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pb[e] = __builtin_amdgcn_exp2f(fmaf(S[q4 >> 1][8 * (q4 & 1) + e], c, nm));
+          ls += pb[e];
+        }
+        P[q4] = M::pack(pb, 0);
+      }
+      return ls;
+    };
+    auto rescale = [&](float mt) {
+      const float mn = fmaxf(m_run, mt);
+      const float al = __builtin_amdgcn_exp2f(m_run - mn);
+      lsum *= al;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[dt][r] *= al;
+      m_run = mn;
+    };
+
+    // Tile t sits in stage t & 1; the other stage, last read in tile t-1,
+    // takes tile t+1, published by the barrier at the end of tile t.
+    auto tile = [&](auto st_c, const int t) {
+      constexpr int ST = decltype(st_c)::value;
+      const Fwd fw = fwd_read(t, ST);
+      if (t + 1 < ntiles) {
+        load_k(t + 1, ST ^ 1);
+        load_v(t + 1, ST ^ 1);
+      }
+      const int stores = fwd_store(fw, t);
+      if (t < ntiles_w) {
+        // the offsets are rebuilt per tile from one register (kept out of
+        // the loop's live set)
+        int rb = rbase;
+        asm volatile("" : "+v"(rb));
+        const int ro[4] = {rb, rb ^ 32, rb ^ 64, rb ^ 96};
+        f32x16 S[2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) S[kh][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+            S[kh] = M::mma(*(const s16x8 *)(lds + ro[ks] + ST * KTILE + kh * 32 * KROW), qf[ks],
+                           S[kh]);
+        if (t >= nfull_w) {
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int j = t * kPBN + kh * 32 + (r >> 2) * 8 + 4 * hl + (r & 3);
+              if (j >= jlim) S[kh][r] = -INFINITY;
+            }
+        }
+        s16x8 P[4];
+        float ls = probs(S, P);
+        if (wave_any(ls > kSumLimit)) {
+          rescale(half_max(rowmax(S)) * c);
+          ls = probs(S, P);
+        }
+        lsum += ls;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            O[dt] = M::mma(
+                *(const s16x8 *)(lds + ro[q4] + VBASE + ST * VTILE + dt * 32 * VROW), P[q4], O[dt]);
+      }
+      // this wave's loads of tile t+1 have landed (its stores may still run)
+      if (stores)
+        __builtin_amdgcn_s_waitcnt(kWaitVm0 | 4);
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      if constexpr (FWD)
+        lds_barrier();
+      else
+        __syncthreads();
+    };
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+      tile(std::integral_constant<int, 0>(), t);
+      if (t + 1 >= ntiles) break;
+      tile(std::integral_constant<int, 1>(), t + 1);
+    }
+    fwd_direct(ntiles);
+  } else {
+    fwd_direct(0);
+    init_state();
+  }
+  store_state<D>(p, w, i, valid, O, m_run, m_run, lsum);
 }
 
 // V rows [b][h][j][c] (strides) -> packed [bh][tile][c][64]; one workgroup
@@ -481,7 +898,7 @@ __global__ void __launch_bounds__(256) pack_v_kernel(const short *__restrict__ v
   }
 }
 
-template <int D, bool BF16, bool EXACT>
+template <int D, bool BF16, bool EXACT, bool FWD>
 hipError_t launch_packed(const BatchParams &p, hipStream_t s) {
   const int hpg = p.Hq / p.Hkv;
   const int hshift = (hpg == 2 || hpg == 4 || hpg == 8) ? (hpg == 2 ? 1 : hpg == 4 ? 2 : 3) : 0;
@@ -492,18 +909,40 @@ hipError_t launch_packed(const BatchParams &p, hipStream_t s) {
   // more than 64 KB of LDS per workgroup must be opted into, once per process
   // (a function-local static: initialised once even with several host threads)
   static const hipError_t attr =
-      lds > 65536 ? hipFuncSetAttribute((const void *)attn_packed_kernel<D, BF16, EXACT>,
+      lds > 65536 ? hipFuncSetAttribute((const void *)attn_packed_kernel<D, BF16, EXACT, FWD>,
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
                   : hipSuccess;
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((attn_packed_kernel<D, BF16, EXACT>), dim3((unsigned)nwg), dim3(512), lds, s,
-                     p, ntq, hshift);
+  hipLaunchKernelGGL((attn_packed_kernel<D, BF16, EXACT, FWD>), dim3((unsigned)nwg), dim3(512),
+                     lds, s, p, ntq, hshift);
   return hipGetLastError();
+}
+
+template <bool BF16, bool FWD>
+hipError_t launch_lean64(const BatchParams &p, hipStream_t s) {
+  const int hpg = p.Hq / p.Hkv;
+  const int hshift = (hpg == 2 || hpg == 4 || hpg == 8) ? (hpg == 2 ? 1 : hpg == 4 ? 2 : 3) : 0;
+  const int rows = kPBM >> hshift;
+  const int ntq = (p.nq + rows - 1) / rows;
+  const int64_t nwg = (int64_t)ntq * p.nz * p.B * p.Hkv * (hshift ? 1 : hpg);
+  const size_t lds = (size_t)2 * kPBN * 64 * 2 + (size_t)2 * 64 * kPBN * 2;
+  hipLaunchKernelGGL((attn_lean64_kernel<BF16, FWD>), dim3((unsigned)nwg), dim3(512), lds, s, p,
+                     ntq, hshift);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16, bool FWD>
+hipError_t launch_packed_f(const BatchParams &p, hipStream_t s) {
+  if (D == 64 && !p.exact_m) return launch_lean64<BF16, FWD>(p, s);
+  return p.exact_m ? launch_packed<D, BF16, true, FWD>(p, s)
+                   : launch_packed<D, BF16, false, FWD>(p, s);
 }
 
 template <int D, bool BF16>
 hipError_t launch_packed_m(const BatchParams &p, hipStream_t s) {
-  return p.exact_m ? launch_packed<D, BF16, true>(p, s) : launch_packed<D, BF16, false>(p, s);
+  // the forwarding instantiation only where some problem forwards its block
+  const bool fwd = p.fwd && (p.nz > 1 || p.fwd_wrap);
+  return fwd ? launch_packed_f<D, BF16, true>(p, s) : launch_packed_f<D, BF16, false>(p, s);
 }
 
 }  // namespace

@@ -52,6 +52,13 @@ struct BatchParams {
   // to (a running state between hops; m + ln l is the same).
   int32_t exact_m;
   int32_t zz_c, zz_R, q_rank0;
+  // In-kernel hand-off (the ring's FORWARD mode, 16-bit packed path): with
+  // fwd = 1, problem z also writes the K block and the packed V block it reads
+  // to slot z + 1 of the receive buffers fk / fv (laid out like k / v, slot s
+  // at + s*kv_zstride / s*kv_vzstride), and with fwd_wrap the last problem to
+  // slot 0; every workgroup writes its share of the block's 64-key tiles.
+  void *fk, *fv;
+  int32_t fwd, fwd_wrap;
 };
 
 // Packed V: for each (b, h) n_pad/64 tiles of [d][64] (n_pad = n rounded up

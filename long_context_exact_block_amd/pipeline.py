@@ -2,8 +2,9 @@
 original token order to outputs in the original token order:
 
   index maps (ra_layout_permute) -> shard gather of Q, K, V (ra_layout_gather)
-  -> R hops of block attention + online-softmax fold with the K/V hand-off on
-  a side stream (ra_ring_fwd) -> scatter of O and LSE back (ra_layout_scatter).
+  -> R hops of block attention + online-softmax fold with the K/V hand-off (a
+  copy on a side stream, or written on by the block kernel: ra_ring_fwd's
+  COPY / FORWARD) -> scatter of O and LSE back (ra_layout_scatter).
 
 Device memory and streams come from PyTorch; every step runs in libra.so.
 """

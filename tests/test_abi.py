@@ -128,7 +128,7 @@ def _ring(**kw):
 
 @pytest.mark.parametrize("field,value,status", [
     ("R", 0, 2), ("n_ranks", 9, 2), ("rank0", 8, 2), ("rank0", -1, 2), ("rank0", 1, 2), ("layout", 5, 1),
-    ("handoff", 2, 1), ("merge_mode", 7, 1), ("dtype", -1, 3), ("d", 32, 2), ("Hkv", 3, 2),
+    ("handoff", 3, 1), ("merge_mode", 7, 1), ("dtype", -1, 3), ("d", 32, 2), ("Hkv", 3, 2),
     ("q_sh", 0, 1), ("o", 4104, 4),
 ])
 def test_ring_rejects(lib, field, value, status):
@@ -149,6 +149,8 @@ def test_ring_workspace_checks(lib):
     assert lib.ra_ring_fwd(ctypes.byref(a), ctypes.c_void_p(4096 + 16), need, None, None) == 4
     swap = _ring(handoff=1)
     assert lib.ra_ring_fwd_workspace_size(ctypes.byref(swap)) < need
+    forward = _ring(handoff=2)  # the same receive buffers as COPY
+    assert lib.ra_ring_fwd_workspace_size(ctypes.byref(forward)) == need
     sep = _ring(merge_mode=1)
     assert lib.ra_ring_fwd_workspace_size(ctypes.byref(sep)) > need
 
@@ -300,7 +302,7 @@ def _ring_bwd(**kw):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("dtype", rb.DT_FP32, 6), ("dtype", 9, 3), ("layout", 5, 1), ("handoff", 2, 1),
+    ("dtype", rb.DT_FP32, 6), ("dtype", 9, 3), ("layout", 5, 1), ("handoff", 3, 1),
     ("R", 0, 2), ("n_ranks", 9, 2),
     ("rank0", 1, 2), ("d", 32, 2), ("Hkv", 3, 2), ("n", (1 << 23) + 2, 6),
     ("scale", float("inf"), 1), ("dout_sh", 0, 1), ("lse", 0, 1), ("dv_sh", 4104, 4),

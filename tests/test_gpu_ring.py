@@ -1,7 +1,7 @@
 """ra_ring_fwd (the whole emulated ring) against the fp64 oracle on small and
 medium shapes: every row compared; both layouts, ring sizes 1..8, a single
 rank's share, grouped heads, all dtypes, causal and not.  Plus the ring's own
-invariants: COPY and SWAP hand-offs bitwise equal, run-to-run bitwise equal,
+invariants: COPY, FORWARD and SWAP hand-offs bitwise equal, run-to-run bitwise equal,
 FUSED and SEPARATE folds equal to rounding, and the original-order pipeline."""
 import math
 
@@ -95,6 +95,47 @@ def test_copy_equals_swap_and_is_deterministic(case):
         assert torch.equal(torch.nan_to_num(l1, nan=7.0), torch.nan_to_num(l, nan=7.0))
 
 
+# FORWARD on full rings (the block kernels write every block on: d = 128 and the
+# lean d = 64 kernel, grouped heads with one workgroup per group and with one
+# per head, ragged tiles, contiguous causal hops whose workgroups have no keys
+# and only forward), on rank subsets (side copy for the entering block) and on
+# the fp32 path (copied as in COPY)
+FWD_CASES = [CASES[i] for i in (0, 1, 2, 3, 5, 6, 7, 8, 10, 11, 12)] + [
+    ("bf16_striped_R4_gqa3", 1, 3, 1, 1024, 128, 4, "striped", "bf16", True, 0, 4),
+    ("bf16_contig_R4_causal", 1, 2, 2, 2048, 128, 4, "contiguous", "bf16", True, 0, 4),
+    ("fp16_contig_R4_d64_ranks0to2", 1, 4, 2, 2048, 64, 4, "contiguous", "fp16", True, 0, 3),
+]
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=lambda c: c[0])
+def test_forward_equals_swap(case):
+    """FORWARD hand-off: the block kernel writes each block it streams to the next
+    computed rank's receive buffer.  Bitwise equal to SWAP in both folds, with one
+    stream or two."""
+    import torch
+    name, B, Hq, Hkv, S, d, R, layout, dtype, causal, rank0, n_ranks = case
+    x = make_inputs(B, Hq, Hkv, S, d, dtype, 83)
+    for mm in (rb.MERGE_FUSED, rb.MERGE_SEPARATE):
+        _, o0, l0 = run_ring(case, x, rb.HANDOFF_SWAP, merge_mode=mm)
+        for same in (False, True):
+            _, o1, l1 = run_ring(case, x, rb.HANDOFF_FORWARD, merge_mode=mm, same_stream=same)
+            # rows of ranks that are not computed stay NaN in every run
+            assert torch.equal(o0, o1), (name, mm, same)
+            assert torch.equal(torch.nan_to_num(l0, nan=7.0), torch.nan_to_num(l1, nan=7.0)), (
+                name, mm, same)
+
+
+@pytest.mark.parametrize("case", [FWD_CASES[i] for i in (1, 2, 6)], ids=lambda c: c[0])
+def test_forward_matches_oracle(case):
+    name, B, Hq, Hkv, S, d, R, layout, dtype, causal, rank0, n_ranks = case
+    x = make_inputs(B, Hq, Hkv, S, d, dtype, 84)
+    _, o, lse = run_ring(case, x, rb.HANDOFF_FORWARD)
+    ro, rl = oracle.attention_full(x["q32"], x["k32"], x["v32"], 1 / math.sqrt(d), causal)
+    tok = owned_tokens(case)
+    parity.check_o(parity.to_f64(o)[:, :, tok], ro[:, :, tok], name)
+    parity.check_lse(parity.to_f64(lse)[:, :, tok], rl[:, :, tok], name)
+
+
 @pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[3], CASES[7]], ids=lambda c: c[0])
 def test_fused_and_separate_merge_agree(case):
     name, B, Hq, Hkv, S, d, R, layout, dtype, causal, rank0, n_ranks = case
@@ -173,14 +214,16 @@ def test_stream_delays_keep_results():
     events ordering them correctly the outputs stay bitwise equal."""
     import os
     import torch
-    for case in (CASES[1], CASES[5], CASES[7], CASES[11]):
+    for case, hm in ((CASES[1], rb.HANDOFF_COPY), (CASES[5], rb.HANDOFF_COPY),
+                     (CASES[7], rb.HANDOFF_COPY), (CASES[11], rb.HANDOFF_COPY),
+                     (CASES[6], rb.HANDOFF_FORWARD), (CASES[7], rb.HANDOFF_FORWARD)):
         name, B, Hq, Hkv, S, d, R, layout, dtype, causal, rank0, n_ranks = case
         x = make_inputs(B, Hq, Hkv, S, d, dtype, 81)
-        _, o0, l0 = run_ring(case, x)
+        _, o0, l0 = run_ring(case, x, hm)
         for var in ("RA_DEBUG_DELAY_COPY", "RA_DEBUG_DELAY_COMPUTE"):
             os.environ[var] = "40"
             try:
-                _, o1, l1 = run_ring(case, x)
+                _, o1, l1 = run_ring(case, x, hm)
             finally:
                 del os.environ[var]
             # rows of ranks that are not computed stay NaN in every run
