@@ -58,11 +58,35 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_name(w):
+def kernel_name(w, fused=True, forwards=False):
     """The block kernel a ring of this workload runs."""
     if w.dtype == "fp32":
         return "attn_block32_kernel<%d>" % w.d
-    return "attn_packed_kernel<%d,%s>" % (w.d, w.dtype)
+    name = ("attn_lean64_kernel<%s>" % w.dtype if (w.d == 64 and fused) else
+            "attn_packed_kernel<%d,%s>" % (w.d, w.dtype))
+    return name + (" (forwarding)" if forwards else "")
+
+
+def forwards_in_kernel(rb, w, handoff):
+    """Whether the ring's block kernel writes the blocks on itself (the FORWARD hand-off on
+    hops too short for the thin side copy; the library's rule, ra_handoff_thin)."""
+    if handoff != "forward" or w.R == 1 or w.dtype == "fp32":
+        return False
+    elt = 2
+    kb = w.ranks * w.B * w.Hkv * w.n * w.d * elt
+    vb = w.ranks * w.B * w.Hkv * w.d * ((w.n + 63) // 64 * 64) * elt
+    pairs = w.ranks * w.B * w.Hq * float(w.n) * w.n * (0.5 if w.causal else 1.0)
+    return not rb.thin_handoff(2.0 * (kb + vb), pairs, w.d)
+
+
+def hop_forward_bytes(w):
+    """Bytes a forwarding launch writes on at each hop: the K block and the packed V block of
+    every computed rank whose successor is computed (on a full ring every rank; the last hop
+    forwards nothing)."""
+    elt = 2
+    blk = w.B * w.Hkv * (w.n * w.d + w.d * ((w.n + 63) // 64 * 64)) * elt
+    senders = w.ranks if w.ranks == w.R else w.ranks - 1
+    return [blk * senders if h + 1 < w.R else 0 for h in range(w.R)]
 
 
 def rank_hop_pairs(w, layout_code, r, h):
@@ -651,6 +675,10 @@ def main():
     flops_per_launch = [4.0 * w.d * w.B * w.Hq * p for p in pairs]
     achieved = sum(flops_per_launch) * K / (hop_ms.sum() * 1e-3) / 1e12
     bytes_per_launch = hop_bytes(w, lcode, args.merge == "fused")
+    # with the FORWARD hand-off on short hops the launch also writes the block on
+    forwards = forwards_in_kernel(rb, w, args.handoff)
+    fwd_bytes = hop_forward_bytes(w) if forwards else [0] * R
+    bytes_per_launch = [a + b for a, b in zip(bytes_per_launch, fwd_bytes)]
     achieved_gbs = sum(bytes_per_launch) * K / (hop_ms.sum() * 1e-3) / 1e9
     peak_dt = PEAK_BF16_TFLOPS if w.dtype != "fp32" else PEAK_FP32_TFLOPS
     # the kernel's roof: MFMA time or HBM time of its algorithmic work, whichever is longer
@@ -738,10 +766,11 @@ def main():
               "unit": "TFLOP/s", "frac": round(achieved / peak_dt, 4),
               "hbm_view": {"achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": round(achieved_gbs / PEAK_HBM_GBS, 4)}}),
-            traffic=traffic, kernel=kernel_name(w), launches=R * K,
-            avg_launch_ms=round(float(hop_ms.mean()), 4),
+            traffic=traffic, kernel=kernel_name(w, args.merge == "fused", forwards),
+            launches=R * K, avg_launch_ms=round(float(hop_ms.mean()), 4),
             algorithmic_flops_per_launch=sum(flops_per_launch) / R,
-            algorithmic_bytes_per_launch=sum(bytes_per_launch) / R),
+            algorithmic_bytes_per_launch=sum(bytes_per_launch) / R,
+            handoff_bytes_per_launch=sum(fwd_bytes) / R),
         "step_ms_median": round(float(np.median(step_ms)), 3),
         "step_ms_min": round(float(step_ms.min()), 3),
         "hop_ms": [round(float(x), 3) for x in hop_ms.mean(axis=0)],

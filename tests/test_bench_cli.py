@@ -57,3 +57,26 @@ def test_committed_traffic_summaries_match_the_sources():
             prof["hbm_bytes_per_launch"], (
                 "%s: the kernel sources changed since FETCH_SIZE / WRITE_SIZE were taken; "
                 "re-take them with the commands the file lists" % summary)
+
+
+def test_forwarded_bytes_counted_only_where_the_kernel_forwards():
+    """The FORWARD hand-off writes blocks on from the block kernel only on hops the thin
+    side copy cannot hide (the library's rule); only then do the launch's algorithmic bytes
+    include the blocks it writes on (K and packed V of every sending rank, no hop after the
+    last)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from long_context_exact_block_amd import binding as rb
+    from long_context_exact_block_amd import configs
+    c5 = configs.SHORT_512
+    assert bench.forwards_in_kernel(rb, c5, "forward")
+    assert not bench.forwards_in_kernel(rb, c5, "copy")
+    for w in (configs.SHARE_1M, configs.MHA_32K, configs.GQA_128K, configs.TINY):
+        assert not bench.forwards_in_kernel(rb, w, "forward"), w.name
+    fb = bench.hop_forward_bytes(c5)
+    per_rank = c5.B * c5.Hkv * (c5.n * c5.d + c5.d * c5.n) * 2  # n = 512: no padding
+    assert fb == [per_rank * c5.R] * (c5.R - 1) + [0]
+    sub = configs.SHARE_1M  # one computed rank: it sends nothing in the kernel
+    assert bench.hop_forward_bytes(sub) == [0] * sub.R
+    assert bench.kernel_name(c5, True, True) == "attn_lean64_kernel<fp16> (forwarding)"
+    assert bench.kernel_name(c5, False) == "attn_packed_kernel<64,fp16>"
