@@ -59,11 +59,12 @@ def log(*a):
 
 
 def kernel_name(w, fused=True, forwards=False):
-    """The block kernel a ring of this workload runs."""
+    """The block kernel a ring of this workload runs (fused: running state, else exact-max
+    partials for ra_merge)."""
     if w.dtype == "fp32":
         return "attn_block32_kernel<%d>" % w.d
-    name = ("attn_lean64_kernel<%s>" % w.dtype if (w.d == 64 and fused) else
-            "attn_packed_kernel<%d,%s>" % (w.d, w.dtype))
+    name = ("attn_lean64_kernel<%s%s>" % (w.dtype, "" if fused else ", exact") if w.d == 64 else
+            "attn_packed_kernel<%d,%s%s>" % (w.d, w.dtype, "" if fused else ", exact"))
     return name + (" (forwarding)" if forwards else "")
 
 

@@ -564,18 +564,18 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
 }
 
 
-// Lean variant for d = 64 in the fused ring (running maximum, no exact row
-// maximum).  At d = 64 a 64-key tile is 16 MFMAs against 32 exponentials per
-// wave, and a workgroup's key blocks are short (the 512-token shards: 8
-// tiles), so per-workgroup costs -- the running state in and out, the first
+// Lean variant for d = 64 (both folds, and the public block partial).  At
+// d = 64 a 64-key tile is 16 MFMAs against 32 exponentials per wave, and a
+// workgroup's key blocks are short (the 512-token shards: 8 tiles), so
+// per-workgroup costs -- the running state in and out, the first
 // loads, the tile barrier -- weigh as much as the products.  This variant
 // gives up the in-wave pipelining (QK of the next tile under the exponentials
 // of this one, lagging waves) for registers: at <= 128 VGPRs two workgroups
 // share a CU, four waves per SIMD, and one workgroup's state traffic and
 // barrier waits run beside the other's products.  Same arithmetic in the same
-// order as attn_packed_kernel<64, *, false>; K and V^T tiles one tile ahead,
+// order as attn_packed_kernel<64, *, EXACT>; K and V^T tiles one tile ahead,
 // two stages each (32 KB of LDS).
-template <bool BF16, bool FWD>
+template <bool BF16, bool EXACT, bool FWD>
 __global__ void __launch_bounds__(512, 4) attn_lean64_kernel(BatchParams p, int ntq, int hshift) {
   using M = Mfma16<BF16>;
   constexpr int D = 64;
@@ -824,10 +824,18 @@ __global__ void __launch_bounds__(512, 4) attn_lean64_kernel(BatchParams p, int 
             }
         }
         s16x8 P[4];
-        float ls = probs(S, P);
-        if (wave_any(ls > kSumLimit)) {
-          rescale(half_max(rowmax(S)) * c);
+        float ls;
+        if (EXACT) {  // the tile's row maximum first, as in attn_packed_kernel
+          const float mt = half_max(rowmax(S)) * c;
+          m_top = fmaxf(m_top, mt);
+          if (wave_any(mt > m_run + kTau)) rescale(mt);
           ls = probs(S, P);
+        } else {
+          ls = probs(S, P);
+          if (wave_any(ls > kSumLimit)) {
+            rescale(half_max(rowmax(S)) * c);
+            ls = probs(S, P);
+          }
         }
         lsum += ls;
 #pragma unroll
@@ -859,7 +867,7 @@ __global__ void __launch_bounds__(512, 4) attn_lean64_kernel(BatchParams p, int 
     fwd_direct(0);
     init_state();
   }
-  store_state<D>(p, w, i, valid, O, m_run, m_run, lsum);
+  store_state<D>(p, w, i, valid, O, m_run, EXACT ? m_top : m_run, lsum);
 }
 
 // V rows [b][h][j][c] (strides) -> packed [bh][tile][c][64]; one workgroup
@@ -918,7 +926,7 @@ hipError_t launch_packed(const BatchParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool BF16, bool FWD>
+template <bool BF16, bool EXACT, bool FWD>
 hipError_t launch_lean64(const BatchParams &p, hipStream_t s) {
   const int hpg = p.Hq / p.Hkv;
   const int hshift = (hpg == 2 || hpg == 4 || hpg == 8) ? (hpg == 2 ? 1 : hpg == 4 ? 2 : 3) : 0;
@@ -926,14 +934,15 @@ hipError_t launch_lean64(const BatchParams &p, hipStream_t s) {
   const int ntq = (p.nq + rows - 1) / rows;
   const int64_t nwg = (int64_t)ntq * p.nz * p.B * p.Hkv * (hshift ? 1 : hpg);
   const size_t lds = (size_t)2 * kPBN * 64 * 2 + (size_t)2 * 64 * kPBN * 2;
-  hipLaunchKernelGGL((attn_lean64_kernel<BF16, FWD>), dim3((unsigned)nwg), dim3(512), lds, s, p,
-                     ntq, hshift);
+  hipLaunchKernelGGL((attn_lean64_kernel<BF16, EXACT, FWD>), dim3((unsigned)nwg), dim3(512), lds,
+                     s, p, ntq, hshift);
   return hipGetLastError();
 }
 
 template <int D, bool BF16, bool FWD>
 hipError_t launch_packed_f(const BatchParams &p, hipStream_t s) {
-  if (D == 64 && !p.exact_m) return launch_lean64<BF16, FWD>(p, s);
+  if (D == 64)
+    return p.exact_m ? launch_lean64<BF16, true, FWD>(p, s) : launch_lean64<BF16, false, FWD>(p, s);
   return p.exact_m ? launch_packed<D, BF16, true, FWD>(p, s)
                    : launch_packed<D, BF16, false, FWD>(p, s);
 }

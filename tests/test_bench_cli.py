@@ -79,4 +79,5 @@ def test_forwarded_bytes_counted_only_where_the_kernel_forwards():
     sub = configs.SHARE_1M  # one computed rank: it sends nothing in the kernel
     assert bench.hop_forward_bytes(sub) == [0] * sub.R
     assert bench.kernel_name(c5, True, True) == "attn_lean64_kernel<fp16> (forwarding)"
-    assert bench.kernel_name(c5, False) == "attn_packed_kernel<64,fp16>"
+    assert bench.kernel_name(c5, False) == "attn_lean64_kernel<fp16, exact>"
+    assert bench.kernel_name(configs.SHARE_1M) == "attn_packed_kernel<128,bf16>"
