@@ -941,10 +941,11 @@ hipError_t launch_lean64(const BatchParams &p, hipStream_t s) {
 
 template <int D, bool BF16, bool FWD>
 hipError_t launch_packed_f(const BatchParams &p, hipStream_t s) {
-  if (D == 64)
+  if constexpr (D == 64)  // every packed-V call at d = 64 runs the lean kernel
     return p.exact_m ? launch_lean64<BF16, true, FWD>(p, s) : launch_lean64<BF16, false, FWD>(p, s);
-  return p.exact_m ? launch_packed<D, BF16, true, FWD>(p, s)
-                   : launch_packed<D, BF16, false, FWD>(p, s);
+  else
+    return p.exact_m ? launch_packed<D, BF16, true, FWD>(p, s)
+                     : launch_packed<D, BF16, false, FWD>(p, s);
 }
 
 template <int D, bool BF16>
