@@ -302,15 +302,14 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
     // stage (buffer loads with the LDS destination in M0: lane l's 16 bytes
     // land at base + 16 l, so the swizzle is applied on the source side).
     // Completion is awaited (vmcnt) before the barrier that publishes the stage.
+    // (loading waves only: the callers test it)
     auto load_k = [&](int tk, int kstage) {
       const auto krsrc = k_rsrc(kp, tk);
-      if (!loader) return;
 #pragma unroll
       for (int u = 0; u < KPW; ++u)
         dma16(krsrc, (lds_void *)(lds + kstage * KTILE + kLW * 1024 * u + wave * 1024), kvo[u], 0);
     };
     auto load_v = [&](int tv, int vso) {  // vso: byte offset of the V^T stage
-      if (!loader) return;
 #pragma unroll
       for (int u = 0; u < VPW; ++u)
         dma16(vrsrc, (lds_void *)(lds + VBASE + vso + kLW * 1024 * u + wave * 1024), vvo[u],
@@ -320,9 +319,11 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
     // The first tiles, the Q fragments and the running state are requested
     // together, so their latencies overlap: K tiles 0 and 1 and V^T tile 0
     // (awaited before the prologue's barrier) ...
-    load_k(0, 0);
-    if (ntiles > 1) load_k(1, 1);
-    load_v(0, 0);
+    if (loader) {
+      load_k(0, 0);
+      if (ntiles > 1) load_k(1, 1);
+      load_v(0, 0);
+    }
     // ... Q fragments (B operand of S^T = K Q^T): d = 16ks + 8hl .. +7 of
     // this lane's row ...
     s16x8 qf[KS];
@@ -415,7 +416,15 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
     const bool lag = !EXACT && wave >= kPW / 2;
     s16x8 P[4];        // probabilities of the tile whose PV is pending
     s16x8 va0[DT];     // its first group of V^T fragments, read ahead
-    int vst = 0;       // V^T stage of tile t (t % 3)
+    // byte offsets of the V^T stages of tiles t, t+1 and t-1 (stage t % 3)
+    int vcur = 0, vnext = VTILE, vprev = 2 * VTILE;
+    // The per-tile tests as one scalar compare each: a loading wave loads K
+    // tile t+2 while t < kload_end and V^T tile t+1 while t < vload_end; a
+    // lagging wave runs the PV of tile t-1 while t-1 < pv_lag_n (unsigned, so
+    // not at t = 0).
+    const int kload_end = loader ? ntiles - 2 : 0;
+    const int vload_end = loader ? ntiles - 1 : 0;
+    const unsigned pv_lag_n = lag ? (unsigned)ntiles_w : 0u;
     // O^T += V^T P^T for the V^T tile in stage offset vso (va0 read already);
     // EXACT: returns the row max of Sm, computed in the MFMA shadow
     auto pv = [&](int vso, const f32x16 (&Sm)[2]) {
@@ -452,14 +461,11 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
         lds_barrier();
       else
         __syncthreads();
-      const int vcur = vst * VTILE;
-      const int vnext = (vst == 2 ? 0 : vst + 1) * VTILE;
-      const int vprev = (vst == 0 ? 2 : vst - 1) * VTILE;
-      if (t + 2 < ntiles) load_k(t + 2, PAR);
-      if (t + 1 < ntiles) load_v(t + 1, vnext);
+      if (t < kload_end) load_k(t + 2, PAR);
+      if (t < vload_end) load_v(t + 1, vnext);
       int stores = t + 1 < ntiles ? fwd_k(t + 1, PAR ^ 1) : 0;
       stores += fwd_v(t, vcur);
-      if (lag && t >= 1 && t - 1 < ntiles_w) {
+      if ((unsigned)(t - 1) < pv_lag_n) {
         const float m2 = pv(vprev, Sc);
         if (EXACT) mx = m2;
       }
@@ -544,7 +550,10 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
         }
       }
       wait_loads(stores);  // this wave's tile loads have landed
-      vst = vnext / VTILE;
+      const int vfree = vprev;
+      vprev = vcur;
+      vcur = vnext;
+      vnext = vfree;
     };
     // two tiles per iteration so the K stages are immediates and the S
     // register sets swap roles instead of being copied
@@ -554,7 +563,7 @@ __global__ void __launch_bounds__(512) attn_packed_kernel(BatchParams p, int ntq
       tile(std::integral_constant<int, 1>(), t + 1, S1, S);
     }
     // the lagging waves' PV of the last tile (no stage is reloaded any more)
-    if (lag && ntiles_w == ntiles) pv((vst == 0 ? 2 : vst - 1) * VTILE, S);
+    if (lag && ntiles_w == ntiles) pv(vprev, S);
     fwd_direct(ntiles);
   } else {
     fwd_direct(0);
@@ -682,8 +691,16 @@ __global__ void __launch_bounds__(512, 4) attn_lean64_kernel(BatchParams p, int 
     Fwd f;
     f.on = FWD && loader && t >= f0 && t < f1;
     if (f.on) {
-      const char *ks = lds + st * KTILE + wave * 1024 + 16 * lane;
-      const char *vs = lds + VBASE + st * VTILE + wave * 1024 + 16 * lane;
+      // the lane's 16-byte slot, rebuilt from the lane id here (kept live
+      // across the tile it is spilled, and its reload waits for the stores)
+      int slot;
+      asm volatile(
+          "v_mbcnt_lo_u32_b32 %0, -1, 0\n\t"
+          "v_mbcnt_hi_u32_b32 %0, -1, %0\n\t"
+          "v_lshlrev_b32 %0, 4, %0"
+          : "=v"(slot));
+      const char *ks = lds + st * KTILE + wave * 1024 + slot;
+      const char *vs = lds + VBASE + st * VTILE + wave * 1024 + slot;
       f.x[0] = *(const u32x4 *)ks;
       f.x[1] = *(const u32x4 *)(ks + kLW * 1024);
       f.x[2] = *(const u32x4 *)vs;
@@ -722,21 +739,22 @@ __global__ void __launch_bounds__(512, 4) attn_lean64_kernel(BatchParams p, int 
     return;
   }
   if (ntiles > 0) {
+    // (loading waves only: the callers test it)
     auto load_k = [&](int tk, int kstage) {
       const auto krsrc = k_rsrc(kp, tk);
-      if (!loader) return;
       char *dst = lds + kstage * KTILE + wave * 1024;
       dma16(krsrc, (lds_void *)dst, kvo0, 0);
       dma16(krsrc, (lds_void *)(dst + kLW * 1024), kvo0 + 32 * krow_b, 0);
     };
     auto load_v = [&](int tv, int vstage) {
-      if (!loader) return;
       char *dst = lds + VBASE + vstage * VTILE + wave * 1024;
       dma16(vrsrc, (lds_void *)dst, vvo0, tv * VTILE);
       dma16(vrsrc, (lds_void *)(dst + kLW * 1024), vvo0, tv * VTILE + 32 * VROW);
     };
-    load_k(0, 0);
-    load_v(0, 0);
+    if (loader) {
+      load_k(0, 0);
+      load_v(0, 0);
+    }
     s16x8 qf[KS];
     {
       const short *qrow = qp + (int64_t)(valid ? i : 0) * p.qs_t;
@@ -788,11 +806,13 @@ __global__ void __launch_bounds__(512, 4) attn_lean64_kernel(BatchParams p, int 
     };
 
     // Tile t sits in stage t & 1; the other stage, last read in tile t-1,
-    // takes tile t+1, published by the barrier at the end of tile t.
+    // takes tile t+1, published by the barrier at the end of tile t.  A
+    // loading wave loads while t < load_end (one scalar compare per tile).
+    const int load_end = loader ? ntiles - 1 : 0;
     auto tile = [&](auto st_c, const int t) {
       constexpr int ST = decltype(st_c)::value;
       const Fwd fw = fwd_read(t, ST);
-      if (t + 1 < ntiles) {
+      if (t < load_end) {
         load_k(t + 1, ST ^ 1);
         load_v(t + 1, ST ^ 1);
       }
