@@ -1,7 +1,10 @@
 """The five workloads at full size, in the launch configuration the benchmark
-times (COPY hand-off, fused online-softmax fold, original-order pipeline),
-compared with the fp64 oracle on seeded samples of query rows computed one by
-one over their full allowed key sets.  The sample always contains token 0 and
+times (FORWARD hand-off: on the 512-token shards the block kernel writes each
+block on to the next rank, elsewhere the side copy as in COPY; fused
+online-softmax fold; original-order pipeline), compared with the fp64 oracle on
+seeded samples of query rows computed one by one over their full allowed key
+sets.  Where the block kernel forwards, the COPY hand-off's outputs at full size
+must be bitwise equal.  The sample always contains token 0 and
 token S-1 when owned, and the first and last local row of every computed rank
 (under the striped layout the first local row is the row that sees no key in
 blocks coming from higher ranks)."""
@@ -19,6 +22,19 @@ from tests import parity
 pytestmark = pytest.mark.gpu
 
 RANDOM_ROWS = {1: 256, 2: 192, 3: 128, 4: 48, 5: 256}
+
+
+def forwards_in_kernel(w, layout):
+    """Whether the FORWARD hand-off has the block kernel write blocks on for this
+    workload: 16-bit inputs (the packed path), more than one rank, and hops too
+    short for the thin side copy to hide (the library's own rule)."""
+    if w.dtype == "fp32" or w.R == 1:
+        return False
+    elt = 2
+    kb = w.ranks * w.B * w.Hkv * w.n * w.d * elt
+    vb = w.ranks * w.B * w.Hkv * w.d * ((w.n + 63) // 64 * 64) * elt
+    pairs = w.ranks * w.B * w.Hq * float(w.n) * w.n * (0.5 if w.causal else 1.0)
+    return not rb.thin_handoff(2.0 * (kb + vb), pairs, w.d)
 
 
 def _cases():
@@ -46,10 +62,21 @@ def test_full_size_workload(w, layout):
     o = torch.zeros((w.B, w.Hq, w.S, w.d), dtype=tdt, device="cuda")
     lse = torch.full((w.B, w.Hq, w.S), float("nan"), dtype=torch.float32, device="cuda")
     ra = RingAttention(w.B, w.Hq, w.Hkv, w.S, w.d, w.R, layout, tdt, w.causal, w.scale,
-                       rank0=w.rank0, n_ranks=w.ranks)
+                       rank0=w.rank0, n_ranks=w.ranks, handoff=rb.HANDOFF_FORWARD)
     print("[full] %s %s: ring" % (w.name, layout), flush=True)
     ra.run(q, k, v, o, lse)
     torch.cuda.synchronize()
+    if forwards_in_kernel(w, layout):
+        print("[full] %s %s: ring with the COPY hand-off" % (w.name, layout), flush=True)
+        o2 = torch.zeros_like(o)
+        lse2 = torch.full_like(lse, float("nan"))
+        RingAttention(w.B, w.Hq, w.Hkv, w.S, w.d, w.R, layout, tdt, w.causal, w.scale,
+                      rank0=w.rank0, n_ranks=w.ranks, handoff=rb.HANDOFF_COPY).run(
+                          q, k, v, o2, lse2)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2), "%s %s: FORWARD and COPY outputs differ" % (w.name, layout)
+        assert torch.equal(lse, lse2), "%s %s: FORWARD and COPY LSE differ" % (w.name, layout)
+        del o2, lse2
 
     fwd, _ = oracle.layout_maps(rb.LAYOUTS[layout], w.S, w.R)
     special, picks = parity.sample_tokens(fwd, w.n, w.rank0, w.ranks, RANDOM_ROWS[w.index],
@@ -98,7 +125,7 @@ def _mha_32k_outputs():
         o = torch.zeros((w.B, w.Hq, w.S, w.d), dtype=tdt, device="cuda")
         lse = torch.full((w.B, w.Hq, w.S), float("nan"), dtype=torch.float32, device="cuda")
         ra = RingAttention(w.B, w.Hq, w.Hkv, w.S, w.d, w.R, layout, tdt, w.causal, w.scale,
-                           rank0=w.rank0, n_ranks=w.ranks)
+                           rank0=w.rank0, n_ranks=w.ranks, handoff=rb.HANDOFF_FORWARD)
         ra.run(q, k, v, o, lse)
         torch.cuda.synchronize()
         _MHA_OUT[layout] = (o.cpu().double().numpy(), lse.cpu().double().numpy())
