@@ -34,6 +34,12 @@ CASES = [
     ("bf16_zigzag_ragged_chunks", 1, 2, 2, 8 * 200, 128, 4, "zigzag", "bf16", True, 0, 4),
     ("fp32_zigzag_R3", 1, 2, 2, 768, 64, 3, "zigzag", "fp32", True, 0, 3),
     ("bf16_zigzag_noncausal", 1, 2, 2, 1024, 128, 4, "zigzag", "bf16", False, 0, 4),
+    # K/V groups a multiple of 8 (one XCD per group residue): causal work taken two groups at a
+    # time -- an even count of groups per XCD, an odd one (the last group alone), query heads as
+    # work items of their own (3 per K/V head), and grouped heads in one workgroup
+    ("bf16_striped_R2_16groups_3heads", 1, 24, 8, 1024, 64, 2, "striped", "bf16", True, 0, 2),
+    ("fp16_contig_R3_24groups", 1, 8, 8, 1536, 128, 3, "contiguous", "fp16", True, 0, 3),
+    ("bf16_zigzag_R2_16groups_gqa4", 1, 32, 8, 2048, 128, 2, "zigzag", "bf16", True, 0, 2),
 ]
 
 
