@@ -26,6 +26,9 @@ one at a time, and on identities that hold at any size.
   the same bound against the root sum of squares of the per-row and per-key
   terms: they tie the dq kernel to the dk kernel, and dv to the forward output,
   on every key rather than the tail only.
+* The per-hop unit itself (ra_block_bwd) at the 1M share's hop shape, where lse and
+  O are inputs: with seeded stand-ins on both sides the oracle computes dk and dv of
+  keys anywhere in the 131,072-key block, in both striped block classes.
 """
 import gc
 import math
@@ -186,3 +189,73 @@ def check_backward(w, layout, kv_heads, tail, n_rand, grads):
     gc.collect()
     torch.cuda.empty_cache()
     assert math.isfinite(float(rl.sum()))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("kg0,shift", [(3, 0), (4, 1)], ids=["src_le_rank", "src_gt_rank"])
+def test_block_bwd_full_hop_keys_everywhere(kg0, shift):
+    """ra_block_bwd at the 1M-token share's per-hop shape (131,072 queries x 131,072 keys,
+    d = 128, bf16, one head) in both striped block classes of rank 3: query ids 3 + 8i and
+    key ids kg0 + 8j, so key j is allowed for query i iff j <= i (a source at or below the
+    rank, kg0 = 3) or j < i (above it, kg0 = 4).  dk and dv are compared element by element
+    at keys spread over the whole block -- key 0, which (nearly) every query sees, tile and
+    workgroup boundaries, seeded picks and the last keys.  The block kernels take lse and O
+    as inputs, so both sides get the same seeded stand-ins: lse_i = ln(#allowed keys) +
+    scale^2 |q_i|^2 / 2 (what ln sum_j exp(s_ij) is for Gaussian scores, so the
+    probabilities have their real scale), O and dO seeded, and the oracle needs no forward
+    pass over the block.  It sees the block as a causal sequence of its own: row i at
+    position i, key j at position j + shift."""
+    import torch
+    n, d = 131072, 128
+    scale = 1.0 / math.sqrt(d)
+    shp = (1, 1, n, d)
+    q_st, q32 = inputs.to_dtype(inputs.normal(shp, 7101), "bf16")
+    k_st, k32 = inputs.to_dtype(inputs.normal(shp, 7102), "bf16")
+    v_st, v32 = inputs.to_dtype(inputs.normal(shp, 7103), "bf16")
+    g_st, g32 = inputs.to_dtype(inputs.normal(shp, 7104), "bf16")
+    o_st, o32 = inputs.to_dtype(0.05 * inputs.normal(shp, 7105), "bf16")
+    qd = q32[0, 0].astype(np.float64)
+    allowed = np.maximum(np.arange(1, n + 1, dtype=np.float64) - shift, 1.0)
+    lse = np.log(allowed) + 0.5 * scale * scale * (qd * qd).sum(-1)
+    lse = lse.astype(np.float32).astype(np.float64)  # the kernel reads it as fp32
+    Dv = (g32[0, 0].astype(np.float64) * o32[0, 0].astype(np.float64)).sum(-1)
+
+    dev = lambda st: parity.to_device(st, "bf16")
+    q, k, v, g, o = dev(q_st), dev(k_st), dev(v_st), dev(g_st), dev(o_st)
+    lse_d = torch.from_numpy(lse.astype(np.float32).reshape(1, 1, n)).cuda()
+    dq = torch.zeros(shp, dtype=torch.float32, device="cuda")
+    dk = torch.zeros(shp, dtype=torch.float32, device="cuda")
+    dv = torch.zeros(shp, dtype=torch.float32, device="cuda")
+    a = rb.block_bwd_args(q, k, v, o, g, lse_d, dq, dk, dv, scale, True, 3, 8, kg0, 8)
+    ws = torch.empty(max(rb.ra_block_bwd_workspace_size(a), 256), dtype=torch.uint8,
+                     device="cuda")
+    print("\n[block-bwd full hop kg0=%d] kernels" % kg0, flush=True)
+    rb.ra_block_bwd(a, ws)
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(7106 + kg0)
+    keys = np.unique(np.concatenate([
+        [0, 1, 31, 32, 63, 64, 255, 256, 257, 4095, 4096, n // 2, n - 257, n - 256, n - 2,
+         n - 1], rng.integers(0, n, 112)])).astype(np.int64)
+    rows = np.arange(n, dtype=np.int64)
+    zeros = np.zeros(n, np.int64)
+    kz = np.zeros(len(keys), np.int64)
+    k_seq, v_seq = k32, v32
+    if shift:  # key j at position j + 1: a leading row no query is paired with first
+        pad = np.zeros((1, 1, shift, d), np.float32)
+        k_seq = np.concatenate([pad, k32], axis=2)
+        v_seq = np.concatenate([pad, v32], axis=2)
+    print("[block-bwd full hop kg0=%d] oracle dk/dv on %d keys" % (kg0, len(keys)), flush=True)
+    rk, rv = oracle.bwd_keys(q32[0, 0], g32[0, 0], zeros, zeros, rows, lse, Dv, kz, kz,
+                             keys + shift, k_seq, v_seq, 1, scale, True)
+    gk = dk[0, 0].cpu().numpy().astype(np.float64)[keys]
+    gv = dv[0, 0].cpu().numpy().astype(np.float64)[keys]
+    check_grad(gk, rk, "full hop block dk kg0=%d" % kg0)
+    check_grad(gv, rv, "full hop block dv kg0=%d" % kg0)
+    if shift:  # the last key is allowed for no query of a block above the rank
+        assert not np.any(gk[keys == n - 1]) and not np.any(gv[keys == n - 1])
+    print("[block-bwd full hop kg0=%d] dk max err %.3e of max|ref| %.3e, dv max err %.3e of "
+          "%.3e" % (kg0, np.abs(gk - rk).max(), np.abs(rk).max(), np.abs(gv - rv).max(),
+                    np.abs(rv).max()), flush=True)
+    del q, k, v, g, o, dq, dk, dv, ws
+    torch.cuda.empty_cache()
