@@ -26,9 +26,11 @@ one at a time, and on identities that hold at any size.
   the same bound against the root sum of squares of the per-row and per-key
   terms: they tie the dq kernel to the dk kernel, and dv to the forward output,
   on every key rather than the tail only.
-* The per-hop unit itself (ra_block_bwd) at the 1M share's hop shape, where lse and
-  O are inputs: with seeded stand-ins on both sides the oracle computes dk and dv of
-  keys anywhere in the 131,072-key block, in both striped block classes.
+* The per-hop unit itself (ra_block_bwd) at the 1M share's hop shape, and the whole
+  ring backward on the 1M share: both take lse and O as inputs, so with seeded
+  stand-ins on both sides the oracle computes dk and dv of keys anywhere -- in the
+  131,072-key block (both striped block classes), and over the whole 1,048,576-token
+  sequence through the ring's dk/dv hand-off.
 """
 import gc
 import math
@@ -258,4 +260,89 @@ def test_block_bwd_full_hop_keys_everywhere(kg0, shift):
           "%.3e" % (kg0, np.abs(gk - rk).max(), np.abs(rk).max(), np.abs(gv - rv).max(),
                     np.abs(rv).max()), flush=True)
     del q, k, v, g, o, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_ring_bwd_full_share_keys_everywhere():
+    """ra_ring_bwd on the 1M-token share (rank 3 of 8, striped, bf16, COPY hand-off: K, V
+    and the dk/dv accumulators travel around the ring) with dk and dv compared element by
+    element at keys all over the 1,048,576-token sequence -- token 0, block and tile
+    boundaries, seeded picks in every K/V head, and the last tokens, which no query of
+    rank 3 sees.  The backward takes the forward's O and lse as inputs, so both sides get
+    seeded stand-ins for rank 3's rows (lse_t = ln(t + 1) + scale^2 |q_t|^2 / 2: the size
+    of ln sum_j exp(s_tj) for Gaussian scores over the t + 1 allowed keys; O seeded) and
+    the oracle needs no forward pass over the 1M tokens."""
+    import torch
+    w = configs.SHARE_1M
+    assert w.rank0 == 3 and w.ranks == 1 and w.B == 1
+    tag = "[ring-bwd keys everywhere]"
+    print("\n%s inputs" % tag, flush=True)
+    data = inputs.qkv(w.B, w.Hq, w.Hkv, w.S, w.d, w.seed, w.dtype, w.q_scale)
+    g_st, g32 = _dout(w)
+    o_st, o32 = inputs.to_dtype(0.05 * inputs.normal((w.B, w.Hq, w.S, w.d), w.seed + 11),
+                                w.dtype)
+    tdt = parity.torch_dtype(w.dtype)
+    q = parity.to_device(data["q"], w.dtype)
+    k = parity.to_device(data["k"], w.dtype)
+    v = parity.to_device(data["v"], w.dtype)
+    o = parity.to_device(o_st, w.dtype)
+    dout = parity.to_device(g_st, w.dtype)
+    for key in ("q", "k", "v"):
+        del data[key]
+    del o_st, g_st
+    ra = RingAttention(w.B, w.Hq, w.Hkv, w.S, w.d, w.R, "striped", tdt, w.causal, w.scale,
+                       rank0=w.rank0, n_ranks=w.ranks, handoff=rb.HANDOFF_COPY)
+    ra.maps()
+    ra.gather(q, k, v)
+    rb.ra_layout_gather(o, ra.o_sh, ra.fwd, w.R, w.rank0, w.ranks)
+    fwd, _ = oracle.layout_maps(rb.LAYOUTS["striped"], w.S, w.R)
+    toks = np.asarray(fwd[w.rank0 * w.n:(w.rank0 + 1) * w.n], np.int64)  # local row -> token
+    q32 = data["q32"]
+    qq = (q32[0][:, toks].astype(np.float64) ** 2).sum(-1)  # [Hq][n]
+    lse = (np.log(toks + 1.0)[None, :] + 0.5 * w.scale * w.scale * qq).astype(np.float32)
+    ra.lse_sh.copy_(torch.from_numpy(lse).reshape(ra.lse_sh.shape))
+    dq = torch.zeros((w.B, w.Hq, w.S, w.d), dtype=tdt, device="cuda")
+    dk = torch.zeros((w.B, w.Hkv, w.S, w.d), dtype=tdt, device="cuda")
+    dv = torch.zeros((w.B, w.Hkv, w.S, w.d), dtype=tdt, device="cuda")
+    print("%s backward ring" % tag, flush=True)
+    ra.backward(dout, dq, dk, dv)
+    torch.cuda.synchronize()
+    del q, k, v, o, dout, ra, dq
+
+    rng = np.random.default_rng(w.seed + 12)
+    n = w.n
+    fixed = np.array([0, 1, 2, 3, 4, 7, 8, 11, 255, 256, 2047, 2048, n - 1, n, n + 1,
+                      w.S // 2, w.S - 5, w.S - 4, w.S - 1], np.int64)
+    kb, kg, kt = [], [], []
+    for g in range(w.Hkv):
+        tk = np.unique(np.concatenate([fixed, rng.integers(0, w.S, 14)]))
+        kg += [g] * len(tk)
+        kt += list(tk)
+        kb += [0] * len(tk)
+    kb, kg, kt = (np.asarray(x, np.int64) for x in (kb, kg, kt))
+    rows_h = np.repeat(np.arange(w.Hq, dtype=np.int64), n)
+    rows_t = np.tile(toks, w.Hq)
+    rows_b = np.zeros_like(rows_t)
+    q_rows = q32[0][rows_h, rows_t]
+    g_rows = g32[0][rows_h, rows_t]
+    Dv = (g_rows.astype(np.float64) * o32[0][rows_h, rows_t].astype(np.float64)).sum(-1)
+    lse_rows = lse.reshape(-1).astype(np.float64)
+    print("%s oracle dk/dv on %d keys from %d rows" % (tag, len(kt), len(rows_t)), flush=True)
+    rk, rv = oracle.bwd_keys(q_rows, g_rows, rows_b, rows_h, rows_t, lse_rows, Dv, kb, kg, kt,
+                             data["k32"], data["v32"], w.Hq, w.scale, w.causal)
+    idx = (torch.from_numpy(kb), torch.from_numpy(kg), torch.from_numpy(kt))
+    gk = dk.cpu()[idx].double().numpy()
+    gv = dv.cpu()[idx].double().numpy()
+    rm = REL_MEAN[w.dtype]
+    check_grad(gk, rk, tag + " dk", rel_mean=rm)
+    check_grad(gv, rv, tag + " dv", rel_mean=rm)
+    unseen = kt > toks.max()
+    assert unseen.any() and not np.any(gk[unseen]) and not np.any(gv[unseen])
+    print("%s dk max err %.3e of max|ref| %.3e, dv max err %.3e of %.3e (%d keys unseen)" % (
+        tag, np.abs(gk - rk).max(), np.abs(rk).max(), np.abs(gv - rv).max(), np.abs(rv).max(),
+        int(unseen.sum())), flush=True)
+    del dk, dv
+    data.clear()
+    gc.collect()
     torch.cuda.empty_cache()
