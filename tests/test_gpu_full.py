@@ -21,7 +21,7 @@ from tests import parity
 
 pytestmark = pytest.mark.gpu
 
-RANDOM_ROWS = {1: 256, 2: 192, 3: 128, 4: 48, 5: 256}
+RANDOM_ROWS = {1: 2048, 2: 192, 3: 4096, 4: 4096, 5: 4096}
 
 
 def forwards_in_kernel(w, layout):
