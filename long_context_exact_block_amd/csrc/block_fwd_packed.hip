@@ -19,7 +19,7 @@
 //    gfx950's 64 LDS banks so every read pattern is conflict-free.
 //  * 8 waves x 32 queries per workgroup (256 rows), two waves per SIMD; QK of
 //    tile t+1 is interleaved with the exponentials of tile t; K fragments are
-//    read one k-step ahead (247 VGPRs: two waves leave room on each SIMD for
+//    read one k-step ahead (245 VGPRs: two waves leave room on each SIMD for
 //    the one-wave hand-off copy) and V^T fragments one PV group ahead.  In the
 //    fused ring the upper four waves run PV half a tile late (before instead
 //    of after the QK/exponential phase), so the waves sharing a SIMD are in
